@@ -1,0 +1,50 @@
+"""fp64 CPU oracle for one wavefront round of chunk-wise causal attention.
+
+TEST INFRASTRUCTURE ONLY. Nothing in the library or its Python binding may
+import, call or link anything under this package; only the tests, the smoke
+check and the benchmark's CPU-baseline leg do. The oracle shares no code with
+the HIP path: it has its own schedule model, RoPE, rounding emulation and
+attention, written from the method's definition, slowly and plainly.
+
+Sources (the Wave Forcing pages, arXiv 2611.00859):
+  * hyper.ai summary, section "Method": rounds k = i + s, full attention within
+    a chunk, chunk-causal attention in time, mask M_WF(s, j) = 1[j >= s].
+  * e-cogni.com.br article, section "Como funciona": the ordered per-layer
+    context anchor | bounded clean history | live store | denoising K/V; a
+    query slot reads itself and cleaner predecessors only.
+  * thelatestinai.com listing, Table 3 (notation: stage s, store = stage S,
+    rank S is Store) and Figure 1 (S=4 wavefront, one chunk per round).
+  * hyper.ai summary, section "Method" (WaveRT paragraph): K/V are published
+    after QKV projection and RoPE.
+
+Where the pages are silent the oracle takes these readings: softmax scale
+1/sqrt(d); adjacent-pair 3D RoPE on contiguous t|h|w channel ranges with
+per-axis frequencies theta^(-2m/d_a); token order frame, row, column; absolute
+latent-frame position chunk_frames * chunk_id + frame; published Q/K stored as
+bf16 (or fp8 e4m3 with per-64-token-block absmax scales and a per-chunk K mean).
+
+Parity status: every function here is pinned by a CPU test against the pages'
+closed forms, invariants, brute force or a library routine, except the choice
+of the fp8 scale/mean scheme, which the pages do not describe (they only name
+an fp8 payload with scales); its encoder is pinned to torch's float8_e4m3fn
+cast, but the blocking and mean smoothing follow the workload description and
+are "parity unpinned" beyond that.
+"""
+from .schedule import (RoundSchedule, live_mask, legal_positions, GroupRing,
+                       slot_position)
+from .rope import rope_split, token_grid, rope_3d
+from .numerics import (bf16_round, fp8_e4m3_encode, fp8_e4m3_decode,
+                       fp8_block_quantize, FP8_E4M3_MAX)
+from .attention import (masked_softmax_attention, slot_attention, round_attention,
+                        dense_round_attention)
+from .round import oracle_round, rotate_chunk, rotated_context
+
+__all__ = [
+    "RoundSchedule", "live_mask", "legal_positions", "GroupRing", "slot_position",
+    "rope_split", "token_grid", "rope_3d",
+    "bf16_round", "fp8_e4m3_encode", "fp8_e4m3_decode", "fp8_block_quantize",
+    "FP8_E4M3_MAX",
+    "masked_softmax_attention", "slot_attention", "round_attention",
+    "dense_round_attention",
+    "oracle_round", "rotate_chunk", "rotated_context",
+]

@@ -1,0 +1,101 @@
+"""Wavefront schedule model: which chunk sits at which context position.
+
+Wave Forcing, hyper.ai summary, section "Method": the wavefront updates chunk i
+at stage s in round k = i + s; attention is chunk-causal with the mask
+M_WF(s, j) = 1[j >= s] over the query's own slot and all cleaner ones.
+thelatestinai.com listing, Table 3: s indexes denoising stages 0 <= s < S and
+the store occupies stage s = S. e-cogni.com.br article, "Como funciona": each
+layer's context is anchor (initial chunk) | bounded clean history | live store |
+denoising K/V.
+
+Context positions are numbered cleanest first:
+    [anchor_0 .. anchor_{A-1} | hist_0 (oldest) .. hist_{H-1} | store | slot S-1 .. slot 0]
+"""
+from __future__ import annotations
+
+from collections import deque
+
+import numpy as np
+
+
+def live_mask(S: int) -> np.ndarray:
+    """M_WF over the S+1 live slots (store included), indexed [query s][key j]."""
+    M = np.zeros((S + 1, S + 1), dtype=np.int64)
+    for s in range(S + 1):
+        for j in range(S + 1):
+            M[s, j] = 1 if j >= s else 0
+    return M
+
+
+def slot_position(s: int, S: int, A: int, H: int) -> int:
+    """Context position of live slot s (s = S is the store)."""
+    if not 0 <= s <= S:
+        raise ValueError("slot out of range")
+    if s == S:
+        return A + H
+    return A + H + 1 + (S - 1 - s)
+
+
+def legal_positions(s: int, S: int, A: int, H: int) -> list:
+    """Context positions query slot s may read, in context order.
+
+    Anchor and clean history are cleaner than every live slot and are read by
+    all of them; among live slots the mask M_WF decides.
+    """
+    M = live_mask(S)
+    out = list(range(A)) + list(range(A, A + H))
+    live = [j for j in range(S, -1, -1) if M[s, j]]          # store first, then S-1 .. 0
+    out += [slot_position(j, S, A, H) for j in live]
+    return sorted(out)
+
+
+class RoundSchedule:
+    """Chunk ids of every context position in round k (steady state only).
+
+    Fill and drain rounds, where some positions hold no chunk yet, are not
+    modelled: the schedule raises for k below the first full round.
+    """
+
+    def __init__(self, S: int, A: int, H: int, k: int):
+        if k < S + H + A:
+            raise ValueError("round %d is a fill round; first full round is %d" % (k, S + H + A))
+        self.S, self.A, self.H, self.k = S, A, H, k
+        self.T = A + H + S + 1
+
+    def chunk_at(self, p: int) -> int:
+        S, A, H, k = self.S, self.A, self.H, self.k
+        if p < A:
+            return p                                   # anchor: the initial chunk(s)
+        if p < A + H:
+            return k - S - H + (p - A)                 # history, oldest first
+        if p == A + H:
+            return k - S                               # store = stage S
+        s = S - 1 - (p - A - H - 1)
+        return k - s                                   # live slot s holds chunk i = k - s
+
+    def chunk_ids(self) -> list:
+        return [self.chunk_at(p) for p in range(self.T)]
+
+    def slot_chunk(self, s: int) -> int:
+        return self.chunk_at(slot_position(s, self.S, self.A, self.H))
+
+
+class GroupRing:
+    """Physical-page-group bookkeeping written as a plain rotation.
+
+    The H+S+1 non-anchor positions hold one page group each. When a round ends
+    every chunk moves one position cleaner without being copied: the store's
+    group becomes the newest history, and the group that held the oldest
+    history is handed to slot 0 (the noisiest), which is re-published next
+    round. Anchor groups never move.
+    """
+
+    def __init__(self, S: int, A: int, H: int):
+        self.A = A
+        self.ring = deque(range(A, A + H + S + 1))
+
+    def advance(self):
+        self.ring.rotate(-1)
+
+    def groups(self) -> list:
+        return list(range(self.A)) + list(self.ring)

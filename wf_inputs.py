@@ -1,0 +1,163 @@
+"""Seeded synthetic inputs for wavefront-round attention.
+
+This module is shared by the tests, the benchmark and the smoke check. It holds
+only workload shapes and random draws: no RoPE, no schedule, no attention and
+no quantisation. Both the fp64 oracle and the HIP path consume what it returns.
+
+Workloads follow the Wave Forcing pages: Wan2.1 model widths (p5 Table 11),
+3 latent frames per chunk at 832x480 (p3 metrics table; p4 limitations), and
+the pages' own system runs use dummy DiT weights (p5 Fig. 7 caption, Table 4
+caption), so activations are drawn i.i.d. N(0, 1).
+
+Draw key: every (workload seed, round, slot) triple owns an independent PCG64
+stream, from which q, k and v are drawn in that order. A chunk that a round
+publishes from the store slot (slot S) becomes clean history later; its K/V are
+therefore re-drawn with the key (seed, round it was stored in, S).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    S: int                 # denoising slots; the store is slot S
+    A: int                 # anchor chunks
+    H: int                 # clean-history ring chunks
+    heads: int
+    head_dim: int
+    chunk_frames: int      # latent frames per chunk
+    frame_h: int           # patch rows per latent frame
+    frame_w: int           # patch columns per latent frame
+    page_tokens: int       # tokens per K/V page (divides the chunk)
+    in_dtype: str          # "fp32" | "bf16": dtype of the projected Q/K/V
+    qk_dtype: str          # "bf16" | "fp8": published Q/K format
+    rope_split: tuple      # (d_t, d_h, d_w)
+    rope_theta: float
+    seed: int
+    outlier_frac: float = 0.0     # fraction of the h*d channels scaled in Q and K
+    outlier_scale: float = 1.0
+    fused_qkv: bool = False       # input is one [tokens, 3*h*d] projection output
+    layer_rounds: int = 1         # consecutive rounds of one layer's pool
+    description: str = ""
+
+    @property
+    def N(self) -> int:
+        return self.chunk_frames * self.frame_h * self.frame_w
+
+    @property
+    def T(self) -> int:
+        """Ordered context positions: anchor | history | store | slots S-1..0."""
+        return self.A + self.H + self.S + 1
+
+    @property
+    def hd(self) -> int:
+        return self.heads * self.head_dim
+
+    @property
+    def steady_round(self) -> int:
+        """First round whose history ring is full of chunks other than the anchor."""
+        return self.S + self.H + self.A
+
+    def key_chunk_pairs(self) -> int:
+        """Legal (query chunk, key chunk) pairs in one round (all slots)."""
+        return (self.S + 1) * (self.A + self.H) + (self.S + 1) * (self.S + 2) // 2
+
+    def attention_flops(self) -> float:
+        """Mask-aware FLOPs of one round: QK^T plus PV, one multiply-add = 2."""
+        return 4.0 * self.N * self.N * self.head_dim * self.heads * self.key_chunk_pairs()
+
+
+def _split(d: int) -> tuple:
+    dh = 2 * (d // 6)
+    return (d - 2 * dh, dh, dh)
+
+
+WORKLOADS = {
+    # Tiny CPU-checkable round: S=2 + store, one 8x8 latent frame per chunk.
+    "tiny": Workload("tiny", S=2, A=1, H=2, heads=2, head_dim=64, chunk_frames=1,
+                     frame_h=8, frame_w=8, page_tokens=64, in_dtype="fp32", qk_dtype="bf16",
+                     rope_split=_split(64), rope_theta=1e4, seed=1,
+                     description="S=2+store, chunk 64 tokens (1x8x8), A=1, H=2, 2 heads x 64, fp32"),
+    # Wan2.1-1.3B, 4-step WF: chunk = 3 latent frames x 30x52 patches.
+    "wan1.3b_s4": Workload("wan1.3b_s4", S=4, A=1, H=2, heads=12, head_dim=128, chunk_frames=3,
+                           frame_h=30, frame_w=52, page_tokens=1560, in_dtype="bf16",
+                           qk_dtype="bf16", rope_split=(44, 42, 42), rope_theta=1e4, seed=2,
+                           description="Wan2.1-1.3B S=4+store, chunk 4680 (3x30x52), 12x128, A=1 H=2, bf16"),
+    # Wan2.1-1.3B, 5-step WF, 30 consecutive layer-rounds with rotation.
+    "wan1.3b_s5_30": Workload("wan1.3b_s5_30", S=5, A=1, H=2, heads=12, head_dim=128,
+                              chunk_frames=3, frame_h=30, frame_w=52, page_tokens=1560,
+                              in_dtype="bf16", qk_dtype="bf16", rope_split=(44, 42, 42),
+                              rope_theta=1e4, seed=3, layer_rounds=30,
+                              description="Wan2.1-1.3B S=5+store, 30 consecutive layer-rounds"),
+    # 14B-class: 40 heads, history ring 3, 1% outlier channels x20 in Q and K.
+    "wan14b_s4": Workload("wan14b_s4", S=4, A=1, H=3, heads=40, head_dim=128, chunk_frames=3,
+                          frame_h=30, frame_w=52, page_tokens=1560, in_dtype="bf16",
+                          qk_dtype="bf16", rope_split=(44, 42, 42), rope_theta=1e4, seed=4,
+                          outlier_frac=0.01, outlier_scale=20.0,
+                          description="14B-class S=4+store, chunk 4680, 40x128, H=3, Q/K outliers"),
+    # Quantised QK path from a fused bf16 QKV projection output.
+    "wan1.3b_s4_fp8": Workload("wan1.3b_s4_fp8", S=4, A=1, H=2, heads=12, head_dim=128,
+                               chunk_frames=3, frame_h=30, frame_w=52, page_tokens=1560,
+                               in_dtype="bf16", qk_dtype="fp8", rope_split=(44, 42, 42),
+                               rope_theta=1e4, seed=5, fused_qkv=True,
+                               description="Wan2.1-1.3B S=4 round, Q/K fp8 e4m3, fused QKV input"),
+    # Mid-size parity shapes: several tiles and ragged tails everywhere.
+    "ragged128": Workload("ragged128", S=3, A=1, H=2, heads=3, head_dim=128, chunk_frames=2,
+                          frame_h=10, frame_w=13, page_tokens=130, in_dtype="bf16",
+                          qk_dtype="bf16", rope_split=(44, 42, 42), rope_theta=1e4, seed=11,
+                          description="S=3, chunk 260 (2x10x13), page 130, 3x128, bf16"),
+    "ragged64": Workload("ragged64", S=3, A=1, H=1, heads=2, head_dim=64, chunk_frames=3,
+                         frame_h=6, frame_w=9, page_tokens=54, in_dtype="bf16", qk_dtype="bf16",
+                         rope_split=_split(64), rope_theta=1e4, seed=12,
+                         description="S=3, chunk 162 (3x6x9), page 54, 2x64, bf16"),
+    "ragged_fp8": Workload("ragged_fp8", S=3, A=1, H=2, heads=3, head_dim=128, chunk_frames=2,
+                           frame_h=10, frame_w=13, page_tokens=130, in_dtype="bf16",
+                           qk_dtype="fp8", rope_split=(44, 42, 42), rope_theta=1e4, seed=13,
+                           fused_qkv=True,
+                           description="fp8 QK, chunk 260 (2x10x13), 3x128, fused QKV"),
+}
+
+
+def round_to_bf16(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to the nearest bfloat16 (ties to even); returns float32."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
+    return u.astype(np.uint32).view(np.float32)
+
+
+def outlier_channels(w: Workload) -> np.ndarray:
+    """The fixed set of h*d channel indices scaled in Q and K (empty if none)."""
+    n = int(round(w.outlier_frac * w.hd))
+    if n == 0:
+        return np.zeros(0, dtype=np.int64)
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([w.seed, 0x6F75])))
+    return np.sort(rng.choice(w.hd, size=n, replace=False))
+
+
+def draw(w: Workload, round_index: int, slot: int):
+    """Pre-RoPE q, k, v of one chunk as float32 [N, heads*head_dim].
+
+    Values are bf16-exact when the workload's input dtype is bf16.
+    """
+    ss = np.random.SeedSequence([w.seed, int(round_index), int(slot)])
+    rng = np.random.Generator(np.random.PCG64(ss))
+    shape = (w.N, w.hd)
+    q = rng.standard_normal(shape, dtype=np.float32)
+    k = rng.standard_normal(shape, dtype=np.float32)
+    v = rng.standard_normal(shape, dtype=np.float32)
+    ch = outlier_channels(w)
+    if ch.size:
+        q[:, ch] *= np.float32(w.outlier_scale)
+        k[:, ch] *= np.float32(w.outlier_scale)
+    if w.in_dtype == "bf16":
+        q, k, v = round_to_bf16(q), round_to_bf16(k), round_to_bf16(v)
+    return q, k, v
+
+
+def stored_draw(w: Workload, chunk_id: int):
+    """K/V of a clean chunk as published by the store slot (round chunk_id + S)."""
+    return draw(w, chunk_id + w.S, w.S)
