@@ -7,10 +7,11 @@ funciona"), and attention then runs over the ordered context.
 
 Storage models of the published Q/K pages:
   "exact" - no rounding (self-checks);
-  "bf16"  - post-RoPE Q and K rounded to bfloat16, V as given (bf16 inputs);
+  "bf16"  - post-RoPE Q and K rounded to bfloat16; V rounded to bfloat16
+            (the page format; exact for bf16 inputs);
   "fp8"   - post-RoPE Q quantised per 64-token block to e4m3; K has its
             per-(chunk, head) fp32 channel mean removed, is quantised the same
-            way, and the mean is added back: K_hat = deq(K8) + mean.
+            way, and the mean is added back: K_hat = deq(K8) + mean; V bf16.
 """
 from __future__ import annotations
 
@@ -79,7 +80,8 @@ def rotated_context(shape, k, live, clean, storage="bf16"):
         else:
             kk, vv = clean[c]
         ctx_k[p] = store(rotate_chunk(shape, c, kk), storage, "k")
-        ctx_v[p] = np.asarray(vv, dtype=np.float64).reshape(N, h, d)
+        vv = np.asarray(vv, dtype=np.float64).reshape(N, h, d)
+        ctx_v[p] = vv if storage == "exact" else bf16_round(vv)     # V pages are bf16
     Qs = np.empty((S + 1, N, h, d))
     for s in range(S + 1):
         Qs[s] = store(rotate_chunk(shape, sched.slot_chunk(s), live[s][0]), storage, "q")
