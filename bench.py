@@ -1,0 +1,240 @@
+"""Benchmark: one wavefront round per step on one MI355X.
+
+A step is the whole hot path over one round of synthetic Wan2.1-shaped input:
+fused 3D-RoPE + K/V publish of all S+1 slots, wavefront attention of all S+1
+query slots over the paged context, and the round advance (page-table
+rotation). Inputs are resident in HBM before timing starts.
+
+Prints one JSON line. `value` is mask-aware attention TFLOP/s over the whole
+step (publish + attention + advance); rounds/s, per-kernel times, the
+attention roofline and an fp64-oracle CPU baseline ride along.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "wavefront-round attention TFLOP/s + rounds/sec, 1 MI355X, Wan2.1-1.3B S=4 shape"
+PEAK_BF16_TFLOPS = 2500.0          # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0             # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_bf16_wan1.3b_s4_traffic.txt")
+ATTN_SOURCES = [os.path.join(ROOT, "wavefront_causal_attention_amd", "csrc", f)
+                for f in ("wf_attention.hip", "wf_internal.h")]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ATTN_SOURCES:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per attention launch from the committed counter summary, or
+    None if the kernel source changed since the counters were taken."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    vals = {}
+    for line in open(TRAFFIC_FILE):
+        if ":" in line:
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="wan1.3b_s4")
+    ap.add_argument("--out-dtype", default="bf16", choices=["bf16", "fp32"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=24, help="query rows per (slot, head) in the CPU sample")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="also run one device copy of this many MiB (counter calibration)")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the wavefront round is built and timed on a single "
+              "MI355X; multi-GPU runs are not part of this build (requested %d)" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import wf_inputs as W
+    import wavefront_causal_attention_amd as wf
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    wf.load()
+    w = W.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    k0 = w.steady_round
+    cfg = wf.make_config(S=w.S, anchor_chunks=w.A, history_chunks=w.H, heads=w.heads,
+                         head_dim=w.head_dim, chunk_frames=w.chunk_frames, frame_h=w.frame_h,
+                         frame_w=w.frame_w, page_tokens=w.page_tokens, in_dtype=w.in_dtype,
+                         qk_dtype=w.qk_dtype, rope_split=w.rope_split, rope_theta=w.rope_theta,
+                         first_round=k0)
+    pool = wf.Pool(cfg, device=dev)
+    tdt = torch.bfloat16 if w.in_dtype == "bf16" else torch.float32
+
+    def to_dev(arrs):
+        return torch.from_numpy(np.concatenate(arrs, 0)).to(tdt).to(dev)
+
+    # seed anchor + history with the K/V their store rounds published
+    ids = pool.chunk_ids()
+    cl = [W.stored_draw(w, ids[w.T - 1 - slot]) for slot in range(w.S + 1, w.T)]
+    kc, vc = to_dev([x[1] for x in cl]), to_dev([x[2] for x in cl])
+    pool.publish(0, w.S + 1, w.T - w.S - 1, None, kc, vc, w.hd)
+    del cl
+    # live slots: one seeded round of projected Q/K/V, resident for every step
+    live = W.draw_slots(w, k0, range(w.S + 1))
+    if w.fused_qkv:
+        fused = to_dev([np.concatenate(x, 1) for x in live])
+        qd, kd, vd, stride = fused[:, :w.hd], fused[:, w.hd:2 * w.hd], fused[:, 2 * w.hd:], 3 * w.hd
+    else:
+        qd, kd, vd = to_dev([x[0] for x in live]), to_dev([x[1] for x in live]), to_dev([x[2] for x in live])
+        stride = w.hd
+    del live
+    q = pool.q_buffer()
+    qs = pool.q_scale_buffer()
+    out = pool.out_buffer(args.out_dtype)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        pool.publish(0, 0, w.S + 1, qd, kd, vd, stride, q_out=q, q_scales=qs, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        pool.attention(0, 0, w.S + 1, q, out, q_scales=qs, stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+        pool.advance(stream=stream)
+        if ev is not None:
+            ev[3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    pub_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    att_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    adv_ms = [e[2].elapsed_time(e[3]) for e in evs]
+    ms_step = wall * 1e3 / K
+    F = w.attention_flops()
+    att_avg = float(np.mean(att_ms))
+    pub_avg = float(np.mean(pub_ms))
+    n_el = (w.S + 1) * w.N * w.hd
+    in_bytes = 3 * n_el * (2 if w.in_dtype == "bf16" else 4)
+    qk_bytes = 1 if w.qk_dtype == "fp8" else 2
+    pub_bytes = in_bytes + 2 * n_el * qk_bytes + 2 * n_el            # read QKV; write Q, K, V
+    attn_tflops = F / (att_avg * 1e-3) / 1e12
+    traffic = measured_traffic()
+
+    if args.calibrate_copy_mib > 0:
+        nb = args.calibrate_copy_mib * (1 << 20)
+        src = torch.empty(nb, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+
+    res = {
+        "metric": METRIC,
+        "value": round(F * K / wall / 1e12, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.qk_dtype == "bf16" else "fp8-qk/bf16-pv",
+        "data": "synthetic: seeded N(0,1) Q/K/V, bf16, steady-state round",
+        "config": {"workload": w.name, "S": w.S, "anchor_chunks": w.A, "history_chunks": w.H,
+                   "chunk_tokens": w.N, "chunk_shape": [w.chunk_frames, w.frame_h, w.frame_w],
+                   "heads": w.heads, "head_dim": w.head_dim, "page_tokens": w.page_tokens,
+                   "mask_aware_flops_per_round": F, "out_dtype": args.out_dtype},
+        "rounds_per_sec": round(1e3 / ms_step, 3),
+        "attention_ms": round(att_avg, 4),
+        "attention_ms_minmax": [round(min(att_ms), 4), round(max(att_ms), 4)],
+        "publish_ms": round(pub_avg, 4),
+        "advance_ms": round(float(np.mean(adv_ms)), 4),
+        "attention_tflops": round(attn_tflops, 2),
+        "publish_gbps": round(pub_bytes / (pub_avg * 1e-3) / 1e9, 1),
+        "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic},
+        "publish_roofline": {"bound": "hbm", "achieved": round(pub_bytes / (pub_avg * 1e-3) / 1e9, 1),
+                             "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                             "frac": round(pub_bytes / (pub_avg * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+                             "algorithmic_bytes": pub_bytes},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, args.cpu_rows)
+    print(json.dumps(res), flush=True)
+
+
+def cpu_baseline(w, rows_per_slot_head):
+    """The fp64 oracle on a bounded sample of the same round, timed on the host.
+
+    Sample: every slot and head, `rows_per_slot_head` query rows each, over
+    the full legal context (RoPE of every context chunk included); FLOPs are
+    the mask-aware QK^T + PV FLOPs of the sampled rows."""
+    import numpy as np
+    import wf_inputs as W
+    from oracle import RoundSchedule, rotated_context, round_attention
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    k = w.steady_round
+    sch = RoundSchedule(w.S, w.A, w.H, k)
+    live = W.draw_slots(w, k, range(w.S + 1))
+    clean = {c: W.stored_draw(w, c)[1:] for c in sch.chunk_ids()[:w.A + w.H]}
+    rows = np.linspace(0, w.N - 1, rows_per_slot_head).astype(np.int64)
+    t0 = time.perf_counter()
+    Qs, ck, cv, _ = rotated_context(w, k, live, clean, storage=w.qk_dtype)
+    round_attention(Qs, ck, cv, w.S, w.A, w.H, rows=rows)
+    dt = time.perf_counter() - t0
+    flops = sum(4.0 * len(rows) * (w.T - s) * w.N * w.head_dim * w.heads for s in range(w.S + 1))
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": "%s round k=%d: RoPE of all %d context chunks + attention of %d query rows "
+                      "per (slot, head), all %d slots x %d heads, fp64 numpy; %.1f s"
+                      % (w.name, k, w.T, len(rows), w.S + 1, w.heads, dt)}
+
+
+if __name__ == "__main__":
+    main()

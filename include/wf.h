@@ -1,0 +1,176 @@
+/*
+ * wf.h - C ABI of the wavefront-round attention library (libwf.so), gfx950.
+ *
+ * One wavefront round of chunk-wise causal attention in a Wan2.1-style DiT
+ * layer (Wave Forcing, arXiv 2611.00859). In round k the S denoising slots
+ * hold chunks k-s (s = 0 is the noisiest) and the store slot s = S holds the
+ * chunk being written to clean history (hyper.ai summary, section "Method":
+ * k = i + s; thelatestinai.com listing, Table 3: store = stage S). Every layer
+ * attends over one ordered context (e-cogni.com.br article, "Como funciona"):
+ *
+ *     position:  0..A-1   | A..A+H-1               | A+H   | A+H+1 .. T-1
+ *     contents:  anchor   | clean history, oldest  | store | slot S-1 .. slot 0
+ *
+ * with T = A+H+S+1. Attention is full inside a chunk and follows the mask
+ * M_WF(s, j) = 1[j >= s] across live slots (hyper.ai, "Method"), so query slot
+ * s reads exactly the context prefix [0, T-s) (anchor, history, store, and
+ * slots S-1..s) and never a noisier slot.
+ *
+ * The library holds host state only (configuration, round index, readiness
+ * bits). The caller owns all device memory: the K/V pool, the page table, Q,
+ * O and scales. Every launching call enqueues its work on the given stream
+ * (a hipStream_t passed as void*, NULL for the default stream) and returns
+ * without synchronising. No exception crosses the ABI; every call returns a
+ * status and on any error launches nothing and changes no state.
+ *
+ * Slot numbering used by wf_kv_publish: slot s in [0, T) is context position
+ * T-1-s. Slots 0..S are the live slots (s = S is the store); slots S+1..T-1
+ * are the clean positions (history newest..oldest, then the anchor), which are
+ * published directly only to seed a pool; in steady state they are filled by
+ * wf_round_advance relabelling the store and history pages.
+ */
+#ifndef WF_H
+#define WF_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define WF_OK              0
+#define WF_E_INVALID_ARG   1   /* bad pointer, index, dtype or range */
+#define WF_E_SHAPE         2   /* configuration or buffer size not supported */
+#define WF_E_NOT_READY     3   /* a required context position is not published */
+#define WF_E_HIP           4   /* a HIP runtime call failed (see wf_last_error) */
+#define WF_E_NO_DEVICE     5   /* launching call on a host-model handle is not allowed here */
+
+/* element types */
+#define WF_DTYPE_BF16      0
+#define WF_DTYPE_FP32      1
+#define WF_DTYPE_FP8_E4M3  2   /* OCP e4m3: max 448, no infinities */
+
+typedef struct wf_config {
+    int32_t S;               /* denoising slots, >= 1; the store is slot S          */
+    int32_t anchor_chunks;   /* A >= 1: chunks of the initial anchor                */
+    int32_t history_chunks;  /* H >= 0: bounded clean-history ring                  */
+    int32_t heads;           /* attention heads per layer                           */
+    int32_t head_dim;        /* d: 64 or 128                                        */
+    int32_t num_layers;      /* layers sharing this pool and its page table        */
+    int32_t chunk_frames;    /* latent frames per chunk                             */
+    int32_t frame_h;         /* patch rows per latent frame                         */
+    int32_t frame_w;         /* patch columns per latent frame                      */
+    int32_t page_tokens;     /* tokens per page; divides the chunk, multiple of 8   */
+    int32_t in_dtype;        /* projected Q/K/V input: WF_DTYPE_BF16 | WF_DTYPE_FP32 */
+    int32_t qk_dtype;        /* published Q/K: WF_DTYPE_BF16 | WF_DTYPE_FP8_E4M3    */
+    int32_t rope_split[3];   /* (d_t, d_h, d_w), even, summing to head_dim          */
+    int32_t first_round;     /* round index k of the pool's first round, >= S+H+A   */
+    double  rope_theta;      /* RoPE base, e.g. 10000                               */
+} wf_config;
+
+typedef struct wf_handle wf_handle;
+
+/*
+ * Device memory a configuration needs. pool_bytes covers the K/V pages of all
+ * layers, the fp8 scales and per-chunk K means (fp8 only) and the RoPE
+ * tables; table_bytes is the int32 page table [T][pages_per_chunk].
+ * Returns WF_E_SHAPE for an unsupported configuration.
+ */
+int wf_pool_bytes(const wf_config* cfg, size_t* pool_bytes, size_t* table_bytes);
+
+/*
+ * Bind a configuration to caller-allocated device memory (pool_dev of at least
+ * pool_bytes, page_table_dev of at least table_bytes, both on the current
+ * device). Writes the RoPE tables and the initial page table and waits for
+ * them (blocking, setup only). Nothing is published yet. The library never
+ * frees the caller's memory.
+ */
+int wf_pool_create(const wf_config* cfg, void* pool_dev, size_t pool_bytes,
+                   int32_t* page_table_dev, size_t table_bytes, wf_handle** out);
+
+/*
+ * A handle with no device: it validates, schedules and tracks readiness
+ * exactly like a device handle, but its launching calls enqueue nothing and
+ * return WF_OK after every check and state change. For planning and for
+ * testing the host state machine without a GPU; it never computes outputs.
+ */
+int wf_pool_create_host_model(const wf_config* cfg, wf_handle** out);
+
+/* Frees host state only. */
+void wf_pool_destroy(wf_handle* h);
+
+/*
+ * Fused 3D RoPE + K/V publish (hyper.ai summary, "Method": WaveRT publishes
+ * K/V right after QKV projection and RoPE; paged delivery writes K/V straight
+ * into ordered attention slots). One launch covers slots
+ * [slot_first, slot_first + nslots) of one layer.
+ *
+ * q, k, v: device, in_dtype, row-major token rows; row (i*N + n) holds token n
+ *          of slot slot_first + i, heads*head_dim contiguous elements starting
+ *          at the pointer plus row * row_stride_elems. A fused [tokens, 3*h*d]
+ *          projection output is q = base, k = base + h*d, v = base + 2*h*d with
+ *          row_stride_elems = 3*h*d.
+ * chunk_t0_host: optional host array [nslots] of RoPE time offsets (latent
+ *          frame index of each slot's first frame); NULL takes
+ *          chunk_frames * chunk id from the round schedule.
+ * q_out:   device [S+1][heads][N][head_dim] bf16 (or fp8 e4m3 codes when
+ *          qk_dtype is fp8, with q_scales device float [S+1][heads][ceil(N/64)]);
+ *          rows of the published slots are written. q and q_out must both be
+ *          NULL when the range includes clean slots (s > S), and may both be
+ *          NULL to publish K/V only.
+ * The K pages of the slot's context position receive RoPE'd K (bf16, or fp8
+ * with per-64-token-block scales after subtracting the chunk's per-channel
+ * mean); the V pages receive V in bf16. Marks the slots published for this
+ * layer and round.
+ */
+int wf_kv_publish(wf_handle* h, int32_t layer, int32_t slot_first, int32_t nslots,
+                  const void* q, const void* k, const void* v, int64_t row_stride_elems,
+                  const int32_t* chunk_t0_host, void* q_out, float* q_scales, void* stream);
+
+/*
+ * Wavefront attention over the paged context (hyper.ai summary, "Method":
+ * M_WF(s, j) = 1[j >= s], full attention inside a chunk). One launch computes
+ * O = softmax(Q K^T / sqrt(d)) V for query slots [slot_first, slot_first+nslots)
+ * of one layer, each over its legal prefix; tiles of noisier slots are never
+ * read.
+ *
+ * q:        device, as q_out of wf_kv_publish (full [S+1] buffer).
+ * q_scales: device fp8 query scales, NULL for bf16.
+ * out:      device [S+1][N][heads*head_dim], out_dtype WF_DTYPE_BF16 or
+ *           WF_DTYPE_FP32 (full-precision parity mode); rows of the computed
+ *           slots are written.
+ * Returns WF_E_NOT_READY, launching nothing, unless every context position the
+ * slots read is published for this layer in this round (the readiness check
+ * made just before attention).
+ */
+int wf_attention_round(wf_handle* h, int32_t layer, int32_t slot_first, int32_t nslots,
+                       const void* q, const float* q_scales, void* out, int32_t out_dtype,
+                       void* stream);
+
+/*
+ * End the round: every chunk moves one position cleaner by rewriting the page
+ * table, never by copying pages. The store's pages become the newest history,
+ * the oldest history's pages are handed to slot 0 (re-published next round),
+ * and the anchor stays. After r advances, non-anchor position p maps to page
+ * group A + ((p - A + r) mod (H+S+1)); group g owns pages g*ppc .. g*ppc+ppc-1.
+ * Requires the store published in every layer (WF_E_NOT_READY otherwise).
+ * Live slots become unpublished; history keeps its readiness.
+ */
+int wf_round_advance(wf_handle* h, void* stream);
+
+/* Host queries (no device access). */
+int wf_round_index(const wf_handle* h, int64_t* k);
+int wf_schedule_chunk_ids(const wf_handle* h, int64_t* ids /* [T] */);
+int wf_page_table_host(const wf_handle* h, int32_t* table /* [T * pages_per_chunk] */);
+int wf_ready_mask(const wf_handle* h, int32_t layer, uint64_t* mask /* bit p = position p */);
+int wf_geometry(const wf_handle* h, int64_t* out /* [8]: N, T, pages_per_chunk, pool
+                 K offset, pool V offset, K bytes per layer, V bytes per layer, fp8 meta offset */);
+const char* wf_status_string(int status);
+const char* wf_last_error(const wf_handle* h);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* WF_H */

@@ -1,0 +1,139 @@
+"""Helpers for the GPU parity tests: drive a pool through the C ABI with seeded
+inputs, and evaluate the oracle on the same inputs (never on GPU results)."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import wf_inputs as W
+import wavefront_causal_attention_amd as wf
+from oracle import RoundSchedule, oracle_round
+
+
+def config_of(w: W.Workload, first_round=None, num_layers=1):
+    return wf.make_config(S=w.S, anchor_chunks=w.A, history_chunks=w.H, heads=w.heads,
+                          head_dim=w.head_dim, chunk_frames=w.chunk_frames, frame_h=w.frame_h,
+                          frame_w=w.frame_w, page_tokens=w.page_tokens, in_dtype=w.in_dtype,
+                          qk_dtype=w.qk_dtype, rope_split=w.rope_split, rope_theta=w.rope_theta,
+                          first_round=first_round, num_layers=num_layers)
+
+
+def to_dev(x: np.ndarray, in_dtype: str):
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    t = t.to(torch.bfloat16) if in_dtype == "bf16" else t
+    return t.cuda()
+
+
+def stack_dev(arrs, in_dtype):
+    return to_dev(np.concatenate(arrs, axis=0), in_dtype)
+
+
+class RoundRunner:
+    """A pool plus the seeded data published into it, round by round."""
+
+    def __init__(self, w: W.Workload, k0=None, draw=None, stored=None):
+        self.w = w
+        self.k0 = w.steady_round if k0 is None else k0
+        self.draw = draw or (lambda k, s: W.draw(w, k, s))
+        self.stored = stored or (lambda c: W.stored_draw(w, c))
+        self.pool = wf.Pool(config_of(w, first_round=self.k0))
+        self.q = self.pool.q_buffer()
+        self.qs = self.pool.q_scale_buffer()
+        self.k = self.k0
+        self.live = None
+        self.clean = {}
+
+    def seed_clean(self):
+        """Publish anchor and history of the current round (slots S+1 .. T-1)."""
+        w = self.w
+        sch = RoundSchedule(w.S, w.A, w.H, self.k)
+        ks, vs = [], []
+        for slot in range(w.S + 1, w.T):
+            c = sch.chunk_at(w.T - 1 - slot)
+            _, kk, vv = self.stored(c)
+            self.clean[c] = (kk, vv)
+            ks.append(kk)
+            vs.append(vv)
+        kd, vd = stack_dev(ks, w.in_dtype), stack_dev(vs, w.in_dtype)
+        self.pool.publish(0, w.S + 1, w.T - w.S - 1, None, kd, vd, w.hd)
+        torch.cuda.synchronize()
+
+    def publish_live(self, live=None, slot_first=0, nslots=None):
+        w = self.w
+        if live is None:
+            live = [self.draw(self.k, s) for s in range(w.S + 1)]
+        self.live = live
+        nslots = w.S + 1 - slot_first if nslots is None else nslots
+        sel = live[slot_first:slot_first + nslots]
+        if w.fused_qkv:
+            fused = np.concatenate([np.concatenate(x, axis=1) for x in sel], axis=0)
+            fd = to_dev(fused, w.in_dtype)
+            hd = w.hd
+            self.pool.publish(0, slot_first, nslots, fd[:, :hd], fd[:, hd:], fd[:, 2 * hd:], 3 * hd,
+                              q_out=self.q, q_scales=self.qs)
+            self._keep = fd
+        else:
+            qd = stack_dev([x[0] for x in sel], w.in_dtype)
+            kd = stack_dev([x[1] for x in sel], w.in_dtype)
+            vd = stack_dev([x[2] for x in sel], w.in_dtype)
+            self.pool.publish(0, slot_first, nslots, qd, kd, vd, w.hd, q_out=self.q, q_scales=self.qs)
+            self._keep = (qd, kd, vd)
+
+    def attention(self, out_dtype="fp32", slot_first=0, nslots=None):
+        w = self.w
+        nslots = w.S + 1 - slot_first if nslots is None else nslots
+        out = self.pool.out_buffer(out_dtype)
+        out.fill_(float("nan"))
+        self.pool.attention(0, slot_first, nslots, self.q, out, q_scales=self.qs)
+        torch.cuda.synchronize()
+        return out
+
+    def advance(self):
+        w = self.w
+        sch = RoundSchedule(w.S, w.A, w.H, self.k)
+        # the store's chunk becomes history with the K/V it was published with
+        c = sch.chunk_at(w.A + w.H)
+        self.clean[c] = tuple(self.live[w.S][1:])
+        self.pool.advance()
+        self.k += 1
+
+    def clean_for_round(self):
+        sch = RoundSchedule(self.w.S, self.w.A, self.w.H, self.k)
+        return {c: self.clean[c] for c in sch.chunk_ids()[:self.w.A + self.w.H]}
+
+
+def head_subset(w: W.Workload, heads):
+    """Workload restricted to some heads (attention is independent per head)."""
+    import dataclasses
+    return dataclasses.replace(w, heads=len(heads))
+
+
+def take_heads(x: np.ndarray, w: W.Workload, heads):
+    d = w.head_dim
+    return np.concatenate([x[:, h * d:(h + 1) * d] for h in heads], axis=1)
+
+
+def oracle_rows(w, k, live, clean, rows, heads=None, storage=None, slots=None):
+    """Oracle O[slots, rows, heads, d] on the same seeded inputs."""
+    storage = storage or w.qk_dtype
+    if heads is not None:
+        ws = head_subset(w, heads)
+        live = [tuple(take_heads(a, w, heads) for a in x) for x in live]
+        clean = {c: tuple(take_heads(a, w, heads) for a in kv) for c, kv in clean.items()}
+        w = ws
+    return oracle_round(w, k, live, clean, storage=storage, rows=rows, slots=slots)
+
+
+def gpu_rows(out: torch.Tensor, w: W.Workload, rows, heads=None, slots=None):
+    o = out.float().cpu().numpy().reshape(w.S + 1, w.N, w.heads, w.head_dim)
+    o = o[:, rows]
+    if heads is not None:
+        o = o[:, :, heads]
+    if slots is not None:
+        o = o[slots]
+    return o.astype(np.float64)
+
+
+def err_stats(gpu: np.ndarray, ref: np.ndarray):
+    diff = gpu - ref
+    return float(np.max(np.abs(diff))), float(np.linalg.norm(diff) / np.linalg.norm(ref))

@@ -1,0 +1,226 @@
+"""CPU tests of libwf.so: exports, validation, schedule, page table and
+readiness, through the C ABI on host-model handles (no device calls)."""
+import os
+import re
+
+import numpy as np
+import pytest
+
+import wf_inputs as W
+import wavefront_causal_attention_amd as wf
+from wavefront_causal_attention_amd import _lib
+from oracle import GroupRing, RoundSchedule
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 1 << 20            # an aligned non-null address; host-model calls never touch it
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    return wf.load()
+
+
+def cfg_of(w, **kw):
+    from _gpu_round import config_of
+    return config_of(w, **kw)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    header = open(os.path.join(ROOT, "include", "wf.h")).read()
+    declared = set(re.findall(r"\b(wf_[a-z_]+)\s*\(", header))
+    assert {"wf_kv_publish", "wf_attention_round", "wf_round_advance"} <= declared
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert set(_lib.EXPORTED) == declared
+
+
+def test_status_strings(lib):
+    for st in range(6):
+        assert _lib.status_string(st)
+
+
+@pytest.mark.parametrize("name", list(W.WORKLOADS))
+def test_pool_bytes_cover_pages(lib, name):
+    w = W.WORKLOADS[name]
+    pb, tb = wf.wf_pool_bytes(cfg_of(w))
+    elems = w.T * w.N * w.heads * w.head_dim
+    kbytes = elems * (1 if w.qk_dtype == "fp8" else 2)
+    assert pb >= kbytes + 2 * elems
+    assert tb == w.T * (w.N // w.page_tokens) * 4
+
+
+def test_wan13b_pool_size_matches_pages(lib):
+    w = W.WORKLOADS["wan1.3b_s4"]
+    pb, _ = wf.wf_pool_bytes(cfg_of(w))
+    # 8 chunks x 4680 tokens x 1536 channels x bf16, K and V = 230,031,360 B
+    assert 8 * 4680 * 1536 * 2 * 2 == 230031360
+    assert 230031360 <= pb < 230031360 + 65536
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("S", 0, wf.WF_E_SHAPE), ("anchor_chunks", 0, wf.WF_E_SHAPE), ("history_chunks", -1, wf.WF_E_SHAPE),
+    ("head_dim", 96, wf.WF_E_SHAPE), ("heads", 0, wf.WF_E_SHAPE), ("num_layers", 0, wf.WF_E_SHAPE),
+    ("page_tokens", 100, wf.WF_E_SHAPE), ("page_tokens", 4, wf.WF_E_SHAPE),
+    ("in_dtype", 7, wf.WF_E_INVALID_ARG), ("qk_dtype", 1, wf.WF_E_INVALID_ARG),
+    ("first_round", 6, wf.WF_E_SHAPE), ("rope_theta", 0.0, wf.WF_E_INVALID_ARG),
+    ("S", 70, wf.WF_E_SHAPE),
+])
+def test_config_validation(lib, field, value, status):
+    c = cfg_of(W.WORKLOADS["wan1.3b_s4"])
+    setattr(c, field, value)
+    with pytest.raises(wf.WfError) as e:
+        wf.wf_pool_bytes(c)
+    assert e.value.status == status
+
+
+def test_bad_rope_split(lib):
+    c = cfg_of(W.WORKLOADS["wan1.3b_s4"])
+    c.rope_split[2] = 40
+    with pytest.raises(wf.WfError) as e:
+        wf.wf_pool_bytes(c)
+    assert e.value.status == wf.WF_E_SHAPE
+
+
+def test_undersized_buffers_rejected_before_any_device_access(lib):
+    c = cfg_of(W.WORKLOADS["ragged128"])
+    pb, tb = wf.wf_pool_bytes(c)
+    for args in [(pb - 1, tb), (pb, tb - 4)]:
+        with pytest.raises(wf.WfError) as e:
+            wf.wf_pool_create(c, FAKE, args[0], FAKE, args[1])
+        assert e.value.status == wf.WF_E_SHAPE
+    with pytest.raises(wf.WfError) as e:
+        wf.wf_pool_create(c, FAKE + 16, pb, FAKE, tb)          # pool not 256-byte aligned
+    assert e.value.status == wf.WF_E_INVALID_ARG
+
+
+@pytest.mark.parametrize("name", ["wan1.3b_s4", "wan1.3b_s5_30", "wan14b_s4", "tiny"])
+def test_schedule_and_page_table_closed_form(lib, name):
+    w = W.WORKLOADS[name]
+    h = wf.wf_pool_create_host_model(cfg_of(w))
+    ring = GroupRing(w.S, w.A, w.H)
+    ppc = w.N // w.page_tokens
+    try:
+        for step in range(3 * (w.H + w.S + 1) + 1):
+            k = w.steady_round + step
+            assert wf.wf_round_index(h) == k
+            assert wf.wf_schedule_chunk_ids(h, w.T) == RoundSchedule(w.S, w.A, w.H, k).chunk_ids()
+            table = wf.wf_page_table_host(h, w.T * ppc)
+            assert table == [g * ppc + i for g in ring.groups() for i in range(ppc)]
+            assert sorted(table) == list(range(w.T * ppc))           # a permutation of the pages
+            # every live slot and the store publish, then the round ends
+            wf.wf_kv_publish(h, 0, 0, w.S + 1, FAKE, FAKE, FAKE, w.hd, None, FAKE, FAKE, None)
+            wf.wf_round_advance(h, None)
+            ring.advance()
+    finally:
+        wf.wf_pool_destroy(h)
+
+
+def test_readiness_and_failure_forcing(lib):
+    w = W.WORKLOADS["wan1.3b_s4"]
+    h = wf.wf_pool_create_host_model(cfg_of(w))
+    T, S, A, H = w.T, w.S, w.A, w.H
+    try:
+        # nothing published: attention and advance refuse
+        for call in (lambda: wf.wf_attention_round(h, 0, 0, S + 1, FAKE, None, FAKE, wf.WF_DTYPE_FP32, None),
+                     lambda: wf.wf_round_advance(h, None)):
+            with pytest.raises(wf.WfError) as e:
+                call()
+            assert e.value.status == wf.WF_E_NOT_READY
+        # clean positions (slots S+1..T-1) published with K/V only
+        wf.wf_kv_publish(h, 0, S + 1, T - S - 1, None, FAKE, FAKE, w.hd, None, None, None, None)
+        assert wf.wf_ready_mask(h, 0) == (1 << (A + H)) - 1
+        # the store alone makes slot S attendable, not slot S-1
+        wf.wf_kv_publish(h, 0, S, 1, FAKE, FAKE, FAKE, w.hd, None, FAKE, None, None)
+        wf.wf_attention_round(h, 0, S, 1, FAKE, None, FAKE, wf.WF_DTYPE_BF16, None)
+        with pytest.raises(wf.WfError) as e:
+            wf.wf_attention_round(h, 0, S - 1, 2, FAKE, None, FAKE, wf.WF_DTYPE_BF16, None)
+        assert e.value.status == wf.WF_E_NOT_READY
+        # slots 1..S-1: slot 1 is attendable, slot 0 is not
+        wf.wf_kv_publish(h, 0, 1, S - 1, FAKE, FAKE, FAKE, w.hd, None, FAKE, None, None)
+        wf.wf_attention_round(h, 0, 1, S, FAKE, None, FAKE, wf.WF_DTYPE_FP32, None)
+        with pytest.raises(wf.WfError) as e:
+            wf.wf_attention_round(h, 0, 0, S + 1, FAKE, None, FAKE, wf.WF_DTYPE_FP32, None)
+        assert e.value.status == wf.WF_E_NOT_READY
+        wf.wf_kv_publish(h, 0, 0, 1, FAKE, FAKE, FAKE, w.hd, None, FAKE, None, None)
+        wf.wf_attention_round(h, 0, 0, S + 1, FAKE, None, FAKE, wf.WF_DTYPE_FP32, None)
+        assert wf.wf_ready_mask(h, 0) == (1 << T) - 1
+        # advance: history and anchor stay published, live slots need re-publishing
+        wf.wf_round_advance(h, None)
+        assert wf.wf_ready_mask(h, 0) == (1 << (A + H)) - 1
+        with pytest.raises(wf.WfError) as e:
+            wf.wf_round_advance(h, None)
+        assert e.value.status == wf.WF_E_NOT_READY
+        assert wf.wf_round_index(h) == w.steady_round + 1
+    finally:
+        wf.wf_pool_destroy(h)
+
+
+def test_store_required_in_every_layer(lib):
+    w = W.WORKLOADS["ragged128"]
+    h = wf.wf_pool_create_host_model(cfg_of(w, num_layers=3))
+    try:
+        for layer in (0, 1):
+            wf.wf_kv_publish(h, layer, 0, w.S + 1, FAKE, FAKE, FAKE, w.hd, None, FAKE, None, None)
+        with pytest.raises(wf.WfError) as e:
+            wf.wf_round_advance(h, None)
+        assert e.value.status == wf.WF_E_NOT_READY
+        wf.wf_kv_publish(h, 2, w.S, 1, None, FAKE, FAKE, w.hd, None, None, None, None)
+        wf.wf_round_advance(h, None)
+    finally:
+        wf.wf_pool_destroy(h)
+
+
+@pytest.mark.parametrize("args", [
+    dict(layer=1), dict(layer=-1), dict(slot_first=-1), dict(nslots=0), dict(nslots=9),
+    dict(k=None), dict(v=None), dict(stride=100), dict(q_out=None),
+    dict(slot_first=4, nslots=2),          # q given but range includes a clean slot
+    dict(q=FAKE + 2),                      # misaligned
+])
+def test_publish_invalid_args(lib, args):
+    w = W.WORKLOADS["wan1.3b_s4"]
+    h = wf.wf_pool_create_host_model(cfg_of(w))
+    a = dict(layer=0, slot_first=0, nslots=w.S + 1, q=FAKE, k=FAKE, v=FAKE, stride=w.hd, q_out=FAKE)
+    a.update(args)
+    try:
+        with pytest.raises(wf.WfError) as e:
+            wf.wf_kv_publish(h, a["layer"], a["slot_first"], a["nslots"], a["q"], a["k"], a["v"],
+                             a["stride"], None, a["q_out"], None, None)
+        assert e.value.status == wf.WF_E_INVALID_ARG
+        assert wf.wf_ready_mask(h, 0) == 0               # nothing changed
+    finally:
+        wf.wf_pool_destroy(h)
+
+
+@pytest.mark.parametrize("args", [
+    dict(layer=2), dict(slot_first=5), dict(nslots=6), dict(q=None), dict(out=None),
+    dict(out_dtype=wf.WF_DTYPE_FP8_E4M3), dict(out=FAKE + 8),
+])
+def test_attention_invalid_args(lib, args):
+    w = W.WORKLOADS["wan1.3b_s4"]
+    h = wf.wf_pool_create_host_model(cfg_of(w))
+    wf.wf_kv_publish(h, 0, w.S + 1, w.T - w.S - 1, None, FAKE, FAKE, w.hd, None, None, None, None)
+    wf.wf_kv_publish(h, 0, 0, w.S + 1, FAKE, FAKE, FAKE, w.hd, None, FAKE, None, None)
+    a = dict(layer=0, slot_first=0, nslots=w.S + 1, q=FAKE, out=FAKE, out_dtype=wf.WF_DTYPE_FP32)
+    a.update(args)
+    try:
+        with pytest.raises(wf.WfError) as e:
+            wf.wf_attention_round(h, a["layer"], a["slot_first"], a["nslots"], a["q"], None,
+                                  a["out"], a["out_dtype"], None)
+        assert e.value.status == wf.WF_E_INVALID_ARG
+    finally:
+        wf.wf_pool_destroy(h)
+
+
+def test_explicit_rope_offsets_validated(lib):
+    w = W.WORKLOADS["tiny"]
+    h = wf.wf_pool_create_host_model(cfg_of(w))
+    try:
+        with pytest.raises(wf.WfError) as e:
+            wf.wf_kv_publish(h, 0, 0, 1, FAKE, FAKE, FAKE, w.hd, [-3], FAKE, None, None)
+        assert e.value.status == wf.WF_E_INVALID_ARG
+        wf.wf_kv_publish(h, 0, 0, 2, FAKE, FAKE, FAKE, w.hd, [5, 6], FAKE, None, None)
+    finally:
+        wf.wf_pool_destroy(h)

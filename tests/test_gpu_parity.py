@@ -1,0 +1,261 @@
+"""GPU parity of the HIP path against the fp64 oracle, through the C ABI.
+
+Floating-point bar (bf16 path): max-abs <= 1e-2 and relative L2 <= 5e-3 on the
+fp32 output mode, against the oracle with bf16 storage of the published Q/K
+(the pages' BF16 backend publishes bf16 pages). Integer work (page table,
+placement, schedule) is compared bit for bit.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import wf_inputs as W
+from oracle import GroupRing, RoundSchedule, bf16_round, oracle_round, rotate_chunk
+
+from _gpu_round import RoundRunner, err_stats, gpu_rows, oracle_rows
+
+pytestmark = pytest.mark.gpu
+
+BF16_MAX_ABS = 1e-2
+BF16_REL_L2 = 5e-3
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    assert torch.cuda.is_available(), "GPU tests need a ROCm device"
+    import wavefront_causal_attention_amd as wf
+    wf.load()                      # fails loudly if libwf.so is missing
+    yield
+
+
+def _bf16_dev_to_np(t):
+    return t.view(torch.int16).cpu().numpy().astype(np.int32).astype(np.uint32) << 16
+
+
+def _bf16_ulps(a, b):
+    """Distance in bf16 ulps between two arrays of bf16-exact values (same sign)."""
+    ia = (np.asarray(a, dtype=np.float32).view(np.uint32) >> 16).astype(np.int64)
+    ib = (np.asarray(b, dtype=np.float32).view(np.uint32) >> 16).astype(np.int64)
+    return np.abs(ia - ib)
+
+
+@pytest.mark.parametrize("name", ["tiny", "ragged128", "ragged64"])
+def test_round_parity_full(name):
+    w = W.WORKLOADS[name]
+    say("case", name, "full round")
+    r = RoundRunner(w)
+    r.seed_clean()
+    r.publish_live()
+    out = r.attention("fp32")
+    ref = oracle_round(w, r.k, r.live, r.clean_for_round(), storage="bf16")
+    g = gpu_rows(out, w, np.arange(w.N))
+    assert not np.isnan(g).any()
+    mx, rel = err_stats(g, ref)
+    say(name, "fp32-out max_abs %.3e rel_l2 %.3e" % (mx, rel))
+    assert mx <= BF16_MAX_ABS and rel <= BF16_REL_L2
+    # bf16 output mode: same bound plus the output's own rounding
+    outb = r.attention("bf16")
+    gb = gpu_rows(outb, w, np.arange(w.N))
+    mxb, relb = err_stats(gb, ref)
+    say(name, "bf16-out max_abs %.3e rel_l2 %.3e" % (mxb, relb))
+    assert mxb <= BF16_MAX_ABS and relb <= BF16_REL_L2
+    # the bf16 output is the fp32 output rounded once
+    assert np.array_equal(gb, bf16_round(g))
+
+
+@pytest.mark.parametrize("name", ["tiny", "ragged128", "ragged64"])
+def test_page_table_and_publish_placement(name):
+    w = W.WORKLOADS[name]
+    say("case", name, "placement")
+    r = RoundRunner(w)
+    r.seed_clean()
+    r.publish_live()
+    torch.cuda.synchronize()
+    pool = r.pool
+    ppc = pool.ppc
+    # device page table == host closed form == oracle's rotation model
+    ring = GroupRing(w.S, w.A, w.H)
+    dev_table = pool.table.cpu().numpy().tolist()
+    expect = [g * ppc + i for g in ring.groups() for i in range(ppc)]
+    assert dev_table == expect == pool.page_table_host()
+    assert pool.chunk_ids() == RoundSchedule(w.S, w.A, w.H, r.k).chunk_ids()
+    # read the pages back
+    g = pool.geometry
+    npages = w.T * ppc
+    kp = pool.pool[g["k_off"]:g["k_off"] + npages * w.heads * w.page_tokens * w.head_dim * 2]
+    kp = kp.view(torch.int16).view(npages, w.heads, w.page_tokens, w.head_dim)
+    vp = pool.pool[g["v_off"]:g["v_off"] + npages * w.heads * w.page_tokens * w.head_dim * 2]
+    vp = vp.view(torch.int16).view(npages, w.heads, w.head_dim, w.page_tokens)
+    kbits = _bf16_dev_to_np(kp)
+    vbits = _bf16_dev_to_np(vp)
+    sch = RoundSchedule(w.S, w.A, w.H, r.k)
+    clean = r.clean_for_round()
+    pos_slot = {w.T - 1 - s: s for s in range(w.S + 1)}
+    total = diff = 0
+    for p in range(w.T):
+        c = sch.chunk_at(p)
+        kk, vv = (r.live[pos_slot[p]][1:] if p in pos_slot else clean[c])
+        pages = [dev_table[p * ppc + i] for i in range(ppc)]
+        kg = np.concatenate([kbits[pg] for pg in pages], axis=1).view(np.float32)   # [heads, N, d]
+        vg = np.concatenate([vbits[pg] for pg in pages], axis=2).view(np.float32)   # [heads, d, N]
+        kref = bf16_round(rotate_chunk(w, c, kk)).transpose(1, 0, 2)
+        vref = np.asarray(vv, dtype=np.float64).reshape(w.N, w.heads, w.head_dim).transpose(1, 2, 0)
+        assert np.array_equal(vg.astype(np.float64), bf16_round(vref)), p        # V bit-exact
+        ulp = _bf16_ulps(kg, kref)
+        assert ulp.max() <= 1, p
+        total += ulp.size
+        diff += int(np.count_nonzero(ulp))
+    # Q rows of the live slots
+    qbits = _bf16_dev_to_np(r.q).view(np.float32)               # [S+1, heads, N, d]
+    for s in range(w.S + 1):
+        qref = bf16_round(rotate_chunk(w, sch.slot_chunk(s), r.live[s][0])).transpose(1, 0, 2)
+        ulp = _bf16_ulps(qbits[s], qref)
+        assert ulp.max() <= 1, s
+        total += ulp.size
+        diff += int(np.count_nonzero(ulp))
+    say(name, "Q/K elements differing by 1 ulp: %d of %d" % (diff, total))
+    assert diff <= 1e-3 * total
+
+
+@pytest.mark.parametrize("name", ["ragged128", "tiny"])
+def test_noisier_slots_poisoned_with_nan_do_not_change_cleaner_outputs(name):
+    w = W.WORKLOADS[name]
+    say("case", name, "nan poison")
+    r = RoundRunner(w)
+    r.seed_clean()
+    r.publish_live()
+    base = r.attention("fp32").cpu().numpy()
+    live = list(r.live)
+    for s in range(1, w.S + 1):
+        nan = np.full((w.N, w.hd), np.nan, dtype=np.float32)
+        poisoned = [(nan, nan, nan)] * s
+        r.publish_live(live=poisoned + live[s:], slot_first=0, nslots=s)
+        out = r.attention("fp32").cpu().numpy()
+        assert np.array_equal(out[s:], base[s:]), s            # bit-identical
+        assert np.isnan(out[:s]).all()
+        r.publish_live(live=live, slot_first=0, nslots=s)      # restore
+
+
+def test_zero_query_reads_exactly_the_legal_chunks():
+    w = W.WORKLOADS["ragged128"]
+    say("case zero-query chunk means")
+    rng = np.random.default_rng(0)
+
+    def draw(k, s):
+        c = k - s
+        return (np.zeros((w.N, w.hd), np.float32), W.round_to_bf16(rng.standard_normal((w.N, w.hd), dtype=np.float32)),
+                np.full((w.N, w.hd), float(c), np.float32))
+
+    def stored(c):
+        return (None, W.round_to_bf16(rng.standard_normal((w.N, w.hd), dtype=np.float32)),
+                np.full((w.N, w.hd), float(c), np.float32))
+
+    r = RoundRunner(w, draw=draw, stored=stored)
+    r.seed_clean()
+    r.publish_live()
+    out = r.attention("fp32").cpu().numpy().reshape(w.S + 1, w.N, w.hd)
+    ids = RoundSchedule(w.S, w.A, w.H, r.k).chunk_ids()
+    for s in range(w.S + 1):
+        legal = ids[:w.T - s]
+        expect = sum(legal) / len(legal)
+        assert np.max(np.abs(out[s] - expect)) <= 2e-6 * abs(expect), s
+
+
+def test_constant_values_pass_through():
+    w = W.WORKLOADS["ragged64"]
+    say("case V constant")
+
+    def draw(k, s):
+        q, kk, _ = W.draw(w, k, s)
+        return q, kk, np.full((w.N, w.hd), -2.375, np.float32)
+
+    def stored(c):
+        _, kk, _ = W.stored_draw(w, c)
+        return None, kk, np.full((w.N, w.hd), -2.375, np.float32)
+
+    r = RoundRunner(w, draw=draw, stored=stored)
+    r.seed_clean()
+    r.publish_live()
+    out = r.attention("fp32").cpu().numpy()
+    assert np.max(np.abs(out + 2.375)) <= 2.375 * 2 ** -7      # P in bf16, sums in fp32
+
+
+def test_slot_subset_launch_matches_full_round():
+    w = W.WORKLOADS["ragged128"]
+    say("case slot subsets")
+    r = RoundRunner(w)
+    r.seed_clean()
+    r.publish_live()
+    full = r.attention("fp32").cpu().numpy()
+    for first, n in [(0, 1), (1, 2), (w.S, 1), (2, w.S - 1)]:
+        part = r.attention("fp32", slot_first=first, nslots=n).cpu().numpy()
+        assert np.array_equal(part[first:first + n], full[first:first + n])
+        others = [i for i in range(w.S + 1) if not first <= i < first + n]
+        assert np.isnan(part[others]).all()
+
+
+def _sample_rows(N, seed, extra=16):
+    rng = np.random.default_rng(seed)
+    fixed = [0, 1, 63, 64, 127, 128, 129, N // 2, N - 73, N - 72, N - 71, N - 2, N - 1]
+    fixed += [(N // 128) * 128 - 1, (N // 128) * 128]
+    return np.array(sorted(set(int(x) for x in fixed + list(rng.integers(0, N, extra)) if 0 <= x < N)))
+
+
+@pytest.mark.parametrize("name,heads", [("wan1.3b_s4", None), ("wan14b_s4", "sample")])
+def test_full_size_round_sampled(name, heads):
+    w = W.WORKLOADS[name]
+    say("case", name, "full size, sampled rows")
+    r = RoundRunner(w)
+    r.seed_clean()
+    r.publish_live(live=W.draw_slots(w, r.k, range(w.S + 1)))
+    out = r.attention("fp32")
+    rows = _sample_rows(w.N, w.seed)
+    if heads == "sample":
+        ch = W.outlier_channels(w)
+        counts = np.bincount(ch // w.head_dim, minlength=w.heads)
+        heads = sorted({0, int(np.argmax(counts)), w.heads // 2, w.heads - 1})
+    ref = oracle_rows(w, r.k, r.live, r.clean_for_round(), rows, heads=heads)
+    g = gpu_rows(out, w, rows, heads=heads)
+    mx, rel = err_stats(g, ref)
+    say(name, "heads", heads, "rows", len(rows), "max_abs %.3e rel_l2 %.3e" % (mx, rel))
+    assert mx <= BF16_MAX_ABS and rel <= BF16_REL_L2
+    # every output of the full launch is finite
+    assert torch.isfinite(out).all().item()
+
+
+def test_thirty_layer_rounds_with_rotation():
+    w = W.WORKLOADS["wan1.3b_s5_30"]
+    say("case", w.name, "30 consecutive layer-rounds")
+    r = RoundRunner(w)
+    r.seed_clean()
+    worst = (0.0, 0.0)
+    for i in range(w.layer_rounds):
+        r.publish_live(live=W.draw_slots(w, r.k, range(w.S + 1)))
+        out = r.attention("fp32")
+        assert r.pool.round_index() == r.k
+        assert r.pool.chunk_ids() == RoundSchedule(w.S, w.A, w.H, r.k).chunk_ids()
+        full = i in (0, w.layer_rounds - 1)
+        rows = _sample_rows(w.N, 100 + i, extra=16 if full else 2)
+        heads = list(range(w.heads)) if full else [i % w.heads]
+        if not full:
+            rows = rows[::3]
+        ref = oracle_rows(w, r.k, r.live, r.clean_for_round(), rows, heads=heads)
+        g = gpu_rows(out, w, rows, heads=heads)
+        mx, rel = err_stats(g, ref)
+        worst = (max(worst[0], mx), max(worst[1], rel))
+        assert mx <= BF16_MAX_ABS and rel <= BF16_REL_L2, (i, mx, rel)
+        ring = GroupRing(w.S, w.A, w.H)
+        for _ in range(i):
+            ring.advance()
+        dev = r.pool.table.cpu().numpy().tolist()
+        assert dev == [g_ * r.pool.ppc + j for g_ in ring.groups() for j in range(r.pool.ppc)]
+        r.advance()
+        say("round", i, "ok max_abs %.2e rel %.2e" % (mx, rel))
+    say("30 rounds worst max_abs %.3e rel_l2 %.3e" % worst)

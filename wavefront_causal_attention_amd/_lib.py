@@ -1,0 +1,207 @@
+"""ctypes binding of libwf.so: the C ABI declared in include/wf.h, same names.
+
+Argument marshalling only. Device buffers are passed as raw pointers (torch
+tensors are accepted and passed by data_ptr()); streams as hipStream_t
+handles (a torch.cuda.Stream, an int, or None for torch's current stream).
+Every call that returns a non-zero status raises WfError.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libwf.so")
+
+WF_OK = 0
+WF_E_INVALID_ARG = 1
+WF_E_SHAPE = 2
+WF_E_NOT_READY = 3
+WF_E_HIP = 4
+
+WF_DTYPE_BF16 = 0
+WF_DTYPE_FP32 = 1
+WF_DTYPE_FP8_E4M3 = 2
+
+
+class wf_config(ctypes.Structure):
+    _fields_ = [
+        ("S", ctypes.c_int32),
+        ("anchor_chunks", ctypes.c_int32),
+        ("history_chunks", ctypes.c_int32),
+        ("heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("num_layers", ctypes.c_int32),
+        ("chunk_frames", ctypes.c_int32),
+        ("frame_h", ctypes.c_int32),
+        ("frame_w", ctypes.c_int32),
+        ("page_tokens", ctypes.c_int32),
+        ("in_dtype", ctypes.c_int32),
+        ("qk_dtype", ctypes.c_int32),
+        ("rope_split", ctypes.c_int32 * 3),
+        ("first_round", ctypes.c_int32),
+        ("rope_theta", ctypes.c_double),
+    ]
+
+
+class WfError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str = ""):
+        self.status = status
+        msg = "%s failed: %s (status %d)" % (where, status_string(status), status)
+        if detail:
+            msg += ": " + detail
+        super().__init__(msg)
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load libwf.so (built in-tree by build.py). Raises if it is not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("libwf.so is not built at %s; run __graft_entry__.build() "
+                          "(or python -m wavefront_causal_attention_amd.build)" % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.c_void_p
+    I32, I64 = ctypes.c_int32, ctypes.c_int64
+    sig = {
+        "wf_pool_bytes": (ctypes.c_int, [ctypes.POINTER(wf_config), ctypes.POINTER(ctypes.c_size_t),
+                                         ctypes.POINTER(ctypes.c_size_t)]),
+        "wf_pool_create": (ctypes.c_int, [ctypes.POINTER(wf_config), P, ctypes.c_size_t, P,
+                                          ctypes.c_size_t, ctypes.POINTER(P)]),
+        "wf_pool_create_host_model": (ctypes.c_int, [ctypes.POINTER(wf_config), ctypes.POINTER(P)]),
+        "wf_pool_destroy": (None, [P]),
+        "wf_kv_publish": (ctypes.c_int, [P, I32, I32, I32, P, P, P, I64, P, P, P, P]),
+        "wf_attention_round": (ctypes.c_int, [P, I32, I32, I32, P, P, P, I32, P]),
+        "wf_round_advance": (ctypes.c_int, [P, P]),
+        "wf_round_index": (ctypes.c_int, [P, ctypes.POINTER(I64)]),
+        "wf_schedule_chunk_ids": (ctypes.c_int, [P, P]),
+        "wf_page_table_host": (ctypes.c_int, [P, P]),
+        "wf_ready_mask": (ctypes.c_int, [P, I32, ctypes.POINTER(ctypes.c_uint64)]),
+        "wf_geometry": (ctypes.c_int, [P, P]),
+        "wf_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+        "wf_last_error": (ctypes.c_char_p, [P]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load().wf_status_string(int(status)).decode()
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    if hasattr(x, "data_ptr"):
+        return x.data_ptr()
+    raise TypeError("expected a tensor, an int address or None, got %r" % type(x))
+
+
+def _stream(st):
+    if st is None:
+        import torch
+        if torch.cuda.is_available():
+            return torch.cuda.current_stream().cuda_stream
+        return None
+    if isinstance(st, int):
+        return st
+    return st.cuda_stream
+
+
+def _check(status, where, handle=None):
+    if status != WF_OK:
+        detail = load().wf_last_error(handle).decode() if handle else ""
+        raise WfError(status, where, detail)
+
+
+def wf_pool_bytes(cfg: wf_config):
+    pb, tb = ctypes.c_size_t(), ctypes.c_size_t()
+    _check(load().wf_pool_bytes(ctypes.byref(cfg), ctypes.byref(pb), ctypes.byref(tb)), "wf_pool_bytes")
+    return pb.value, tb.value
+
+
+def wf_pool_create(cfg: wf_config, pool, pool_bytes: int, page_table, table_bytes: int) -> int:
+    h = ctypes.c_void_p()
+    _check(load().wf_pool_create(ctypes.byref(cfg), _ptr(pool), pool_bytes, _ptr(page_table),
+                                 table_bytes, ctypes.byref(h)), "wf_pool_create")
+    return h.value
+
+
+def wf_pool_create_host_model(cfg: wf_config) -> int:
+    h = ctypes.c_void_p()
+    _check(load().wf_pool_create_host_model(ctypes.byref(cfg), ctypes.byref(h)), "wf_pool_create_host_model")
+    return h.value
+
+
+def wf_pool_destroy(h: int) -> None:
+    load().wf_pool_destroy(h)
+
+
+def wf_kv_publish(h, layer, slot_first, nslots, q, k, v, row_stride_elems,
+                  chunk_t0=None, q_out=None, q_scales=None, stream=None) -> None:
+    t0 = None
+    if chunk_t0 is not None:
+        arr = (ctypes.c_int32 * len(chunk_t0))(*[int(x) for x in chunk_t0])
+        t0 = ctypes.cast(arr, ctypes.c_void_p)
+    _check(load().wf_kv_publish(h, layer, slot_first, nslots, _ptr(q), _ptr(k), _ptr(v),
+                                int(row_stride_elems), t0, _ptr(q_out), _ptr(q_scales),
+                                _stream(stream)), "wf_kv_publish", h)
+
+
+def wf_attention_round(h, layer, slot_first, nslots, q, q_scales, out, out_dtype, stream=None) -> None:
+    _check(load().wf_attention_round(h, layer, slot_first, nslots, _ptr(q), _ptr(q_scales),
+                                     _ptr(out), int(out_dtype), _stream(stream)),
+           "wf_attention_round", h)
+
+
+def wf_round_advance(h, stream=None) -> None:
+    _check(load().wf_round_advance(h, _stream(stream)), "wf_round_advance", h)
+
+
+def wf_round_index(h) -> int:
+    k = ctypes.c_int64()
+    _check(load().wf_round_index(h, ctypes.byref(k)), "wf_round_index")
+    return k.value
+
+
+def wf_schedule_chunk_ids(h, T: int):
+    arr = (ctypes.c_int64 * T)()
+    _check(load().wf_schedule_chunk_ids(h, ctypes.cast(arr, ctypes.c_void_p)), "wf_schedule_chunk_ids")
+    return list(arr)
+
+
+def wf_page_table_host(h, n: int):
+    arr = (ctypes.c_int32 * n)()
+    _check(load().wf_page_table_host(h, ctypes.cast(arr, ctypes.c_void_p)), "wf_page_table_host")
+    return list(arr)
+
+
+def wf_ready_mask(h, layer: int) -> int:
+    m = ctypes.c_uint64()
+    _check(load().wf_ready_mask(h, layer, ctypes.byref(m)), "wf_ready_mask")
+    return m.value
+
+
+def wf_geometry(h):
+    arr = (ctypes.c_int64 * 8)()
+    _check(load().wf_geometry(h, ctypes.cast(arr, ctypes.c_void_p)), "wf_geometry")
+    keys = ["N", "T", "ppc", "k_off", "v_off", "k_layer_bytes", "v_layer_bytes", "meta_off"]
+    return dict(zip(keys, list(arr)))
+
+
+EXPORTED = [
+    "wf_pool_bytes", "wf_pool_create", "wf_pool_create_host_model", "wf_pool_destroy",
+    "wf_kv_publish", "wf_attention_round", "wf_round_advance", "wf_round_index",
+    "wf_schedule_chunk_ids", "wf_page_table_host", "wf_ready_mask", "wf_geometry",
+    "wf_status_string", "wf_last_error",
+]

@@ -1,0 +1,383 @@
+// C ABI of the wavefront-round attention library: validation, the round
+// schedule, readiness bookkeeping and the page-table closed form. Every device
+// step is a kernel launched through wf_internal.h.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "../../include/wf.h"
+#include "wf_internal.h"
+
+namespace {
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Byte layout of the caller's pool allocation.
+struct Layout {
+    int N = 0, T = 0, R = 0, ppc = 0, nblk = 0;
+    size_t k_layer = 0, v_layer = 0;       // bytes per layer
+    size_t k_off = 0, v_off = 0;           // region offsets
+    size_t scale_off = 0, mean_off = 0;    // fp8 metadata
+    size_t scale_layer = 0, mean_layer = 0;
+    size_t htab_off = 0, wtab_off = 0, omega_off = 0;
+    size_t pool_bytes = 0, table_bytes = 0;
+};
+
+int validate(const wf_config* c, Layout* L) {
+    if (!c) return WF_E_INVALID_ARG;
+    if (c->S < 1 || c->anchor_chunks < 1 || c->history_chunks < 0) return WF_E_SHAPE;
+    const int T = c->anchor_chunks + c->history_chunks + c->S + 1;
+    if (T > wf::kMaxSlots) return WF_E_SHAPE;
+    if (c->heads < 1 || c->heads > 1024) return WF_E_SHAPE;
+    if (c->head_dim != 64 && c->head_dim != 128) return WF_E_SHAPE;
+    if (c->num_layers < 1 || c->num_layers > 4096) return WF_E_SHAPE;
+    if (c->chunk_frames < 1 || c->frame_h < 1 || c->frame_w < 1) return WF_E_SHAPE;
+    const int64_t N = (int64_t)c->chunk_frames * c->frame_h * c->frame_w;
+    if (N > (1 << 20)) return WF_E_SHAPE;
+    if (c->page_tokens < 8 || c->page_tokens % 8 != 0 || N % c->page_tokens != 0) return WF_E_SHAPE;
+    const int ppc = (int)(N / c->page_tokens);
+    if ((int64_t)T * ppc > wf::kMaxTablePages) return WF_E_SHAPE;
+    if (c->in_dtype != WF_DTYPE_BF16 && c->in_dtype != WF_DTYPE_FP32) return WF_E_INVALID_ARG;
+    if (c->qk_dtype != WF_DTYPE_BF16 && c->qk_dtype != WF_DTYPE_FP8_E4M3) return WF_E_INVALID_ARG;
+    const int dt = c->rope_split[0], dh = c->rope_split[1], dw = c->rope_split[2];
+    if (dt < 0 || dh < 0 || dw < 0 || (dt | dh | dw) & 1 || dt + dh + dw != c->head_dim) return WF_E_SHAPE;
+    if (dt > 64) return WF_E_SHAPE;
+    if (!(c->rope_theta > 0.0) || !std::isfinite(c->rope_theta)) return WF_E_INVALID_ARG;
+    if (c->first_round < c->S + c->history_chunks + c->anchor_chunks) return WF_E_SHAPE;
+    if ((int64_t)c->first_round + 1000000000LL > INT32_MAX / std::max(1, c->chunk_frames)) {
+        // keep chunk_frames * chunk id representable for a very long stream
+        if ((int64_t)c->chunk_frames * (c->first_round + 1) > INT32_MAX / 2) return WF_E_SHAPE;
+    }
+    if (!L) return WF_OK;
+    const bool fp8 = c->qk_dtype == WF_DTYPE_FP8_E4M3;
+    L->N = (int)N;
+    L->T = T;
+    L->R = c->history_chunks + c->S + 1;
+    L->ppc = ppc;
+    L->nblk = (int)((N + wf::kFp8Block - 1) / wf::kFp8Block);
+    const size_t pages = (size_t)T * ppc;
+    const size_t elems = pages * c->heads * c->page_tokens * (size_t)c->head_dim;
+    L->k_layer = align_up(elems * (fp8 ? 1 : 2), 256);
+    L->v_layer = align_up(elems * 2, 256);
+    size_t off = 0;
+    L->k_off = off;  off += L->k_layer * c->num_layers;
+    L->v_off = off;  off += L->v_layer * c->num_layers;
+    if (fp8) {
+        L->scale_layer = align_up((size_t)T * c->heads * L->nblk * 4, 256);
+        L->mean_layer = align_up((size_t)T * c->heads * c->head_dim * 4, 256);
+        L->scale_off = off;  off += L->scale_layer * c->num_layers;
+        L->mean_off = off;   off += L->mean_layer * c->num_layers;
+    }
+    L->htab_off = off;  off += align_up((size_t)c->frame_h * (dh / 2) * 8 + 8, 256);
+    L->wtab_off = off;  off += align_up((size_t)c->frame_w * (dw / 2) * 8 + 8, 256);
+    L->omega_off = off; off += align_up((size_t)(dt / 2) * 8 + 8, 256);
+    L->pool_bytes = off;
+    L->table_bytes = pages * sizeof(int32_t);
+    return WF_OK;
+}
+
+}  // namespace
+
+struct wf_handle {
+    wf_config cfg;
+    Layout L;
+    bool host_model = false;
+    char* pool = nullptr;
+    int32_t* table = nullptr;
+    int64_t ring = 0;                    // advances since creation
+    std::vector<uint64_t> ready;         // per layer, bit p = context position p
+    char err[512] = {0};
+
+    int A() const { return cfg.anchor_chunks; }
+    int H() const { return cfg.history_chunks; }
+    int S() const { return cfg.S; }
+    int64_t round() const { return cfg.first_round + ring; }
+    int position_of_slot(int s) const { return L.T - 1 - s; }
+
+    // Chunk id at context position p in the current round (k = i + s).
+    int64_t chunk_at(int p) const {
+        const int64_t k = round();
+        if (p < A()) return p;
+        if (p < A() + H()) return k - S() - H() + (p - A());
+        const int s = L.T - 1 - p;       // live slot index, store = S
+        return k - s;
+    }
+    // Page group of context position p: the anchor is fixed; the ring of
+    // H+S+1 groups rotates by one per advance.
+    int group_at(int p) const {
+        if (p < A()) return p;
+        return A() + (int)(((int64_t)(p - A()) + ring) % L.R);
+    }
+    uint64_t prefix_bits(int n) const { return n >= 64 ? ~0ull : ((1ull << n) - 1); }
+
+    int fail_hip(hipError_t e, const char* what) {
+        snprintf(err, sizeof err, "%s: %s", what, hipGetErrorString(e));
+        return WF_E_HIP;
+    }
+};
+
+extern "C" {
+
+int wf_pool_bytes(const wf_config* cfg, size_t* pool_bytes, size_t* table_bytes) {
+    if (!pool_bytes || !table_bytes) return WF_E_INVALID_ARG;
+    Layout L;
+    const int st = validate(cfg, &L);
+    if (st != WF_OK) return st;
+    *pool_bytes = L.pool_bytes;
+    *table_bytes = L.table_bytes;
+    return WF_OK;
+}
+
+static int make_handle(const wf_config* cfg, wf_handle** out, Layout* L) {
+    if (!out) return WF_E_INVALID_ARG;
+    const int st = validate(cfg, L);
+    if (st != WF_OK) return st;
+    wf_handle* h = new (std::nothrow) wf_handle();
+    if (!h) return WF_E_INVALID_ARG;
+    h->cfg = *cfg;
+    h->L = *L;
+    h->ready.assign(cfg->num_layers, 0);
+    *out = h;
+    return WF_OK;
+}
+
+int wf_pool_create_host_model(const wf_config* cfg, wf_handle** out) {
+    Layout L;
+    wf_handle* h = nullptr;
+    const int st = make_handle(cfg, &h, &L);
+    if (st != WF_OK) return st;
+    h->host_model = true;
+    *out = h;
+    return WF_OK;
+}
+
+int wf_pool_create(const wf_config* cfg, void* pool_dev, size_t pool_bytes,
+                   int32_t* page_table_dev, size_t table_bytes, wf_handle** out) {
+    if (!pool_dev || !page_table_dev || !out) return WF_E_INVALID_ARG;
+    Layout L;
+    int st = validate(cfg, &L);
+    if (st != WF_OK) return st;
+    if (pool_bytes < L.pool_bytes || table_bytes < L.table_bytes) return WF_E_SHAPE;
+    if (((uintptr_t)pool_dev & 255) || ((uintptr_t)page_table_dev & 3)) return WF_E_INVALID_ARG;
+    wf_handle* h = nullptr;
+    st = make_handle(cfg, &h, &L);
+    if (st != WF_OK) return st;
+    h->pool = (char*)pool_dev;
+    h->table = page_table_dev;
+
+    // RoPE tables, fp64 on the host, stored as fp32 (cos, sin) for the row and
+    // column axes; the time axis keeps fp64 frequencies because its positions
+    // grow with the stream and are expanded per launch.
+    const int dt = cfg->rope_split[0], dh = cfg->rope_split[1], dw = cfg->rope_split[2];
+    std::vector<float> htab((size_t)cfg->frame_h * (dh / 2) * 2 + 2, 0.f);
+    std::vector<float> wtab((size_t)cfg->frame_w * (dw / 2) * 2 + 2, 0.f);
+    std::vector<double> om((size_t)(dt / 2) + 1, 0.0);
+    for (int y = 0; y < cfg->frame_h; ++y)
+        for (int m = 0; m < dh / 2; ++m) {
+            const double phi = y * std::pow(cfg->rope_theta, -2.0 * m / dh);
+            htab[((size_t)y * (dh / 2) + m) * 2 + 0] = (float)std::cos(phi);
+            htab[((size_t)y * (dh / 2) + m) * 2 + 1] = (float)std::sin(phi);
+        }
+    for (int x = 0; x < cfg->frame_w; ++x)
+        for (int m = 0; m < dw / 2; ++m) {
+            const double phi = x * std::pow(cfg->rope_theta, -2.0 * m / dw);
+            wtab[((size_t)x * (dw / 2) + m) * 2 + 0] = (float)std::cos(phi);
+            wtab[((size_t)x * (dw / 2) + m) * 2 + 1] = (float)std::sin(phi);
+        }
+    for (int m = 0; m < dt / 2; ++m) om[m] = std::pow(cfg->rope_theta, -2.0 * m / dt);
+
+    hipError_t e = hipMemcpy(h->pool + L.htab_off, htab.data(), htab.size() * 4, hipMemcpyHostToDevice);
+    if (e == hipSuccess)
+        e = hipMemcpy(h->pool + L.wtab_off, wtab.data(), wtab.size() * 4, hipMemcpyHostToDevice);
+    if (e == hipSuccess)
+        e = hipMemcpy(h->pool + L.omega_off, om.data(), om.size() * 8, hipMemcpyHostToDevice);
+    if (e == hipSuccess)
+        e = wf::launch_page_table(h->table, L.T, cfg->anchor_chunks, L.ppc, h->ring, nullptr);
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (e != hipSuccess) {
+        delete h;
+        return WF_E_HIP;
+    }
+    *out = h;
+    return WF_OK;
+}
+
+void wf_pool_destroy(wf_handle* h) { delete h; }
+
+int wf_kv_publish(wf_handle* h, int32_t layer, int32_t slot_first, int32_t nslots,
+                  const void* q, const void* k, const void* v, int64_t row_stride_elems,
+                  const int32_t* chunk_t0_host, void* q_out, float* q_scales, void* stream) {
+    if (!h) return WF_E_INVALID_ARG;
+    const wf_config& c = h->cfg;
+    const Layout& L = h->L;
+    if (layer < 0 || layer >= c.num_layers) return WF_E_INVALID_ARG;
+    if (nslots < 1 || slot_first < 0 || slot_first + nslots > L.T) return WF_E_INVALID_ARG;
+    if (!k || !v) return WF_E_INVALID_ARG;
+    if (row_stride_elems < (int64_t)c.heads * c.head_dim) return WF_E_INVALID_ARG;
+    if ((q == nullptr) != (q_out == nullptr)) return WF_E_INVALID_ARG;
+    if (q && slot_first + nslots > c.S + 1) return WF_E_INVALID_ARG;
+    const bool fp8 = c.qk_dtype == WF_DTYPE_FP8_E4M3;
+    if (fp8 && q_out && !q_scales) return WF_E_INVALID_ARG;
+    const int esz = c.in_dtype == WF_DTYPE_FP32 ? 4 : 2;
+    if (((uintptr_t)k | (uintptr_t)v | (uintptr_t)q) % (esz * 8) ||
+        (row_stride_elems * esz) % 16)
+        return WF_E_INVALID_ARG;      // 8-element vector loads
+    if (q_out && ((uintptr_t)q_out % 16)) return WF_E_INVALID_ARG;
+
+    wf::PublishArgs a{};
+    for (int i = 0; i < nslots; ++i) {
+        const int64_t t0 = chunk_t0_host
+                               ? (int64_t)chunk_t0_host[i]
+                               : (int64_t)c.chunk_frames * h->chunk_at(h->position_of_slot(slot_first + i));
+        if (t0 < 0 || t0 > INT32_MAX / 2) return WF_E_INVALID_ARG;
+        a.t0[i] = (int)t0;
+    }
+    if (!h->host_model) {
+        a.q = q; a.k = k; a.v = v;
+        a.row_stride = row_stride_elems;
+        a.q_out = q_out;
+        a.q_scales = q_scales;
+        a.kpage = h->pool + L.k_off + L.k_layer * layer;
+        a.vpage = (uint16_t*)(h->pool + L.v_off + L.v_layer * layer);
+        a.kscale = fp8 ? (float*)(h->pool + L.scale_off + L.scale_layer * layer) : nullptr;
+        a.kmean = fp8 ? (float*)(h->pool + L.mean_off + L.mean_layer * layer) : nullptr;
+        a.table = h->table;
+        a.htab = (const float2*)(h->pool + L.htab_off);
+        a.wtab = (const float2*)(h->pool + L.wtab_off);
+        a.omega_t = (const double*)(h->pool + L.omega_off);
+        a.N = L.N; a.heads = c.heads; a.D = c.head_dim; a.pt = c.page_tokens; a.ppc = L.ppc;
+        a.T = L.T; a.S = c.S;
+        a.frame_h = c.frame_h; a.frame_w = c.frame_w;
+        a.dt = c.rope_split[0]; a.dh = c.rope_split[1]; a.dw = c.rope_split[2];
+        a.slot_first = slot_first; a.nslots = nslots;
+        a.in_fp32 = c.in_dtype == WF_DTYPE_FP32;
+        a.nblk = L.nblk;
+        const hipError_t e = wf::launch_publish(a, fp8, (hipStream_t)stream);
+        if (e != hipSuccess) return h->fail_hip(e, "wf_kv_publish launch");
+    }
+    for (int i = 0; i < nslots; ++i) h->ready[layer] |= 1ull << h->position_of_slot(slot_first + i);
+    return WF_OK;
+}
+
+int wf_attention_round(wf_handle* h, int32_t layer, int32_t slot_first, int32_t nslots,
+                       const void* q, const float* q_scales, void* out, int32_t out_dtype,
+                       void* stream) {
+    if (!h) return WF_E_INVALID_ARG;
+    const wf_config& c = h->cfg;
+    const Layout& L = h->L;
+    if (layer < 0 || layer >= c.num_layers) return WF_E_INVALID_ARG;
+    if (nslots < 1 || slot_first < 0 || slot_first + nslots > c.S + 1) return WF_E_INVALID_ARG;
+    if (!q || !out) return WF_E_INVALID_ARG;
+    if (out_dtype != WF_DTYPE_BF16 && out_dtype != WF_DTYPE_FP32) return WF_E_INVALID_ARG;
+    const bool fp8 = c.qk_dtype == WF_DTYPE_FP8_E4M3;
+    if (fp8 && !q_scales) return WF_E_INVALID_ARG;
+    if (((uintptr_t)q % 16) || ((uintptr_t)out % 16)) return WF_E_INVALID_ARG;
+    // readiness check made just before attention: the union of the requested
+    // slots' legal contexts is the prefix [0, T - slot_first)
+    const uint64_t need = h->prefix_bits(L.T - slot_first);
+    if ((h->ready[layer] & need) != need) {
+        snprintf(h->err, sizeof h->err, "layer %d: positions 0x%llx not published", layer,
+                 (unsigned long long)(need & ~h->ready[layer]));
+        return WF_E_NOT_READY;
+    }
+    if (h->host_model) return WF_OK;
+    wf::AttnArgs a{};
+    a.q = q; a.q_scales = q_scales; a.out = out;
+    a.kpage = h->pool + L.k_off + L.k_layer * layer;
+    a.vpage = (const uint16_t*)(h->pool + L.v_off + L.v_layer * layer);
+    a.kscale = fp8 ? (const float*)(h->pool + L.scale_off + L.scale_layer * layer) : nullptr;
+    a.kmean = fp8 ? (const float*)(h->pool + L.mean_off + L.mean_layer * layer) : nullptr;
+    a.table = h->table;
+    a.N = L.N; a.heads = c.heads; a.D = c.head_dim; a.pt = c.page_tokens; a.ppc = L.ppc;
+    a.T = L.T; a.S = c.S;
+    a.slot_first = slot_first; a.nslots = nslots;
+    a.out_fp32 = out_dtype == WF_DTYPE_FP32;
+    a.nblk = L.nblk;
+    a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)c.head_dim));
+    const hipError_t e = wf::launch_attention(a, fp8, (hipStream_t)stream);
+    if (e != hipSuccess) return h->fail_hip(e, "wf_attention_round launch");
+    return WF_OK;
+}
+
+int wf_round_advance(wf_handle* h, void* stream) {
+    if (!h) return WF_E_INVALID_ARG;
+    const int A = h->A(), H = h->H();
+    const int store = A + H;
+    for (int l = 0; l < h->cfg.num_layers; ++l)
+        if (!(h->ready[l] >> store & 1)) {
+            snprintf(h->err, sizeof h->err, "layer %d: store not published", l);
+            return WF_E_NOT_READY;
+        }
+    if (!h->host_model) {
+        const hipError_t e =
+            wf::launch_page_table(h->table, h->L.T, A, h->L.ppc, h->ring + 1, (hipStream_t)stream);
+        if (e != hipSuccess) return h->fail_hip(e, "wf_round_advance launch");
+    }
+    h->ring += 1;
+    for (int l = 0; l < h->cfg.num_layers; ++l) {
+        const uint64_t old = h->ready[l];
+        uint64_t nw = old & h->prefix_bits(A);                       // anchor stays
+        for (int p = A; p < A + H; ++p)                              // history <- one cleaner
+            nw |= ((old >> (p + 1)) & 1ull) << p;
+        h->ready[l] = nw;                                            // live slots cleared
+    }
+    return WF_OK;
+}
+
+int wf_round_index(const wf_handle* h, int64_t* k) {
+    if (!h || !k) return WF_E_INVALID_ARG;
+    *k = h->round();
+    return WF_OK;
+}
+
+int wf_schedule_chunk_ids(const wf_handle* h, int64_t* ids) {
+    if (!h || !ids) return WF_E_INVALID_ARG;
+    for (int p = 0; p < h->L.T; ++p) ids[p] = h->chunk_at(p);
+    return WF_OK;
+}
+
+int wf_page_table_host(const wf_handle* h, int32_t* table) {
+    if (!h || !table) return WF_E_INVALID_ARG;
+    for (int p = 0; p < h->L.T; ++p)
+        for (int i = 0; i < h->L.ppc; ++i) table[p * h->L.ppc + i] = h->group_at(p) * h->L.ppc + i;
+    return WF_OK;
+}
+
+int wf_ready_mask(const wf_handle* h, int32_t layer, uint64_t* mask) {
+    if (!h || !mask || layer < 0 || layer >= h->cfg.num_layers) return WF_E_INVALID_ARG;
+    *mask = h->ready[layer];
+    return WF_OK;
+}
+
+int wf_geometry(const wf_handle* h, int64_t* out) {
+    if (!h || !out) return WF_E_INVALID_ARG;
+    out[0] = h->L.N;
+    out[1] = h->L.T;
+    out[2] = h->L.ppc;
+    out[3] = (int64_t)h->L.k_off;
+    out[4] = (int64_t)h->L.v_off;
+    out[5] = (int64_t)h->L.k_layer;
+    out[6] = (int64_t)h->L.v_layer;
+    out[7] = (int64_t)h->L.scale_off;
+    return WF_OK;
+}
+
+const char* wf_status_string(int status) {
+    switch (status) {
+        case WF_OK: return "ok";
+        case WF_E_INVALID_ARG: return "invalid argument";
+        case WF_E_SHAPE: return "unsupported shape or undersized buffer";
+        case WF_E_NOT_READY: return "context position not published";
+        case WF_E_HIP: return "HIP runtime error";
+        case WF_E_NO_DEVICE: return "no device behind this handle";
+        default: return "unknown status";
+    }
+}
+
+const char* wf_last_error(const wf_handle* h) { return h ? h->err : ""; }
+
+}  // extern "C"

@@ -105,28 +105,35 @@ WORKLOADS = {
                                in_dtype="bf16", qk_dtype="fp8", rope_split=(44, 42, 42),
                                rope_theta=1e4, seed=5, fused_qkv=True,
                                description="Wan2.1-1.3B S=4 round, Q/K fp8 e4m3, fused QKV input"),
-    # Mid-size parity shapes: several tiles and ragged tails everywhere.
+    # Mid-size parity shapes: several tiles, ragged query and key tails, pages
+    # that key tiles straddle.
     "ragged128": Workload("ragged128", S=3, A=1, H=2, heads=3, head_dim=128, chunk_frames=2,
-                          frame_h=10, frame_w=13, page_tokens=130, in_dtype="bf16",
+                          frame_h=12, frame_w=13, page_tokens=104, in_dtype="bf16",
                           qk_dtype="bf16", rope_split=(44, 42, 42), rope_theta=1e4, seed=11,
-                          description="S=3, chunk 260 (2x10x13), page 130, 3x128, bf16"),
+                          description="S=3, chunk 312 (2x12x13), page 104, 3x128, bf16"),
     "ragged64": Workload("ragged64", S=3, A=1, H=1, heads=2, head_dim=64, chunk_frames=3,
-                         frame_h=6, frame_w=9, page_tokens=54, in_dtype="bf16", qk_dtype="bf16",
+                         frame_h=6, frame_w=12, page_tokens=72, in_dtype="bf16", qk_dtype="bf16",
                          rope_split=_split(64), rope_theta=1e4, seed=12,
-                         description="S=3, chunk 162 (3x6x9), page 54, 2x64, bf16"),
+                         description="S=3, chunk 216 (3x6x12), page 72, 2x64, bf16"),
     "ragged_fp8": Workload("ragged_fp8", S=3, A=1, H=2, heads=3, head_dim=128, chunk_frames=2,
-                           frame_h=10, frame_w=13, page_tokens=130, in_dtype="bf16",
+                           frame_h=12, frame_w=13, page_tokens=104, in_dtype="bf16",
                            qk_dtype="fp8", rope_split=(44, 42, 42), rope_theta=1e4, seed=13,
                            fused_qkv=True,
-                           description="fp8 QK, chunk 260 (2x10x13), 3x128, fused QKV"),
+                           description="fp8 QK, chunk 312 (2x12x13), 3x128, fused QKV"),
 }
 
 
 def round_to_bf16(x: np.ndarray) -> np.ndarray:
     """Round float32 values to the nearest bfloat16 (ties to even); returns float32."""
-    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
-    return u.astype(np.uint32).view(np.float32)
+    x = np.asarray(x, dtype=np.float32)
+    if not np.isfinite(x).all():
+        raise ValueError("round_to_bf16 expects finite values")
+    u = x.view(np.uint32) if x.flags.c_contiguous else np.ascontiguousarray(x).view(np.uint32)
+    r = (u >> 16) & np.uint32(1)
+    r += np.uint32(0x7FFF)
+    r += u                                           # finite inputs cannot overflow
+    r &= np.uint32(0xFFFF0000)
+    return r.view(np.float32)
 
 
 def outlier_channels(w: Workload) -> np.ndarray:
@@ -161,3 +168,11 @@ def draw(w: Workload, round_index: int, slot: int):
 def stored_draw(w: Workload, chunk_id: int):
     """K/V of a clean chunk as published by the store slot (round chunk_id + S)."""
     return draw(w, chunk_id + w.S, w.S)
+
+
+def draw_slots(w: Workload, round_index: int, slots, threads: int = 8):
+    """draw() for several slots of one round, drawn concurrently."""
+    from concurrent.futures import ThreadPoolExecutor
+    slots = list(slots)
+    with ThreadPoolExecutor(max(1, min(threads, len(slots)))) as ex:
+        return list(ex.map(lambda s: draw(w, round_index, s), slots))
