@@ -89,12 +89,14 @@ def test_page_table_and_publish_placement(name):
     # read the pages back
     g = pool.geometry
     npages = w.T * ppc
-    kp = pool.pool[g["k_off"]:g["k_off"] + npages * w.heads * w.page_tokens * w.head_dim * 2]
-    kp = kp.view(torch.int16).view(npages, w.heads, w.page_tokens, w.head_dim)
-    vp = pool.pool[g["v_off"]:g["v_off"] + npages * w.heads * w.page_tokens * w.head_dim * 2]
-    vp = vp.view(torch.int16).view(npages, w.heads, w.head_dim, w.page_tokens)
-    kbits = _bf16_dev_to_np(kp)
-    vbits = _bf16_dev_to_np(vp)
+    # K pages [page][head][D/8][tok][8], V pages [page][head][tok/8][D][8]
+    D, pt = w.head_dim, w.page_tokens
+    kp = pool.pool[g["k_off"]:g["k_off"] + npages * w.heads * pt * D * 2]
+    kp = kp.view(torch.int16).view(npages, w.heads, D // 8, pt, 8).permute(0, 1, 3, 2, 4)
+    vp = pool.pool[g["v_off"]:g["v_off"] + npages * w.heads * pt * D * 2]
+    vp = vp.view(torch.int16).view(npages, w.heads, pt // 8, D, 8).permute(0, 1, 2, 4, 3)
+    kbits = _bf16_dev_to_np(kp.reshape(npages, w.heads, pt, D))     # [page, head, tok, d]
+    vbits = _bf16_dev_to_np(vp.reshape(npages, w.heads, pt, D))
     sch = RoundSchedule(w.S, w.A, w.H, r.k)
     clean = r.clean_for_round()
     pos_slot = {w.T - 1 - s: s for s in range(w.S + 1)}
@@ -104,9 +106,9 @@ def test_page_table_and_publish_placement(name):
         kk, vv = (r.live[pos_slot[p]][1:] if p in pos_slot else clean[c])
         pages = [dev_table[p * ppc + i] for i in range(ppc)]
         kg = np.concatenate([kbits[pg] for pg in pages], axis=1).view(np.float32)   # [heads, N, d]
-        vg = np.concatenate([vbits[pg] for pg in pages], axis=2).view(np.float32)   # [heads, d, N]
+        vg = np.concatenate([vbits[pg] for pg in pages], axis=1).view(np.float32)   # [heads, N, d]
         kref = bf16_round(rotate_chunk(w, c, kk)).transpose(1, 0, 2)
-        vref = np.asarray(vv, dtype=np.float64).reshape(w.N, w.heads, w.head_dim).transpose(1, 2, 0)
+        vref = np.asarray(vv, dtype=np.float64).reshape(w.N, w.heads, w.head_dim).transpose(1, 0, 2)
         assert np.array_equal(vg.astype(np.float64), bf16_round(vref)), p        # V bit-exact
         ulp = _bf16_ulps(kg, kref)
         assert ulp.max() <= 1, p

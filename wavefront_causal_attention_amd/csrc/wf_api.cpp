@@ -3,6 +3,7 @@
 // step is a kernel launched through wf_internal.h.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
@@ -24,8 +25,44 @@ struct Layout {
     size_t scale_off = 0, mean_off = 0;    // fp8 metadata
     size_t scale_layer = 0, mean_layer = 0;
     size_t htab_off = 0, wtab_off = 0, omega_off = 0;
+    size_t work_off = 0, work_stride = 0;  // attention work lists, one per slot range
+    int work_len = 0;                      // entries per list
     size_t pool_bytes = 0, table_bytes = 0;
 };
+
+// Attention work order for query slots [first, first + n): every (slot, head,
+// query tile) unit, cost = keys it reads. Units are laid out head-major and cut
+// into kXcds contiguous pieces of equal cost, so one head's K/V is streamed by
+// one or two XCDs (each XCD has its own L2); inside a piece, longest first.
+// Workgroup b runs piece b % kXcds, entry b / kXcds. Returns the padded list.
+std::vector<int32_t> build_work_list(int first, int n, int heads, int qtiles, int T) {
+    struct U { int s, h, q; int64_t cost; };
+    std::vector<U> u;
+    u.reserve((size_t)n * heads * qtiles);
+    for (int h = 0; h < heads; ++h)
+        for (int s = first; s < first + n; ++s)
+            for (int q = 0; q < qtiles; ++q) u.push_back({s, h, q, (int64_t)(T - s)});
+    int64_t total = 0;
+    for (const U& x : u) total += x.cost;
+    std::vector<std::vector<U>> piece(wf::kXcds);
+    int64_t acc = 0;
+    for (const U& x : u) {
+        int xcd = (int)((acc * wf::kXcds + total / 2 / wf::kXcds) / std::max<int64_t>(total, 1));
+        xcd = std::min(std::max(xcd, 0), wf::kXcds - 1);
+        piece[xcd].push_back(x);
+        acc += x.cost;
+    }
+    size_t M = 0;
+    for (auto& p : piece) {
+        std::stable_sort(p.begin(), p.end(), [](const U& a, const U& b) { return a.cost > b.cost; });
+        M = std::max(M, p.size());
+    }
+    std::vector<int32_t> out(M * wf::kXcds, -1);
+    for (int x = 0; x < wf::kXcds; ++x)
+        for (size_t j = 0; j < piece[x].size(); ++j)
+            out[j * wf::kXcds + x] = wf::pack_work(piece[x][j].s, piece[x][j].h, piece[x][j].q);
+    return out;
+}
 
 int validate(const wf_config* c, Layout* L) {
     if (!c) return WF_E_INVALID_ARG;
@@ -63,6 +100,7 @@ int validate(const wf_config* c, Layout* L) {
     const size_t elems = pages * c->heads * c->page_tokens * (size_t)c->head_dim;
     L->k_layer = align_up(elems * (fp8 ? 1 : 2), 256);
     L->v_layer = align_up(elems * 2, 256);
+    if (L->k_layer >= (1ull << 31) || L->v_layer >= (1ull << 31)) return WF_E_SHAPE;  // 32-bit buffer offsets
     size_t off = 0;
     L->k_off = off;  off += L->k_layer * c->num_layers;
     L->v_off = off;  off += L->v_layer * c->num_layers;
@@ -75,6 +113,19 @@ int validate(const wf_config* c, Layout* L) {
     L->htab_off = off;  off += align_up((size_t)c->frame_h * (dh / 2) * 8 + 8, 256);
     L->wtab_off = off;  off += align_up((size_t)c->frame_w * (dw / 2) * 8 + 8, 256);
     L->omega_off = off; off += align_up((size_t)(dt / 2) * 8 + 8, 256);
+    {
+        const int qtiles = (int)((N + wf::kAttnBM - 1) / wf::kAttnBM);
+        const int64_t units = (int64_t)(c->S + 1) * c->heads * qtiles;
+        if (units >= (1 << 22) || qtiles > 0xFFFF) return WF_E_SHAPE;
+        size_t longest = 0;
+        for (int first = 0; first <= c->S; ++first)
+            for (int n = 1; first + n <= c->S + 1; ++n)
+                longest = std::max(longest, build_work_list(first, n, c->heads, qtiles, T).size());
+        L->work_len = (int)longest;
+        L->work_stride = align_up(longest * 4, 256);
+        L->work_off = off;
+        off += L->work_stride * (size_t)(c->S + 1) * (c->S + 1);
+    }
     L->pool_bytes = off;
     L->table_bytes = pages * sizeof(int32_t);
     return WF_OK;
@@ -90,6 +141,7 @@ struct wf_handle {
     int32_t* table = nullptr;
     int64_t ring = 0;                    // advances since creation
     std::vector<uint64_t> ready;         // per layer, bit p = context position p
+    std::vector<int> work_count;         // attention work-list length per slot range
     char err[512] = {0};
 
     int A() const { return cfg.anchor_chunks; }
@@ -141,6 +193,7 @@ static int make_handle(const wf_config* cfg, wf_handle** out, Layout* L) {
     h->cfg = *cfg;
     h->L = *L;
     h->ready.assign(cfg->num_layers, 0);
+    h->work_count.assign((size_t)(cfg->S + 1) * (cfg->S + 1), 0);
     *out = h;
     return WF_OK;
 }
@@ -195,6 +248,15 @@ int wf_pool_create(const wf_config* cfg, void* pool_dev, size_t pool_bytes,
         e = hipMemcpy(h->pool + L.wtab_off, wtab.data(), wtab.size() * 4, hipMemcpyHostToDevice);
     if (e == hipSuccess)
         e = hipMemcpy(h->pool + L.omega_off, om.data(), om.size() * 8, hipMemcpyHostToDevice);
+    const int qtiles = (L.N + wf::kAttnBM - 1) / wf::kAttnBM;
+    for (int first = 0; first <= cfg->S && e == hipSuccess; ++first)
+        for (int n = 1; first + n <= cfg->S + 1 && e == hipSuccess; ++n) {
+            std::vector<int32_t> wl = build_work_list(first, n, cfg->heads, qtiles, L.T);
+            if ((int)wl.size() > L.work_len) { e = hipErrorInvalidValue; break; }
+            h->work_count[first * (cfg->S + 1) + n - 1] = (int)wl.size();
+            e = hipMemcpy(h->pool + L.work_off + L.work_stride * (first * (cfg->S + 1) + n - 1),
+                          wl.data(), wl.size() * 4, hipMemcpyHostToDevice);
+        }
     if (e == hipSuccess)
         e = wf::launch_page_table(h->table, L.T, cfg->anchor_chunks, L.ppc, h->ring, nullptr);
     if (e == hipSuccess) e = hipDeviceSynchronize();
@@ -289,9 +351,14 @@ int wf_attention_round(wf_handle* h, int32_t layer, int32_t slot_first, int32_t 
     a.q = q; a.q_scales = q_scales; a.out = out;
     a.kpage = h->pool + L.k_off + L.k_layer * layer;
     a.vpage = (const uint16_t*)(h->pool + L.v_off + L.v_layer * layer);
+    a.kbytes = (int32_t)L.k_layer;
+    a.vbytes = (int32_t)L.v_layer;
     a.kscale = fp8 ? (const float*)(h->pool + L.scale_off + L.scale_layer * layer) : nullptr;
     a.kmean = fp8 ? (const float*)(h->pool + L.mean_off + L.mean_layer * layer) : nullptr;
     a.table = h->table;
+    const int wl = slot_first * (c.S + 1) + nslots - 1;
+    a.work = (const int32_t*)(h->pool + L.work_off + L.work_stride * wl);
+    a.nwork = h->work_count[wl];
     a.N = L.N; a.heads = c.heads; a.D = c.head_dim; a.pt = c.page_tokens; a.ppc = L.ppc;
     a.T = L.T; a.S = c.S;
     a.slot_first = slot_first; a.nslots = nslots;

@@ -13,8 +13,16 @@
 //   S^T[key][query] = K Q^T      (v_mfma_f32_32x32x16_bf16, K from LDS, Q in VGPRs)
 //   O^T[d][query]  += V^T P^T    (V^T from LDS, P^T from the S^T accumulators)
 // so a lane owns one query row throughout: the softmax max and sum are in-lane
-// except one exchange between the two 32-lane halves.
+// except one exchange between the two 32-lane halves (v_permlane32_swap).
+//
+// Tiles arrive by LDS DMA (buffer_load ... lds): each instruction moves 1 KB
+// of contiguous page memory, keys past the legal prefix read out of range and
+// land as zeros. K runs one tile ahead of V so that S(t+1) = K(t+1) Q^T is
+// issued while the softmax of tile t runs, and PV(t) while the row max of
+// tile t+1 runs.
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 
 #include "wf_internal.h"
 
@@ -22,20 +30,27 @@ namespace wf {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr int BM = 128;         // query rows per workgroup
+constexpr int BM = kAttnBM;     // query rows per workgroup
 constexpr int BN = 64;          // keys per tile
 constexpr int kRescaleLog2 = 8; // running max may lag the true max by up to 2^8
+constexpr uint32_t kOOB = 0x80000000u;   // buffer offset past every region: loads zeros
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
-    bf2 r = {(__bf16)lo, (__bf16)hi};
+    bf16x2 r = {(__bf16)lo, (__bf16)hi};
     return __builtin_bit_cast(uint32_t, r);
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
+
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, const void* lds, uint32_t voff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, voff, 0, 0, 0);
+}
 
 // Position of a flat context key index, tracked incrementally tile by tile.
 struct KeyCursor {
@@ -62,33 +77,37 @@ struct KeyCursor {
 
 template <int D>
 __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
-    constexpr int KST = D + 8;     // K tile row stride in LDS (elements), 16B pad
-    constexpr int VST = BN + 8;    // V^T tile row stride in LDS
-    constexpr int KSTEPS = D / 16; // MFMA k-steps of QK^T
-    constexpr int DB = D / 32;     // 32-wide d blocks of the output
-    constexpr int CPR = D / 8;     // 16-byte vectors per K row
-    constexpr int KRT = D / 32;    // consecutive K rows a thread loads per tile
-    constexpr int VCT = D / 32;    // V^T vectors a thread loads per tile
+    constexpr int DC = D / 8;       // 16-byte channel vectors per key
+    constexpr int KSTEPS = D / 16;  // MFMA k-steps of QK^T
+    constexpr int DB = D / 32;      // 32-wide d blocks of the output
+    constexpr int TILE = BN * D;    // bf16 elements of one K or V tile
+    constexpr int KDMA = DC / 4;    // K DMA instructions per wave per tile
+    constexpr int VDH = D / 64;     // 64-channel halves of a V key-chunk
 
-    __shared__ __align__(16) uint16_t klds[2][BN * KST];
-    __shared__ __align__(16) uint16_t vlds[2][D * VST];
+    // K tile: [channel vector dc][key][8]; V tile: [key chunk kc][d][8]. Four
+    // separate arrays, selected by compile-time buffer indices, so the
+    // compiler can tell the tile being filled by DMA from the one being read
+    // and does not wait for the DMA before reading.
+    __shared__ __align__(16) uint16_t k0lds[TILE];
+    __shared__ __align__(16) uint16_t k1lds[TILE];
+    __shared__ __align__(16) uint16_t v0lds[TILE];
+    __shared__ __align__(16) uint16_t v1lds[TILE];
     __shared__ int ptab[kMaxTablePages];
 
     const int tid = threadIdx.x;
-    int w = blockIdx.x;
-    const int per_slot = a.heads * a.qtiles;
-    const int sr = w / per_slot;
-    w -= sr * per_slot;
-    const int head = w / a.qtiles;
-    const int qt = w - head * a.qtiles;
-    const int s = a.slot_first + sr;
+    const int32_t unit = a.work[blockIdx.x];
+    if (unit < 0) return;                          // padding of the per-XCD work lists
+    const int s = work_slot(unit);
+    const int head = work_head(unit);
+    const int qt = work_qtile(unit);
     const int N = a.N, pt = a.pt, ppc = a.ppc;
     const int nkeys = (a.T - s) * N;               // legal prefix of slot s
     const int ntiles = (nkeys + BN - 1) / BN;
 
     for (int i = tid; i < a.T * ppc; i += 256) ptab[i] = a.table[i];
 
-    const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
     const int qrow = qt * BM + wave * 32 + l32;
 
     // Q^T operand fragments: lane holds Q[qrow][16*ks + 8*hf .. +7]
@@ -104,58 +123,46 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
         }
     }
 
-    const uint16_t* kpage = static_cast<const uint16_t*>(a.kpage);
-    const uint16_t* vpage = a.vpage;
-    const int64_t head_stride_k = (int64_t)pt * D;     // one (page, head) block of K
-    const int kr0 = KRT * (tid / CPR);                   // first K row of this thread
-    const int kdc = tid % CPR;
-    const int vkc = tid & 7;                             // 8-key group of this thread
-    const int vdd = tid >> 3;                            // first V^T row of this thread
-    KeyCursor kc, vc;
-    kc.init(kr0, N, pt);
-    vc.init(8 * vkc, N, pt);
+    const __amdgpu_buffer_rsrc_t krs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(a.kpage), (short)0, a.kbytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t vrs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.vpage), (short)0, a.vbytes, 0x00020000);
+    const int64_t head_blk = (int64_t)pt * D;      // elements of one (page, head) block
+    KeyCursor kcur, vcur0, vcur1;
+    kcur.init(lane, N, pt);                        // K: lane loads key row `lane` of each tile
+    vcur0.init(8 * (2 * wave), N, pt);             // V: this wave loads key chunks 2w, 2w+1
+    vcur1.init(8 * (2 * wave + 1), N, pt);
 
-    uint4 kreg[KRT], vreg[VCT];
-    auto load_tile = [&]() {
-        if (kc.g < nkeys) {
-            const int phys = ptab[kc.p * ppc + kc.pg];
-            const uint16_t* src = kpage + ((int64_t)phys * a.heads + head) * head_stride_k +
-                                  (int64_t)kc.tok * D + kdc * 8;
-#pragma unroll
-            for (int i = 0; i < KRT; ++i) kreg[i] = *reinterpret_cast<const uint4*>(src + i * D);
-        } else {
-#pragma unroll
-            for (int i = 0; i < KRT; ++i) kreg[i] = make_uint4(0, 0, 0, 0);
+    __syncthreads();                               // ptab visible
+
+    auto dma_k = [&](auto bufc) {
+        uint16_t* kl = decltype(bufc)::value ? k1lds : k0lds;
+        uint32_t off = kOOB;
+        if (kcur.g < nkeys) {
+            const int phys = ptab[kcur.p * ppc + kcur.pg];
+            off = (uint32_t)((((int64_t)phys * a.heads + head) * head_blk + (int64_t)kcur.tok * 8) * 2);
         }
-        if (vc.g < nkeys) {
-            const int phys = ptab[vc.p * ppc + vc.pg];
-            const uint16_t* src = vpage + ((int64_t)phys * a.heads + head) * (int64_t)D * pt + vc.tok;
 #pragma unroll
-            for (int i = 0; i < VCT; ++i)
-                vreg[i] = *reinterpret_cast<const uint4*>(src + (int64_t)(vdd + 32 * i) * pt);
-        } else {
-#pragma unroll
-            for (int i = 0; i < VCT; ++i) vreg[i] = make_uint4(0, 0, 0, 0);
+        for (int i = 0; i < KDMA; ++i) {
+            const int dc = wave * KDMA + i;
+            dma16(krs, kl + dc * BN * 8, off == kOOB ? kOOB : off + (uint32_t)(dc * pt * 16));
         }
-        kc.step(BN, pt, ppc);
+        kcur.step(BN, pt, ppc);
+    };
+    auto dma_v_chunk = [&](uint16_t* vl, KeyCursor& vc, int kc) {
+        const bool ok = vc.g < nkeys;
+        const int phys = ok ? ptab[vc.p * ppc + vc.pg] : 0;
+        const uint32_t base =
+            (uint32_t)((((int64_t)phys * a.heads + head) * head_blk + (int64_t)vc.tok * D) * 2);
+#pragma unroll
+        for (int h = 0; h < VDH; ++h)
+            dma16(vrs, vl + (kc * D + 64 * h) * 8, ok ? base + (uint32_t)((64 * h + lane) * 16) : kOOB);
         vc.step(BN, pt, ppc);
     };
-    // V^T rows are stored with keys permuted inside each 16-key group so that
-    // lane half hf reads its 8 keys {4hf..4hf+3, 8+4hf..8+4hf+3} as one vector:
-    // position 8h+i holds key 4h+i, position 8h+4+i holds key 8+4h+i.
-    auto store_tile = [&](int buf) {
-        uint16_t* kl = klds[buf];
-#pragma unroll
-        for (int i = 0; i < KRT; ++i)
-            *reinterpret_cast<uint4*>(kl + (kr0 + i) * KST + kdc * 8) = kreg[i];
-        uint16_t* vl = vlds[buf];
-        const int g16 = vkc >> 1, half = vkc & 1;
-#pragma unroll
-        for (int i = 0; i < VCT; ++i) {
-            uint16_t* row = vl + (vdd + 32 * i) * VST + 16 * g16;
-            *reinterpret_cast<uint2*>(row + 4 * half) = make_uint2(vreg[i].x, vreg[i].y);
-            *reinterpret_cast<uint2*>(row + 8 + 4 * half) = make_uint2(vreg[i].z, vreg[i].w);
-        }
+    auto dma_v = [&](auto bufc) {
+        uint16_t* vl = decltype(bufc)::value ? v1lds : v0lds;
+        dma_v_chunk(vl, vcur0, 2 * wave);
+        dma_v_chunk(vl, vcur1, 2 * wave + 1);
     };
 
     f32x16 oacc[DB];
@@ -164,52 +171,47 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
         for (int j = 0; j < 16; ++j) oacc[db][j] = 0.f;
     float m_run = -INFINITY;   // running max of raw scores (may lag by < 2^8 in exp2 units)
-    float l_run = 0.f;         // this lane's partial row sum
+    float l_run = 0.f;         // this lane's partial row sum (of the bf16-rounded weights)
     const bf16x2 kOnes = {(__bf16)1.0f, (__bf16)1.0f};
     const float c = a.scale_log2;
 
-    __syncthreads();           // ptab visible
-    load_tile();
-    store_tile(0);
-    __syncthreads();
-
-    for (int t = 0; t < ntiles; ++t) {
-        const int buf = t & 1;
-        const bool more = t + 1 < ntiles;
-        if (more) load_tile();
-
-        // S^T = K Q^T for two 32-key blocks
-        f32x16 sacc[2];
-        const uint16_t* kl = klds[buf];
+    auto compute_s = [&](auto bufc, f32x16 (&S)[2]) {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int j = 0; j < 16; ++j) sacc[kb][j] = 0.f;
-            const uint16_t* krow = kl + (32 * kb + l32) * KST + 8 * hf;
+            for (int j = 0; j < 16; ++j) S[kb][j] = 0.f;
+        const uint16_t* kl = decltype(bufc)::value ? k1lds : k0lds;
 #pragma unroll
-            for (int ks = 0; ks < KSTEPS; ++ks) {
-                const bf16x8 ka = as_bf16x8(*reinterpret_cast<const uint4*>(krow + 16 * ks));
-                sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ks], sacc[kb], 0, 0, 0);
+        for (int ks = 0; ks < KSTEPS; ++ks)
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                const bf16x8 ka = as_bf16x8(
+                    *reinterpret_cast<const uint4*>(kl + ((2 * ks + hf) * BN + 32 * kb + l32) * 8));
+                S[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ks], S[kb], 0, 0, 0);
             }
-        }
-        // keys past the legal prefix (last tile only)
-        const int kbase = t * BN;
+    };
+    // Row max of tile `tile` (keys past the prefix set to -inf), then the
+    // running-max update; O and l are rescaled only when the max grows by more
+    // than 2^8 in exp2 units (a wave-uniform, rare branch).
+    auto update_max = [&](f32x16 (&S)[2], int tile) {
+        const int kbase = tile * BN;
         if (kbase + BN > nkeys) {
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int j = 0; j < 16; ++j) {
                     const int key = 32 * kb + 8 * (j >> 2) + 4 * hf + (j & 3);
-                    if (kbase + key >= nkeys) sacc[kb][j] = -INFINITY;
+                    if (kbase + key >= nkeys) S[kb][j] = -INFINITY;
                 }
         }
-        // online softmax, one query row per lane (pair of lanes l, l+32)
-        float mx = sacc[0][0];
+        float mx = S[0][0];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sacc[kb][j]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
+            for (int j = 0; j < 16; ++j) mx = fmaxf(mx, S[kb][j]);
+        const uint32_t mb = __float_as_uint(mx);
+        const auto sw = __builtin_amdgcn_permlane32_swap(mb, mb, false, false);
+        mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
         const float m_new = fmaxf(m_run, mx);
         if (__any((m_new - m_run) * c > (float)kRescaleLog2)) {
             const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);
@@ -220,40 +222,80 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
                 for (int j = 0; j < 16; ++j) oacc[db][j] *= alpha;
         }
-        // P is rounded to bf16 for the PV product; the row sum adds the same
-        // rounded values (v_dot2 with (1, 1)), so the weights actually applied
-        // to V are normalised exactly.
+    };
+    // P = exp2(S*c - m*c) rounded to bf16; the row sum adds the same rounded
+    // values (v_dot2 with (1, 1)) so the weights applied to V are normalised
+    // exactly. The S^T accumulator gives lane half h keys {4h..4h+3, 8+4h..}
+    // of each 16-key group; two v_permlane32_swap per group put them in
+    // natural order (half 0 keys 0-7, half 1 keys 8-15), matching V^T in LDS.
+    auto exp_pack = [&](f32x16 (&S)[2], bf16x8 (&P)[4]) {
         const float mb = m_run * c;
-        uint32_t pk[2][8];
+        uint32_t w[2][8];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int j = 0; j < 16; j += 2) {
-                const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][j], c, -mb));
-                const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][j + 1], c, -mb));
-                pk[kb][j >> 1] = pack_bf16x2(p0, p1);
-                l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[kb][j >> 1]),
+                const float p0 = __builtin_amdgcn_exp2f(fmaf(S[kb][j], c, -mb));
+                const float p1 = __builtin_amdgcn_exp2f(fmaf(S[kb][j + 1], c, -mb));
+                w[kb][j >> 1] = pack_bf16x2(p0, p1);
+                l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[kb][j >> 1]),
                                                         kOnes, l_run, false);
             }
-        // O^T += V^T P^T over four 16-key groups
-        const uint16_t* vl = vlds[buf];
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const uint32_t* src = pk[g >> 1] + 4 * (g & 1);
-            const bf16x8 pb = as_bf16x8(make_uint4(src[0], src[1], src[2], src[3]));
+        for (int G = 0; G < 4; ++G) {
+            const uint32_t* src = w[G >> 1] + 4 * (G & 1);
+            const auto x = __builtin_amdgcn_permlane32_swap(src[0], src[2], false, false);
+            const auto y = __builtin_amdgcn_permlane32_swap(src[1], src[3], false, false);
+            P[G] = as_bf16x8(make_uint4(x[0], y[0], x[1], y[1]));
+        }
+    };
+    auto compute_pv = [&](auto bufc, const bf16x8 (&P)[4]) {
+        const uint16_t* vl = decltype(bufc)::value ? v1lds : v0lds;
+#pragma unroll
+        for (int G = 0; G < 4; ++G)
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
                 const bf16x8 va = as_bf16x8(
-                    *reinterpret_cast<const uint4*>(vl + (32 * db + l32) * VST + 16 * g + 8 * hf));
-                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, oacc[db], 0, 0, 0);
+                    *reinterpret_cast<const uint4*>(vl + ((2 * G + hf) * D + 32 * db + l32) * 8));
+                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, P[G], oacc[db], 0, 0, 0);
             }
-        }
-        if (more) store_tile(buf ^ 1);
+    };
+    // One pipeline step for tile t (buffer parity B = t % 2): K(t+2) and
+    // V(t+1) are fetched while S(t+1) is computed next to the softmax of tile
+    // t, then PV(t) runs next to the max of tile t+1. S(t+1) is computed even
+    // past the last tile (from stale LDS, never used) so that its MFMAs share
+    // a basic block with the softmax.
+    using B0 = std::integral_constant<int, 0>;
+    using B1 = std::integral_constant<int, 1>;
+    auto step = [&](int t, auto bcur, auto bnext, f32x16 (&Scur)[2], f32x16 (&Snext)[2]) {
         __syncthreads();
+        if (t + 2 < ntiles) dma_k(bcur);
+        if (t + 1 < ntiles) dma_v(bnext);
+        bf16x8 P[4];
+        compute_s(bnext, Snext);
+        exp_pack(Scur, P);
+        compute_pv(bcur, P);
+        if (t + 1 < ntiles) update_max(Snext, t + 1);
+        wait_vmem();
+    };
+
+    f32x16 SA[2], SB[2];
+    dma_k(B0{});
+    dma_v(B0{});
+    if (ntiles > 1) dma_k(B1{});
+    wait_vmem();
+    __syncthreads();
+    compute_s(B0{}, SA);
+    update_max(SA, 0);
+    for (int t = 0; t < ntiles; t += 2) {
+        step(t, B0{}, B1{}, SA, SB);
+        if (t + 1 < ntiles) step(t + 1, B1{}, B0{}, SB, SA);
     }
 
     // normalise and store: lane holds O[qrow][32*db + 8*(j/4) + 4*hf + j%4]
-    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    const uint32_t lb = __float_as_uint(l_run);
+    const auto lsw = __builtin_amdgcn_permlane32_swap(lb, lb, false, false);
+    const float l_tot = __uint_as_float(lsw[0]) + __uint_as_float(lsw[1]);
     const float inv = 1.0f / l_tot;
     if (qrow < N) {
         const int64_t obase = (((int64_t)s * N + qrow) * a.heads + head) * D + 4 * hf;
@@ -285,8 +327,8 @@ hipError_t launch_attention(const AttnArgs& a0, bool fp8, hipStream_t st) {
     if (fp8) return hipErrorNotSupported;
     AttnArgs a = a0;
     a.qtiles = (a.N + BM - 1) / BM;
-    const int64_t blocks = (int64_t)a.nslots * a.heads * a.qtiles;
-    if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+    const int64_t blocks = a.nwork;
+    if (blocks <= 0 || blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
     if (a.D == 128)
         hipLaunchKernelGGL(attn_bf16_kernel<128>, dim3((unsigned)blocks), dim3(256), 0, st, a);
     else if (a.D == 64)

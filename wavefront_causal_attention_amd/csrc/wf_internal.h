@@ -9,6 +9,27 @@ namespace wf {
 constexpr int kMaxSlots = 64;      // context positions per round (bit per position)
 constexpr int kMaxTablePages = 1024;  // T * pages_per_chunk, staged in LDS by attention
 constexpr int kFp8Block = 64;      // tokens per fp8 scale block (restarts at each chunk)
+constexpr int kAttnBM = 128;       // query rows per attention workgroup
+constexpr int kXcds = 8;           // MI355X: workgroup b runs on XCD b % 8
+
+// Work-list entry of one attention workgroup: (slot, head, query tile), or -1.
+__host__ __device__ inline int32_t pack_work(int s, int h, int q) { return (s << 26) | (h << 16) | q; }
+__host__ __device__ inline int work_slot(int32_t w) { return (w >> 26) & 63; }
+__host__ __device__ inline int work_head(int32_t w) { return (w >> 16) & 1023; }
+__host__ __device__ inline int work_qtile(int32_t w) { return w & 0xFFFF; }
+
+// Page formats (per layer, physical page `phys`, head `h`, page token `t`,
+// channel `d`). Both are made of 16-byte vectors of 8 bf16 values so that one
+// 64-lane LDS-DMA instruction moves 1 KB of contiguous memory:
+//   K: [phys][h][D/8][page_tokens][8]   element (t, d) at ((d/8)*pt + t)*8 + d%8
+//   V: [phys][h][page_tokens/8][D][8]   element (t, d) at ((t/8)*D + d)*8 + t%8
+// Physical page of (context position p, page i of its chunk) = table[p*ppc + i].
+__host__ __device__ inline int64_t k_elem(int64_t page_head_base, int pt, int t, int d) {
+    return page_head_base + ((int64_t)(d >> 3) * pt + t) * 8 + (d & 7);
+}
+__host__ __device__ inline int64_t v_elem(int64_t page_head_base, int D, int t, int d) {
+    return page_head_base + ((int64_t)(t >> 3) * D + d) * 8 + (t & 7);
+}
 
 // Fused RoPE + publish of `nslots` consecutive slots of one layer.
 struct PublishArgs {
@@ -18,8 +39,8 @@ struct PublishArgs {
     int64_t row_stride;       // elements between consecutive token rows
     void* q_out;              // [S+1][heads][N][D] bf16 or fp8
     float* q_scales;          // [S+1][heads][nblk] (fp8)
-    void* kpage;              // this layer's K pages: [phys][head][tok][D] (bf16 or fp8)
-    uint16_t* vpage;          // this layer's V pages: [phys][head][D][tok] bf16
+    void* kpage;              // this layer's K pages (format above)
+    uint16_t* vpage;          // this layer's V pages (format above)
     float* kscale;            // fp8: [group][head][nblk]
     float* kmean;             // fp8: [group][head][D]
     const int32_t* table;     // page table [T][ppc]
@@ -40,11 +61,14 @@ struct AttnArgs {
     const void* q;            // [S+1][heads][N][D]
     const float* q_scales;    // fp8: [S+1][heads][nblk]
     void* out;                // [S+1][N][heads*D]
-    const void* kpage;        // this layer's K pages
-    const uint16_t* vpage;    // this layer's V pages (transposed per page)
+    const void* kpage;        // this layer's K pages (format above)
+    const uint16_t* vpage;    // this layer's V pages (format above)
+    int32_t kbytes, vbytes;   // bytes of this layer's K / V regions (< 2^31)
     const float* kscale;      // fp8
     const float* kmean;       // fp8
     const int32_t* table;     // [T][ppc]
+    const int32_t* work;      // per-workgroup (slot, head, qtile), -1 = idle
+    int nwork;                // workgroups in the launch (multiple of kXcds)
     int N, heads, D, pt, ppc, T, S;
     int slot_first, nslots;
     int qtiles;               // query tiles per (slot, head)

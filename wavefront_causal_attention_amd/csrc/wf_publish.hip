@@ -6,11 +6,8 @@
 // written straight into the ordered attention slots (paged delivery), so the
 // attention kernel never concatenates or copies context.
 //
-// Pool layout written here (per layer):
-//   K pages [phys_page][head][page_token][D]   (row-major, one 2*D-byte row per token)
-//   V pages [phys_page][head][D][page_token]   (transposed: 8 consecutive tokens of
-//                                               one channel form a 16-byte vector)
-// Physical page of (context position p, page i of its chunk) = table[p*ppc + i].
+// Page formats written here are described in wf_internal.h (16-byte vectors,
+// K channel-chunk major, V token-chunk major).
 #include <hip/hip_runtime.h>
 
 #include "wf_internal.h"
@@ -69,12 +66,16 @@ __device__ __forceinline__ void rope8(float* x, int c0, const float2* ttab_f, co
     }
 }
 
-// grid: (ceil(N/64), heads, nslots); block 256
+// grid: (ceil(N/64), heads, nslots); block 256. One block rotates and
+// publishes 64 tokens of one head of one slot. Reads run along channels
+// (coalesced rows of the projection output); page writes run along tokens, so
+// K and V are transposed through LDS.
 template <int D, bool IN_FP32>
 __global__ __launch_bounds__(256) void publish_bf16_kernel(PublishArgs a) {
     constexpr int CPR = D / 8;                       // 8-channel vectors per token row
     __shared__ float2 ttab[kMaxFramesPerTile][32];   // time-axis (cos, sin), this tile's frames
-    __shared__ __align__(16) uint16_t vt[D][kTokTile + 8];
+    __shared__ __align__(16) uint4 kst[CPR * kTokTile];       // K vectors, [ch][tok ^ (ch & 7)]
+    __shared__ __align__(16) uint16_t vst[kTokTile * D];      // V rows, [tok][d]
 
     const int tid = threadIdx.x;
     const int sr = blockIdx.z;
@@ -100,7 +101,6 @@ __global__ __launch_bounds__(256) void publish_bf16_kernel(PublishArgs a) {
 
     const int64_t row0 = (int64_t)sr * a.N;
     const int64_t col = (int64_t)head * D;
-    // Q and K: rotate, write Q rows and K page rows
     for (int c = tid; c < kTokTile * CPR; c += 256) {
         const int tk = c / CPR, ch = c - tk * CPR;
         const int n = n0 + tk;
@@ -115,11 +115,7 @@ __global__ __launch_bounds__(256) void publish_bf16_kernel(PublishArgs a) {
         float x[8];
         load8<IN_FP32>(a.k, e, x);
         rope8(x, ch * 8, tf, hrow, wrow, a.dt, a.dh);
-        const int pg = n / a.pt, tok = n - pg * a.pt;
-        const int phys = a.table[p * a.ppc + pg];
-        uint16_t* kp = static_cast<uint16_t*>(a.kpage) +
-                       (((int64_t)phys * a.heads + head) * a.pt + tok) * D + ch * 8;
-        *reinterpret_cast<uint4*>(kp) = pack8(x);
+        kst[ch * kTokTile + (tk ^ (ch & 7))] = pack8(x);
         if (a.q) {
             load8<IN_FP32>(a.q, e, x);
             rope8(x, ch * 8, tf, hrow, wrow, a.dt, a.dh);
@@ -127,26 +123,37 @@ __global__ __launch_bounds__(256) void publish_bf16_kernel(PublishArgs a) {
                            (((int64_t)s * a.heads + head) * a.N + n) * D + ch * 8;
             *reinterpret_cast<uint4*>(qp) = pack8(x);
         }
-        // V: stage transposed in LDS
         load8<IN_FP32>(a.v, e, x);
-#pragma unroll
-        for (int i = 0; i < 8; i += 2) {
-            const uint32_t w = pack_bf16x2(x[i], x[i + 1]);
-            vt[ch * 8 + i][tk] = (uint16_t)(w & 0xFFFF);
-            vt[ch * 8 + i + 1][tk] = (uint16_t)(w >> 16);
-        }
+        *reinterpret_cast<uint4*>(&vst[tk * D + ch * 8]) = pack8(x);
     }
     __syncthreads();
-    // V^T: 8 tokens of one channel per 16-byte store; N and pages are multiples
-    // of 8 so a group never straddles a page
-    for (int c = tid; c < D * (kTokTile / 8); c += 256) {
-        const int dd = c / (kTokTile / 8), kc = c - dd * (kTokTile / 8);
-        const int n = n0 + kc * 8;
+
+    // K pages: one 16-byte vector (8 channels of one token) per thread, tokens fastest
+    for (int j = tid; j < CPR * kTokTile; j += 256) {
+        const int ch = j / kTokTile, tk = j - ch * kTokTile;
+        const int n = n0 + tk;
         if (n >= a.N) continue;
         const int pg = n / a.pt, tok = n - pg * a.pt;
         const int phys = a.table[p * a.ppc + pg];
-        uint16_t* vp = a.vpage + (((int64_t)phys * a.heads + head) * D + dd) * a.pt + tok;
-        *reinterpret_cast<uint4*>(vp) = *reinterpret_cast<const uint4*>(&vt[dd][kc * 8]);
+        const int64_t base = ((int64_t)phys * a.heads + head) * a.pt * D;
+        *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.kpage) + k_elem(base, a.pt, tok, ch * 8)) =
+            kst[ch * kTokTile + (tk ^ (ch & 7))];
+    }
+    // V pages: one vector of 8 consecutive tokens of one channel per thread,
+    // channels fastest. N and pages are multiples of 8, so a group never
+    // straddles a page.
+    for (int j = tid; j < (kTokTile / 8) * D; j += 256) {
+        const int kc = j / D, d = j - kc * D;
+        const int n = n0 + kc * 8;
+        if (n >= a.N) continue;
+        uint32_t w[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            w[r] = (uint32_t)vst[(kc * 8 + 2 * r) * D + d] | ((uint32_t)vst[(kc * 8 + 2 * r + 1) * D + d] << 16);
+        const int pg = n / a.pt, tok = n - pg * a.pt;
+        const int phys = a.table[p * a.ppc + pg];
+        const int64_t base = ((int64_t)phys * a.heads + head) * a.pt * D;
+        *reinterpret_cast<uint4*>(a.vpage + v_elem(base, D, tok, d)) = make_uint4(w[0], w[1], w[2], w[3]);
     }
 }
 
