@@ -48,6 +48,51 @@ __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+#ifndef WF_SCHED
+#define WF_SCHED 1
+#endif
+#ifndef WF_SCHED_PRE
+#define WF_SCHED_PRE 4
+#endif
+#ifndef WF_SCHED_VS
+#define WF_SCHED_VS 5
+#endif
+#ifndef WF_SCHED_VP
+#define WF_SCHED_VP 2
+#endif
+// Scheduling template for one pipeline step: LDS reads issued ahead, each
+// MFMA of S(t+1) then of PV(t) followed by the next LDS read and a few VALU
+// instructions of the softmax.
+template <int D>
+__device__ __forceinline__ void sched_pipeline() {
+#if WF_SCHED == 1
+    constexpr int NS = 2 * (D / 16);
+    constexpr int NP = 4 * (D / 32);
+    __builtin_amdgcn_sched_group_barrier(0x100, WF_SCHED_PRE, 0);
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, WF_SCHED_VS, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, WF_SCHED_VP, 0);
+    }
+#elif WF_SCHED == 2
+    constexpr int NM = 2 * (D / 16) + 4 * (D / 32);
+    __builtin_amdgcn_sched_group_barrier(0x100, WF_SCHED_PRE, 0);
+#pragma unroll
+    for (int i = 0; i < NM; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, WF_SCHED_VS, 0);
+    }
+#endif
+}
+
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, const void* lds, uint32_t voff) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, voff, 0, 0, 0);
 }
@@ -109,6 +154,13 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
     const int qrow = qt * BM + wave * 32 + l32;
+    const __amdgpu_buffer_rsrc_t krs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(a.kpage), (short)0, a.kbytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t vrs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.vpage), (short)0, a.vbytes, 0x00020000);
+    const int64_t head_blk = (int64_t)pt * D;      // elements of one (page, head) block
+    const bf16x2 kOnes = {(__bf16)1.0f, (__bf16)1.0f};
+    const float c = a.scale_log2;
 
     // Q^T operand fragments: lane holds Q[qrow][16*ks + 8*hf .. +7]
     bf16x8 qf[KSTEPS];
@@ -123,11 +175,6 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
         }
     }
 
-    const __amdgpu_buffer_rsrc_t krs =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(a.kpage), (short)0, a.kbytes, 0x00020000);
-    const __amdgpu_buffer_rsrc_t vrs =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.vpage), (short)0, a.vbytes, 0x00020000);
-    const int64_t head_blk = (int64_t)pt * D;      // elements of one (page, head) block
     KeyCursor kcur, vcur0, vcur1;
     kcur.init(lane, N, pt);                        // K: lane loads key row `lane` of each tile
     vcur0.init(8 * (2 * wave), N, pt);             // V: this wave loads key chunks 2w, 2w+1
@@ -135,8 +182,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
 
     __syncthreads();                               // ptab visible
 
-    auto dma_k = [&](auto bufc) {
-        uint16_t* kl = decltype(bufc)::value ? k1lds : k0lds;
+    auto dma_k = [&](uint16_t* kl) {
         uint32_t off = kOOB;
         if (kcur.g < nkeys) {
             const int phys = ptab[kcur.p * ppc + kcur.pg];
@@ -159,8 +205,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
             dma16(vrs, vl + (kc * D + 64 * h) * 8, ok ? base + (uint32_t)((64 * h + lane) * 16) : kOOB);
         vc.step(BN, pt, ppc);
     };
-    auto dma_v = [&](auto bufc) {
-        uint16_t* vl = decltype(bufc)::value ? v1lds : v0lds;
+    auto dma_v = [&](uint16_t* vl) {
         dma_v_chunk(vl, vcur0, 2 * wave);
         dma_v_chunk(vl, vcur1, 2 * wave + 1);
     };
@@ -172,15 +217,12 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
         for (int j = 0; j < 16; ++j) oacc[db][j] = 0.f;
     float m_run = -INFINITY;   // running max of raw scores (may lag by < 2^8 in exp2 units)
     float l_run = 0.f;         // this lane's partial row sum (of the bf16-rounded weights)
-    const bf16x2 kOnes = {(__bf16)1.0f, (__bf16)1.0f};
-    const float c = a.scale_log2;
 
-    auto compute_s = [&](auto bufc, f32x16 (&S)[2]) {
+    auto compute_s = [&](const uint16_t* kl, f32x16 (&S)[2]) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int j = 0; j < 16; ++j) S[kb][j] = 0.f;
-        const uint16_t* kl = decltype(bufc)::value ? k1lds : k0lds;
 #pragma unroll
         for (int ks = 0; ks < KSTEPS; ++ks)
 #pragma unroll
@@ -190,19 +232,23 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
                 S[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ks], S[kb], 0, 0, 0);
             }
     };
-    // Row max of tile `tile` (keys past the prefix set to -inf), then the
-    // running-max update; O and l are rescaled only when the max grows by more
-    // than 2^8 in exp2 units (a wave-uniform, rare branch).
-    auto update_max = [&](f32x16 (&S)[2], int tile) {
-        const int kbase = tile * BN;
-        if (kbase + BN > nkeys) {
+    // Row max of tile `tile`, then the running-max update; O and l are
+    // rescaled only when the max grows by more than 2^8 in exp2 units (a
+    // wave-uniform, rare branch). Only the last tile of a prefix can hold keys
+    // past it; the masking variant (maskc = true) is instantiated outside the
+    // main loop only, so the steady-state loop carries no masking code.
+    auto update_max = [&](f32x16 (&S)[2], int tile, auto maskc) {
+        if constexpr (decltype(maskc)::value) {
+            const int lim = nkeys - tile * BN - 4 * hf;     // keys >= lim (lane-relative) are masked
+            if (lim < BN) {
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+                for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                for (int j = 0; j < 16; ++j) {
-                    const int key = 32 * kb + 8 * (j >> 2) + 4 * hf + (j & 3);
-                    if (kbase + key >= nkeys) S[kb][j] = -INFINITY;
-                }
+                    for (int j = 0; j < 16; ++j) {
+                        const int key = 32 * kb + 8 * (j >> 2) + (j & 3);
+                        S[kb][j] = key < lim ? S[kb][j] : -INFINITY;
+                    }
+            }
         }
         float mx = S[0][0];
 #pragma unroll
@@ -249,8 +295,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
             P[G] = as_bf16x8(make_uint4(x[0], y[0], x[1], y[1]));
         }
     };
-    auto compute_pv = [&](auto bufc, const bf16x8 (&P)[4]) {
-        const uint16_t* vl = decltype(bufc)::value ? v1lds : v0lds;
+    auto compute_pv = [&](const uint16_t* vl, const bf16x8 (&P)[4]) {
 #pragma unroll
         for (int G = 0; G < 4; ++G)
 #pragma unroll
@@ -260,36 +305,57 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
                 oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, P[G], oacc[db], 0, 0, 0);
             }
     };
-    // One pipeline step for tile t (buffer parity B = t % 2): K(t+2) and
-    // V(t+1) are fetched while S(t+1) is computed next to the softmax of tile
-    // t, then PV(t) runs next to the max of tile t+1. S(t+1) is computed even
-    // past the last tile (from stale LDS, never used) so that its MFMAs share
-    // a basic block with the softmax.
-    using B0 = std::integral_constant<int, 0>;
-    using B1 = std::integral_constant<int, 1>;
-    auto step = [&](int t, auto bcur, auto bnext, f32x16 (&Scur)[2], f32x16 (&Snext)[2]) {
+    // One pipeline step for tile t: K(t+2) and V(t+1) are fetched (into the
+    // buffers freed last step) while S(t+1) is computed next to the softmax
+    // of tile t, then PV(t) runs next to the max of tile t+1. S(t+1) is
+    // computed even past the last tile (from stale LDS, never used) so that
+    // its MFMAs share a basic block with the softmax.
+    using NoMask = std::integral_constant<bool, false>;
+    using Mask = std::integral_constant<bool, true>;
+    using Main = std::integral_constant<bool, true>;   // tiles t+1, t+2 exist, neither is the last
+    using Tail = std::integral_constant<bool, false>;  // one of the last three steps
+    auto step = [&](int t, const uint16_t* k_next, uint16_t* k_fill, const uint16_t* v_cur,
+                    uint16_t* v_fill, f32x16 (&Scur)[2], f32x16 (&Snext)[2], auto mainc) {
+        constexpr bool kMain = decltype(mainc)::value;
         __syncthreads();
-        if (t + 2 < ntiles) dma_k(bcur);
-        if (t + 1 < ntiles) dma_v(bnext);
+        if (kMain || t + 2 < ntiles) dma_k(k_fill);
+        if (kMain || t + 1 < ntiles) dma_v(v_fill);
         bf16x8 P[4];
-        compute_s(bnext, Snext);
+        compute_s(k_next, Snext);
         exp_pack(Scur, P);
-        compute_pv(bcur, P);
-        if (t + 1 < ntiles) update_max(Snext, t + 1);
+        compute_pv(v_cur, P);
+        if constexpr (kMain) {
+            update_max(Snext, t + 1, NoMask{});
+            sched_pipeline<D>();
+        } else {
+            sched_pipeline<D>();
+            if (t + 1 < ntiles) update_max(Snext, t + 1, Mask{});
+        }
         wait_vmem();
     };
 
     f32x16 SA[2], SB[2];
-    dma_k(B0{});
-    dma_v(B0{});
-    if (ntiles > 1) dma_k(B1{});
+    dma_k(k0lds);
+    dma_v(v0lds);
+    if (ntiles > 1) dma_k(k1lds);
     wait_vmem();
     __syncthreads();
-    compute_s(B0{}, SA);
-    update_max(SA, 0);
-    for (int t = 0; t < ntiles; t += 2) {
-        step(t, B0{}, B1{}, SA, SB);
-        if (t + 1 < ntiles) step(t + 1, B1{}, B0{}, SB, SA);
+    compute_s(k0lds, SA);
+    update_max(SA, 0, Mask{});
+    int t = 0;
+    // steady state: the next tile is never the last one, buffers are fixed
+    // per parity (tile t in K/V buffer t % 2)
+    for (; t + 3 < ntiles; t += 2) {
+        step(t, k1lds, k0lds, v0lds, v1lds, SA, SB, Main{});
+        step(t + 1, k0lds, k1lds, v1lds, v0lds, SB, SA, Main{});
+    }
+    // last one to three tiles
+    for (; t < ntiles; ++t) {
+        const bool odd = t & 1;
+        step(t, odd ? k0lds : k1lds, odd ? k1lds : k0lds, odd ? v1lds : v0lds, odd ? v0lds : v1lds,
+             SA, SB, Tail{});
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) SA[kb] = SB[kb];
     }
 
     // normalise and store: lane holds O[qrow][32*db + 8*(j/4) + 4*hf + j%4]
