@@ -165,8 +165,11 @@ int wf_round_index(const wf_handle* h, int64_t* k);
 int wf_schedule_chunk_ids(const wf_handle* h, int64_t* ids /* [T] */);
 int wf_page_table_host(const wf_handle* h, int32_t* table /* [T * pages_per_chunk] */);
 int wf_ready_mask(const wf_handle* h, int32_t layer, uint64_t* mask /* bit p = position p */);
-int wf_geometry(const wf_handle* h, int64_t* out /* [8]: N, T, pages_per_chunk, pool
-                 K offset, pool V offset, K bytes per layer, V bytes per layer, fp8 meta offset */);
+/* Pool geometry, out[12]: N, T, pages_per_chunk, K region offset, V region
+ * offset, K bytes per layer, V bytes per layer, fp8 K-scale region offset,
+ * K-scale bytes per layer, fp8 K-mean region offset, K-mean bytes per layer,
+ * 64-token blocks per chunk. Byte offsets are into the pool. */
+int wf_geometry(const wf_handle* h, int64_t* out);
 const char* wf_status_string(int status);
 const char* wf_last_error(const wf_handle* h);
 

@@ -193,9 +193,10 @@ def wf_ready_mask(h, layer: int) -> int:
 
 
 def wf_geometry(h):
-    arr = (ctypes.c_int64 * 8)()
+    arr = (ctypes.c_int64 * 12)()
     _check(load().wf_geometry(h, ctypes.cast(arr, ctypes.c_void_p)), "wf_geometry")
-    keys = ["N", "T", "ppc", "k_off", "v_off", "k_layer_bytes", "v_layer_bytes", "meta_off"]
+    keys = ["N", "T", "ppc", "k_off", "v_off", "k_layer_bytes", "v_layer_bytes", "kscale_off",
+            "kscale_layer_bytes", "kmean_off", "kmean_layer_bytes", "nblk"]
     return dict(zip(keys, list(arr)))
 
 

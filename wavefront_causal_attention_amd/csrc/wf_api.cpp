@@ -22,8 +22,8 @@ struct Layout {
     int N = 0, T = 0, R = 0, ppc = 0, nblk = 0;
     size_t k_layer = 0, v_layer = 0;       // bytes per layer
     size_t k_off = 0, v_off = 0;           // region offsets
-    size_t scale_off = 0, mean_off = 0;    // fp8 metadata
-    size_t scale_layer = 0, mean_layer = 0;
+    size_t scale_off = 0, mean_off = 0, part_off = 0;        // fp8 metadata
+    size_t scale_layer = 0, mean_layer = 0, part_layer = 0;
     size_t htab_off = 0, wtab_off = 0, omega_off = 0;
     size_t work_off = 0, work_stride = 0;  // attention work lists, one per slot range
     int work_len = 0;                      // entries per list
@@ -105,10 +105,15 @@ int validate(const wf_config* c, Layout* L) {
     L->k_off = off;  off += L->k_layer * c->num_layers;
     L->v_off = off;  off += L->v_layer * c->num_layers;
     if (fp8) {
-        L->scale_layer = align_up((size_t)T * c->heads * L->nblk * 4, 256);
+        // K scale per token (its 64-token block's scale, replicated), K mean
+        // per (group, head), and per-64-token partial sums of the mean
+        L->scale_layer = align_up(pages * c->heads * c->page_tokens * 4, 256);
         L->mean_layer = align_up((size_t)T * c->heads * c->head_dim * 4, 256);
+        L->part_layer = align_up((size_t)T * c->heads * L->nblk * c->head_dim * 4, 256);
+        if (L->scale_layer >= (1ull << 31)) return WF_E_SHAPE;
         L->scale_off = off;  off += L->scale_layer * c->num_layers;
         L->mean_off = off;   off += L->mean_layer * c->num_layers;
+        L->part_off = off;   off += L->part_layer * c->num_layers;
     }
     L->htab_off = off;  off += align_up((size_t)c->frame_h * (dh / 2) * 8 + 8, 256);
     L->wtab_off = off;  off += align_up((size_t)c->frame_w * (dw / 2) * 8 + 8, 256);
@@ -307,6 +312,7 @@ int wf_kv_publish(wf_handle* h, int32_t layer, int32_t slot_first, int32_t nslot
         a.vpage = (uint16_t*)(h->pool + L.v_off + L.v_layer * layer);
         a.kscale = fp8 ? (float*)(h->pool + L.scale_off + L.scale_layer * layer) : nullptr;
         a.kmean = fp8 ? (float*)(h->pool + L.mean_off + L.mean_layer * layer) : nullptr;
+        a.kpart = fp8 ? (float*)(h->pool + L.part_off + L.part_layer * layer) : nullptr;
         a.table = h->table;
         a.htab = (const float2*)(h->pool + L.htab_off);
         a.wtab = (const float2*)(h->pool + L.wtab_off);
@@ -355,6 +361,7 @@ int wf_attention_round(wf_handle* h, int32_t layer, int32_t slot_first, int32_t 
     a.vbytes = (int32_t)L.v_layer;
     a.kscale = fp8 ? (const float*)(h->pool + L.scale_off + L.scale_layer * layer) : nullptr;
     a.kmean = fp8 ? (const float*)(h->pool + L.mean_off + L.mean_layer * layer) : nullptr;
+    a.sbytes = fp8 ? (int32_t)L.scale_layer : 0;
     a.table = h->table;
     const int wl = slot_first * (c.S + 1) + nslots - 1;
     a.work = (const int32_t*)(h->pool + L.work_off + L.work_stride * wl);
@@ -422,14 +429,11 @@ int wf_ready_mask(const wf_handle* h, int32_t layer, uint64_t* mask) {
 
 int wf_geometry(const wf_handle* h, int64_t* out) {
     if (!h || !out) return WF_E_INVALID_ARG;
-    out[0] = h->L.N;
-    out[1] = h->L.T;
-    out[2] = h->L.ppc;
-    out[3] = (int64_t)h->L.k_off;
-    out[4] = (int64_t)h->L.v_off;
-    out[5] = (int64_t)h->L.k_layer;
-    out[6] = (int64_t)h->L.v_layer;
-    out[7] = (int64_t)h->L.scale_off;
+    const Layout& L = h->L;
+    const int64_t g[12] = {L.N, L.T, L.ppc, (int64_t)L.k_off, (int64_t)L.v_off, (int64_t)L.k_layer,
+                           (int64_t)L.v_layer, (int64_t)L.scale_off, (int64_t)L.scale_layer,
+                           (int64_t)L.mean_off, (int64_t)L.mean_layer, L.nblk};
+    for (int i = 0; i < 12; ++i) out[i] = g[i];
     return WF_OK;
 }
 

@@ -32,6 +32,7 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int BM = kAttnBM;     // query rows per workgroup
@@ -63,10 +64,10 @@ __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" 
 // Scheduling template for one pipeline step: LDS reads issued ahead, each
 // MFMA of S(t+1) then of PV(t) followed by the next LDS read and a few VALU
 // instructions of the softmax.
-template <int D>
+template <int D, bool FP8>
 __device__ __forceinline__ void sched_pipeline() {
 #if WF_SCHED == 1
-    constexpr int NS = 2 * (D / 16);
+    constexpr int NS = FP8 ? 2 * (D / 64) : 2 * (D / 16);
     constexpr int NP = 4 * (D / 32);
     __builtin_amdgcn_sched_group_barrier(0x100, WF_SCHED_PRE, 0);
 #pragma unroll
@@ -82,7 +83,7 @@ __device__ __forceinline__ void sched_pipeline() {
         __builtin_amdgcn_sched_group_barrier(0x002, WF_SCHED_VP, 0);
     }
 #elif WF_SCHED == 2
-    constexpr int NM = 2 * (D / 16) + 4 * (D / 32);
+    constexpr int NM = (FP8 ? 2 * (D / 64) : 2 * (D / 16)) + 4 * (D / 32);
     __builtin_amdgcn_sched_group_barrier(0x100, WF_SCHED_PRE, 0);
 #pragma unroll
     for (int i = 0; i < NM; ++i) {
@@ -95,6 +96,12 @@ __device__ __forceinline__ void sched_pipeline() {
 
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, const void* lds, uint32_t voff) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, voff, 0, 0, 0);
+}
+__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, const void* lds, uint32_t voff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 4, voff, 0, 0, 0);
+}
+__device__ __forceinline__ i32x8 as_i32x8(uint4 a, uint4 b) {
+    return i32x8{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
 }
 
 // Position of a flat context key index, tracked incrementally tile by tile.
@@ -120,8 +127,12 @@ struct KeyCursor {
     }
 };
 
-template <int D>
-__global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
+// FP8: Q and K are e4m3 codes with per-64-token-block scales and the chunk's
+// K mean removed; QK^T runs on v_mfma_f32_32x32x64_f8f6f4 and each raw score
+// becomes s_k * (q8 . k8) + q8 . mean(chunk); the query scale is folded into
+// the softmax's exp2 constant. V and PV stay bf16.
+template <int D, bool FP8>
+__global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
     constexpr int DC = D / 8;       // 16-byte channel vectors per key
     constexpr int KSTEPS = D / 16;  // MFMA k-steps of QK^T
     constexpr int DB = D / 32;      // 32-wide d blocks of the output
@@ -161,10 +172,13 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
     const int64_t head_blk = (int64_t)pt * D;      // elements of one (page, head) block
     const bf16x2 kOnes = {(__bf16)1.0f, (__bf16)1.0f};
     const float c = a.scale_log2;
+    float cl = c;                                  // exp2 constant of this lane's row
 
-    // Q^T operand fragments: lane holds Q[qrow][16*ks + 8*hf .. +7]
-    bf16x8 qf[KSTEPS];
-    {
+    // Q^T operand fragments: lane holds Q[qrow][16*ks + 8*hf .. +7] (bf16) or
+    // the 32 codes Q8[qrow][64*ks + 32*hf .. +31] (fp8)
+    bf16x8 qf[FP8 ? 1 : KSTEPS];
+    i32x8 qf8[FP8 ? D / 64 : 1];
+    if constexpr (!FP8) {
         const uint16_t* qb = static_cast<const uint16_t*>(a.q) +
                              (((int64_t)s * a.heads + head) * N + min(qrow, N - 1)) * D + 8 * hf;
 #pragma unroll
@@ -173,6 +187,18 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
             if (qrow >= N) u = make_uint4(0, 0, 0, 0);
             qf[ks] = as_bf16x8(u);
         }
+    } else {
+        const uint8_t* qb = static_cast<const uint8_t*>(a.q) +
+                            (((int64_t)s * a.heads + head) * N + min(qrow, N - 1)) * D + 32 * hf;
+#pragma unroll
+        for (int ks = 0; ks < D / 64; ++ks) {
+            uint4 u0 = *reinterpret_cast<const uint4*>(qb + 64 * ks);
+            uint4 u1 = *reinterpret_cast<const uint4*>(qb + 64 * ks + 16);
+            if (qrow >= N) u0 = u1 = make_uint4(0, 0, 0, 0);
+            qf8[ks] = as_i32x8(u0, u1);
+        }
+        const float sq = a.q_scales[((int64_t)s * a.heads + head) * a.nblk + min(qrow, N - 1) / kFp8Block];
+        cl = c * sq;
     }
 
     KeyCursor kcur, vcur0, vcur1;
@@ -182,16 +208,32 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
 
     __syncthreads();                               // ptab visible
 
+    const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(FP8 ? a.kscale : nullptr), (short)0, FP8 ? a.sbytes : 0, 0x00020000);
     auto dma_k = [&](uint16_t* kl) {
-        uint32_t off = kOOB;
+        uint32_t off = kOOB, soff = kOOB;
         if (kcur.g < nkeys) {
             const int phys = ptab[kcur.p * ppc + kcur.pg];
-            off = (uint32_t)((((int64_t)phys * a.heads + head) * head_blk + (int64_t)kcur.tok * 8) * 2);
+            const int64_t ph = (int64_t)phys * a.heads + head;
+            off = FP8 ? (uint32_t)(ph * head_blk + (int64_t)kcur.tok * 16)
+                      : (uint32_t)((ph * head_blk + (int64_t)kcur.tok * 8) * 2);
+            soff = (uint32_t)((ph * pt + kcur.tok) * 4);
         }
+        if constexpr (!FP8) {
 #pragma unroll
-        for (int i = 0; i < KDMA; ++i) {
-            const int dc = wave * KDMA + i;
-            dma16(krs, kl + dc * BN * 8, off == kOOB ? kOOB : off + (uint32_t)(dc * pt * 16));
+            for (int i = 0; i < KDMA; ++i) {
+                const int dc = wave * KDMA + i;
+                dma16(krs, kl + dc * BN * 8, off == kOOB ? kOOB : off + (uint32_t)(dc * pt * 16));
+            }
+        } else {
+            // K8 tile [16-channel vector][key][16 B], then the 64 key scales
+            uint8_t* kb8 = reinterpret_cast<uint8_t*>(kl);
+#pragma unroll
+            for (int i = 0; i < D / 64; ++i) {
+                const int v16 = wave * (D / 64) + i;
+                dma16(krs, kb8 + v16 * BN * 16, off == kOOB ? kOOB : off + (uint32_t)(v16 * pt * 16));
+            }
+            if (wave == 0) dma4(srs, kb8 + D * BN, soff);
         }
         kcur.step(BN, pt, ppc);
     };
@@ -223,13 +265,81 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int j = 0; j < 16; ++j) S[kb][j] = 0.f;
+        if constexpr (!FP8) {
 #pragma unroll
-        for (int ks = 0; ks < KSTEPS; ++ks)
+            for (int ks = 0; ks < KSTEPS; ++ks)
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                const bf16x8 ka = as_bf16x8(
-                    *reinterpret_cast<const uint4*>(kl + ((2 * ks + hf) * BN + 32 * kb + l32) * 8));
-                S[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ks], S[kb], 0, 0, 0);
+                for (int kb = 0; kb < 2; ++kb) {
+                    const bf16x8 ka = as_bf16x8(
+                        *reinterpret_cast<const uint4*>(kl + ((2 * ks + hf) * BN + 32 * kb + l32) * 8));
+                    S[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ks], S[kb], 0, 0, 0);
+                }
+        } else {
+            const uint8_t* kb8 = reinterpret_cast<const uint8_t*>(kl);
+#pragma unroll
+            for (int ks = 0; ks < D / 64; ++ks)
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) {
+                    const uint4 u0 = *reinterpret_cast<const uint4*>(kb8 + ((4 * ks + 2 * hf) * BN + 32 * kb + l32) * 16);
+                    const uint4 u1 = *reinterpret_cast<const uint4*>(kb8 + ((4 * ks + 2 * hf + 1) * BN + 32 * kb + l32) * 16);
+                    S[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(as_i32x8(u0, u1), qf8[ks], S[kb],
+                                                                            0, 0, 0, 0, 0, 0);
+                }
+        }
+    };
+    // fp8: per-lane bias q8 . mean(chunk) of the chunk a tile starts in (b0)
+    // and of the next one (b1); recomputed only when tiles enter a new chunk.
+    int bchunk = -1, bend = 0;
+    float b0 = 0.f, b1 = 0.f;
+    auto chunk_bias = [&](int pos) -> float {
+        if (pos >= a.T - s) return 0.f;
+        const int g = ptab[pos * ppc] / ppc;
+        const float* mu = a.kmean + ((int64_t)g * a.heads + head) * D + 32 * hf;
+        float acc = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < D / 64; ++ks)
+#pragma unroll 1
+            for (int w = 0; w < 8; ++w) {
+                const float4 m4 = *reinterpret_cast<const float4*>(mu + 64 * ks + 4 * w);
+                const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(qf8[ks][w], false);
+                const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(qf8[ks][w], true);
+                acc = fmaf(lo[0], m4.x, acc);
+                acc = fmaf(lo[1], m4.y, acc);
+                acc = fmaf(hi[0], m4.z, acc);
+                acc = fmaf(hi[1], m4.w, acc);
+            }
+        const uint32_t ab = __float_as_uint(acc);
+        const auto sw = __builtin_amdgcn_permlane32_swap(ab, ab, false, false);
+        return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    };
+    auto dequant_scores = [&](const uint16_t* kl, f32x16 (&S)[2], int tile) {
+        const int kbase = tile * BN;
+        if (bchunk < 0) {
+            bchunk = 0;
+            bend = N;
+            b0 = chunk_bias(0);
+            b1 = chunk_bias(1);
+        }
+        while (kbase >= bend) {
+            ++bchunk;
+            bend += N;
+            b0 = b1;
+            b1 = chunk_bias(bchunk + 1);
+        }
+        const float* ksc = reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(kl) + D * BN);
+        const int lim = bend - kbase - 4 * hf;         // lane-relative first key of the next chunk
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                const float4 sk = *reinterpret_cast<const float4*>(ksc + 32 * kb + 8 * g4 + 4 * hf);
+                const float skv[4] = {sk.x, sk.y, sk.z, sk.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int key = 32 * kb + 8 * g4 + e;
+                    const float b = key < lim ? b0 : b1;
+                    S[kb][4 * g4 + e] = fmaf(S[kb][4 * g4 + e], skv[e], b);
+                }
             }
     };
     // Row max of tile `tile`, then the running-max update; O and l are
@@ -237,7 +347,8 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
     // wave-uniform, rare branch). Only the last tile of a prefix can hold keys
     // past it; the masking variant (maskc = true) is instantiated outside the
     // main loop only, so the steady-state loop carries no masking code.
-    auto update_max = [&](f32x16 (&S)[2], int tile, auto maskc) {
+    auto update_max = [&](f32x16 (&S)[2], int tile, auto maskc, const uint16_t* kl) {
+        if constexpr (FP8) dequant_scores(kl, S, tile);
         if constexpr (decltype(maskc)::value) {
             const int lim = nkeys - tile * BN - 4 * hf;     // keys >= lim (lane-relative) are masked
             if (lim < BN) {
@@ -259,8 +370,8 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
         const auto sw = __builtin_amdgcn_permlane32_swap(mb, mb, false, false);
         mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
         const float m_new = fmaxf(m_run, mx);
-        if (__any((m_new - m_run) * c > (float)kRescaleLog2)) {
-            const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);
+        if (__any((m_new - m_run) * cl > (float)kRescaleLog2)) {
+            const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * cl);
             m_run = m_new;
             l_run *= alpha;
 #pragma unroll
@@ -275,14 +386,14 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
     // of each 16-key group; two v_permlane32_swap per group put them in
     // natural order (half 0 keys 0-7, half 1 keys 8-15), matching V^T in LDS.
     auto exp_pack = [&](f32x16 (&S)[2], bf16x8 (&P)[4]) {
-        const float mb = m_run * c;
+        const float mb = m_run * cl;
         uint32_t w[2][8];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int j = 0; j < 16; j += 2) {
-                const float p0 = __builtin_amdgcn_exp2f(fmaf(S[kb][j], c, -mb));
-                const float p1 = __builtin_amdgcn_exp2f(fmaf(S[kb][j + 1], c, -mb));
+                const float p0 = __builtin_amdgcn_exp2f(fmaf(S[kb][j], cl, -mb));
+                const float p1 = __builtin_amdgcn_exp2f(fmaf(S[kb][j + 1], cl, -mb));
                 w[kb][j >> 1] = pack_bf16x2(p0, p1);
                 l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[kb][j >> 1]),
                                                         kOnes, l_run, false);
@@ -325,11 +436,11 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
         exp_pack(Scur, P);
         compute_pv(v_cur, P);
         if constexpr (kMain) {
-            update_max(Snext, t + 1, NoMask{});
-            sched_pipeline<D>();
+            update_max(Snext, t + 1, NoMask{}, k_next);
+            sched_pipeline<D, FP8>();
         } else {
-            sched_pipeline<D>();
-            if (t + 1 < ntiles) update_max(Snext, t + 1, Mask{});
+            sched_pipeline<D, FP8>();
+            if (t + 1 < ntiles) update_max(Snext, t + 1, Mask{}, k_next);
         }
         wait_vmem();
     };
@@ -341,7 +452,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
     wait_vmem();
     __syncthreads();
     compute_s(k0lds, SA);
-    update_max(SA, 0, Mask{});
+    update_max(SA, 0, Mask{}, k0lds);
     int t = 0;
     // steady state: the next tile is never the last one, buffers are fixed
     // per parity (tile t in K/V buffer t % 2)
@@ -390,17 +501,20 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
 }  // namespace
 
 hipError_t launch_attention(const AttnArgs& a0, bool fp8, hipStream_t st) {
-    if (fp8) return hipErrorNotSupported;
     AttnArgs a = a0;
     a.qtiles = (a.N + BM - 1) / BM;
     const int64_t blocks = a.nwork;
     if (blocks <= 0 || blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
-    if (a.D == 128)
-        hipLaunchKernelGGL(attn_bf16_kernel<128>, dim3((unsigned)blocks), dim3(256), 0, st, a);
-    else if (a.D == 64)
-        hipLaunchKernelGGL(attn_bf16_kernel<64>, dim3((unsigned)blocks), dim3(256), 0, st, a);
-    else
+    const dim3 grid((unsigned)blocks), block(256);
+    if (a.D == 128) {
+        if (fp8) hipLaunchKernelGGL((attn_kernel<128, true>), grid, block, 0, st, a);
+        else hipLaunchKernelGGL((attn_kernel<128, false>), grid, block, 0, st, a);
+    } else if (a.D == 64) {
+        if (fp8) hipLaunchKernelGGL((attn_kernel<64, true>), grid, block, 0, st, a);
+        else hipLaunchKernelGGL((attn_kernel<64, false>), grid, block, 0, st, a);
+    } else {
         return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 

@@ -23,7 +23,15 @@ __host__ __device__ inline int work_qtile(int32_t w) { return w & 0xFFFF; }
 // 64-lane LDS-DMA instruction moves 1 KB of contiguous memory:
 //   K: [phys][h][D/8][page_tokens][8]   element (t, d) at ((d/8)*pt + t)*8 + d%8
 //   V: [phys][h][page_tokens/8][D][8]   element (t, d) at ((t/8)*D + d)*8 + t%8
+// With fp8 Q/K the K pages hold e4m3 codes in 16-byte vectors of 16 channels:
+//   K8: [phys][h][D/16][page_tokens][16]  byte (t, d) at ((d/16)*pt + t)*16 + d%16
+// plus, per layer, the scale of each token's 64-token block
+// kscale[phys][h][page_tokens] (fp32), the chunk's K channel mean
+// kmean[group][h][D] (fp32) and per-block partial sums kpart[group][h][nblk][D].
 // Physical page of (context position p, page i of its chunk) = table[p*ppc + i].
+__host__ __device__ inline int64_t k8_byte(int64_t page_head_base, int pt, int t, int d) {
+    return page_head_base + ((int64_t)(d >> 4) * pt + t) * 16 + (d & 15);
+}
 __host__ __device__ inline int64_t k_elem(int64_t page_head_base, int pt, int t, int d) {
     return page_head_base + ((int64_t)(d >> 3) * pt + t) * 8 + (d & 7);
 }
@@ -41,8 +49,9 @@ struct PublishArgs {
     float* q_scales;          // [S+1][heads][nblk] (fp8)
     void* kpage;              // this layer's K pages (format above)
     uint16_t* vpage;          // this layer's V pages (format above)
-    float* kscale;            // fp8: [group][head][nblk]
+    float* kscale;            // fp8: per-token K scale [phys][head][pt]
     float* kmean;             // fp8: [group][head][D]
+    float* kpart;             // fp8: [group][head][nblk][D] partial sums
     const int32_t* table;     // page table [T][ppc]
     const float2* htab;       // RoPE row-axis (cos, sin) [frame_h][dh/2]
     const float2* wtab;       // RoPE column-axis (cos, sin) [frame_w][dw/2]
@@ -64,8 +73,9 @@ struct AttnArgs {
     const void* kpage;        // this layer's K pages (format above)
     const uint16_t* vpage;    // this layer's V pages (format above)
     int32_t kbytes, vbytes;   // bytes of this layer's K / V regions (< 2^31)
-    const float* kscale;      // fp8
-    const float* kmean;       // fp8
+    const float* kscale;      // fp8: per-token K scale [phys][head][pt]
+    const float* kmean;       // fp8: [group][head][D]
+    int32_t sbytes;           // fp8: bytes of this layer's kscale region
     const int32_t* table;     // [T][ppc]
     const int32_t* work;      // per-workgroup (slot, head, qtile), -1 = idle
     int nwork;                // workgroups in the launch (multiple of kXcds)

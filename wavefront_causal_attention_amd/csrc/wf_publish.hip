@@ -157,6 +157,219 @@ __global__ __launch_bounds__(256) void publish_bf16_kernel(PublishArgs a) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// fp8 e4m3 publish. Q and K are quantised per 64-token block of their chunk
+// (blocks restart at each chunk start, so a publish block is exactly one
+// quantisation block): scale = absmax / 448, codes = RNE(x / scale) clamped to
+// +-448. K first has its chunk's per-channel mean removed; attention adds the
+// mean back exactly as q . mean. V stays bf16. Three launches, all with fixed
+// summation orders: per-block partial sums of RoPE'd K, their reduction to the
+// chunk mean, then the quantising publish.
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+    return v;
+}
+
+__device__ __forceinline__ uint32_t fp8x4(float a, float b, float c, float d) {
+    // v_cvt_pk_fp8_f32 rounds to nearest even but turns out-of-range values
+    // into NaN, so clamp to the largest finite e4m3 value first
+    a = fminf(fmaxf(a, -448.f), 448.f);
+    b = fminf(fmaxf(b, -448.f), 448.f);
+    c = fminf(fmaxf(c, -448.f), 448.f);
+    d = fminf(fmaxf(d, -448.f), 448.f);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xFFFFu;
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, 0, false) & 0xFFFFu;
+    return lo | (hi << 16);
+}
+
+// Fill the time-axis (cos, sin) table for the frames of one 64-token block.
+__device__ __forceinline__ void fill_ttab(float2 (*ttab)[32], const PublishArgs& a, int sr, int f_lo,
+                                          int nf) {
+    const int hp = a.dt >> 1;
+    for (int i = threadIdx.x; i < nf * hp; i += 256) {
+        const int fi = i / hp, m = i - fi * hp;
+        const double phi = (double)(a.t0[sr] + f_lo + fi) * a.omega_t[m];
+        double sn, cs;
+        sincos(phi, &sn, &cs);
+        ttab[fi][m] = make_float2((float)cs, (float)sn);
+    }
+}
+
+// grid (ceil(N/64), heads, nslots): per 64-token block, the per-channel sum of
+// RoPE'd K over its valid tokens -> kpart[group][head][block][D].
+template <int D, bool IN_FP32>
+__global__ __launch_bounds__(256) void kmean_partial_kernel(PublishArgs a) {
+    constexpr int CPR = D / 8;
+    constexpr int ROWS = 256 / CPR;                  // token lanes per channel vector
+    __shared__ float2 ttab[kMaxFramesPerTile][32];
+    __shared__ float part[ROWS][D];
+    const int tid = threadIdx.x;
+    const int sr = blockIdx.z, s = a.slot_first + sr, head = blockIdx.y, n0 = blockIdx.x * kTokTile;
+    const int p = a.T - 1 - s;
+    const int HW = a.frame_h * a.frame_w;
+    const int f_lo = n0 / HW;
+    const int nf = (min(n0 + kTokTile, a.N) - 1) / HW - f_lo + 1;
+    fill_ttab(ttab, a, sr, f_lo, nf);
+    __syncthreads();
+    const int ch = tid % CPR, row = tid / CPR;
+    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int tk = row; tk < kTokTile; tk += ROWS) {
+        const int n = n0 + tk;
+        if (n >= a.N) break;
+        const int y = (n / a.frame_w) % a.frame_h, xw = n % a.frame_w;
+        float x[8];
+        load8<IN_FP32>(a.k, ((int64_t)sr * a.N + n) * a.row_stride + (int64_t)head * D + ch * 8, x);
+        rope8(x, ch * 8, ttab[n / HW - f_lo], a.htab + y * (a.dh >> 1), a.wtab + xw * (a.dw >> 1), a.dt, a.dh);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] += x[e];
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) part[row][ch * 8 + e] = acc[e];
+    __syncthreads();
+    if (tid < D) {
+        float sum = 0.f;
+        for (int r = 0; r < ROWS; ++r) sum += part[r][tid];
+        const int g = a.table[p * a.ppc] / a.ppc;
+        a.kpart[(((int64_t)g * a.heads + head) * a.nblk + blockIdx.x) * D + tid] = sum;
+    }
+}
+
+// grid (heads, nslots), block D: kmean[group][head][d] = sum of the chunk's
+// block partials (fixed order) / N.
+template <int D>
+__global__ void kmean_reduce_kernel(PublishArgs a) {
+    const int s = a.slot_first + blockIdx.y, head = blockIdx.x, d = threadIdx.x;
+    const int g = a.table[(a.T - 1 - s) * a.ppc] / a.ppc;
+    const float* src = a.kpart + ((int64_t)g * a.heads + head) * a.nblk * D + d;
+    float sum = 0.f;
+    for (int b = 0; b < a.nblk; ++b) sum += src[(int64_t)b * D];
+    a.kmean[((int64_t)g * a.heads + head) * D + d] = sum / (float)a.N;
+}
+
+// grid (ceil(N/64), heads, nslots): quantise and publish one 64-token block.
+template <int D, bool IN_FP32>
+__global__ __launch_bounds__(256) void publish_fp8_kernel(PublishArgs a) {
+    constexpr int CPR = D / 8;                       // 8-channel vectors per token row
+    constexpr int ITEMS = kTokTile * CPR / 256;
+    constexpr int C16 = D / 16;                      // 16-byte code vectors per token row
+    __shared__ float2 ttab[kMaxFramesPerTile][32];
+    __shared__ float mu[D];
+    __shared__ float red[2][4];
+    __shared__ __align__(16) uint8_t kcodes[kTokTile * D];   // [tok][16-byte vector ^ (tok % C16)]
+    __shared__ __align__(16) uint16_t vst[kTokTile * D];     // V rows, [tok][d]
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int sr = blockIdx.z, s = a.slot_first + sr, head = blockIdx.y, n0 = blockIdx.x * kTokTile;
+    const int p = a.T - 1 - s;
+    const int HW = a.frame_h * a.frame_w;
+    const int f_lo = n0 / HW;
+    const int nf = (min(n0 + kTokTile, a.N) - 1) / HW - f_lo + 1;
+    fill_ttab(ttab, a, sr, f_lo, nf);
+    const int g = a.table[p * a.ppc] / a.ppc;
+    if (tid < D) mu[tid] = a.kmean[((int64_t)g * a.heads + head) * D + tid];
+    __syncthreads();
+
+    const int64_t row0 = (int64_t)sr * a.N;
+    const int64_t col = (int64_t)head * D;
+    float kx[ITEMS][8], qx[ITEMS][8];
+    float kmax = 0.f, qmax = 0.f;
+#pragma unroll
+    for (int i = 0; i < ITEMS; ++i) {
+        const int c = tid + 256 * i;
+        const int tk = c / CPR, ch = c - tk * CPR;
+        const int n = n0 + tk;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) kx[i][e] = qx[i][e] = 0.f;
+        if (n >= a.N) continue;
+        const int y = (n / a.frame_w) % a.frame_h, xw = n % a.frame_w;
+        const float2* tf = ttab[n / HW - f_lo];
+        const float2* hrow = a.htab + y * (a.dh >> 1);
+        const float2* wrow = a.wtab + xw * (a.dw >> 1);
+        const int64_t e0 = (row0 + n) * a.row_stride + col + ch * 8;
+        load8<IN_FP32>(a.k, e0, kx[i]);
+        rope8(kx[i], ch * 8, tf, hrow, wrow, a.dt, a.dh);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            kx[i][e] -= mu[ch * 8 + e];
+            kmax = fmaxf(kmax, fabsf(kx[i][e]));
+        }
+        if (a.q) {
+            load8<IN_FP32>(a.q, e0, qx[i]);
+            rope8(qx[i], ch * 8, tf, hrow, wrow, a.dt, a.dh);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) qmax = fmaxf(qmax, fabsf(qx[i][e]));
+        }
+        float v[8];
+        load8<IN_FP32>(a.v, e0, v);
+        *reinterpret_cast<uint4*>(&vst[tk * D + ch * 8]) = pack8(v);
+    }
+    kmax = wave_max(kmax);
+    qmax = wave_max(qmax);
+    if (lane == 0) {
+        red[0][wave] = kmax;
+        red[1][wave] = qmax;
+    }
+    __syncthreads();
+    kmax = fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3]));
+    qmax = fmaxf(fmaxf(red[1][0], red[1][1]), fmaxf(red[1][2], red[1][3]));
+    const float ks = kmax > 0.f ? kmax / 448.f : 1.f;     // per-block scales (IEEE divide)
+    const float qs = qmax > 0.f ? qmax / 448.f : 1.f;
+    const float kinv = 1.f / ks, qinv = 1.f / qs;
+#pragma unroll
+    for (int i = 0; i < ITEMS; ++i) {
+        const int c = tid + 256 * i;
+        const int tk = c / CPR, ch = c - tk * CPR;
+        const int n = n0 + tk;
+        if (n >= a.N) continue;
+        const int v16 = ch >> 1;                     // 16-byte vector of this 8-channel group
+        uint2 kc = make_uint2(fp8x4(kx[i][0] * kinv, kx[i][1] * kinv, kx[i][2] * kinv, kx[i][3] * kinv),
+                              fp8x4(kx[i][4] * kinv, kx[i][5] * kinv, kx[i][6] * kinv, kx[i][7] * kinv));
+        *reinterpret_cast<uint2*>(&kcodes[(tk * C16 + (v16 ^ (tk % C16))) * 16 + (ch & 1) * 8]) = kc;
+        if (a.q) {
+            uint2 qc = make_uint2(fp8x4(qx[i][0] * qinv, qx[i][1] * qinv, qx[i][2] * qinv, qx[i][3] * qinv),
+                                  fp8x4(qx[i][4] * qinv, qx[i][5] * qinv, qx[i][6] * qinv, qx[i][7] * qinv));
+            uint8_t* qp = static_cast<uint8_t*>(a.q_out) + (((int64_t)s * a.heads + head) * a.N + n) * D + ch * 8;
+            *reinterpret_cast<uint2*>(qp) = qc;
+        }
+    }
+    if (a.q && tid == 0) a.q_scales[((int64_t)s * a.heads + head) * a.nblk + blockIdx.x] = qs;
+    __syncthreads();
+
+    // K code pages: one 16-byte vector (16 channels of one token) per thread, tokens fastest
+    for (int j = tid; j < C16 * kTokTile; j += 256) {
+        const int v16 = j / kTokTile, tk = j - v16 * kTokTile;
+        const int n = n0 + tk;
+        if (n >= a.N) continue;
+        const int pg = n / a.pt, tok = n - pg * a.pt;
+        const int phys = a.table[p * a.ppc + pg];
+        const int64_t base = ((int64_t)phys * a.heads + head) * a.pt * D;
+        *reinterpret_cast<uint4*>(static_cast<uint8_t*>(a.kpage) + k8_byte(base, a.pt, tok, v16 * 16)) =
+            *reinterpret_cast<const uint4*>(&kcodes[(tk * C16 + (v16 ^ (tk % C16))) * 16]);
+    }
+    if (tid < kTokTile && n0 + tid < a.N) {
+        const int n = n0 + tid;
+        const int pg = n / a.pt, tok = n - pg * a.pt;
+        const int phys = a.table[p * a.ppc + pg];
+        a.kscale[((int64_t)phys * a.heads + head) * a.pt + tok] = ks;
+    }
+    // V pages as in the bf16 publish
+    for (int j = tid; j < (kTokTile / 8) * D; j += 256) {
+        const int kc = j / D, d = j - kc * D;
+        const int n = n0 + kc * 8;
+        if (n >= a.N) continue;
+        uint32_t w[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            w[r] = (uint32_t)vst[(kc * 8 + 2 * r) * D + d] | ((uint32_t)vst[(kc * 8 + 2 * r + 1) * D + d] << 16);
+        const int pg = n / a.pt, tok = n - pg * a.pt;
+        const int phys = a.table[p * a.ppc + pg];
+        const int64_t base = ((int64_t)phys * a.heads + head) * a.pt * D;
+        *reinterpret_cast<uint4*>(a.vpage + v_elem(base, D, tok, d)) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+}
+
 // table[p][i] = group(p) * ppc + i; group(p) = p for the anchor, otherwise
 // A + ((p - A + ring) mod (T - A)).
 __global__ void page_table_kernel(int32_t* table, int T, int A, int ppc, int64_t ring) {
@@ -176,19 +389,23 @@ hipError_t launch_page_table(int32_t* table, int T, int A, int ppc, int64_t ring
     return hipGetLastError();
 }
 
-hipError_t launch_publish(const PublishArgs& a, bool fp8, hipStream_t st) {
-    if (fp8) return hipErrorNotSupported;
+template <int D, bool IN_FP32>
+hipError_t launch_publish_t(const PublishArgs& a, bool fp8, hipStream_t st) {
     const dim3 grid((a.N + kTokTile - 1) / kTokTile, a.heads, a.nslots);
-    if (a.D == 128) {
-        if (a.in_fp32) hipLaunchKernelGGL((publish_bf16_kernel<128, true>), grid, dim3(256), 0, st, a);
-        else hipLaunchKernelGGL((publish_bf16_kernel<128, false>), grid, dim3(256), 0, st, a);
-    } else if (a.D == 64) {
-        if (a.in_fp32) hipLaunchKernelGGL((publish_bf16_kernel<64, true>), grid, dim3(256), 0, st, a);
-        else hipLaunchKernelGGL((publish_bf16_kernel<64, false>), grid, dim3(256), 0, st, a);
-    } else {
-        return hipErrorInvalidValue;
+    if (!fp8) {
+        hipLaunchKernelGGL((publish_bf16_kernel<D, IN_FP32>), grid, dim3(256), 0, st, a);
+        return hipGetLastError();
     }
+    hipLaunchKernelGGL((kmean_partial_kernel<D, IN_FP32>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((kmean_reduce_kernel<D>), dim3(a.heads, a.nslots), dim3(D), 0, st, a);
+    hipLaunchKernelGGL((publish_fp8_kernel<D, IN_FP32>), grid, dim3(256), 0, st, a);
     return hipGetLastError();
+}
+
+hipError_t launch_publish(const PublishArgs& a, bool fp8, hipStream_t st) {
+    if (a.D == 128) return a.in_fp32 ? launch_publish_t<128, true>(a, fp8, st) : launch_publish_t<128, false>(a, fp8, st);
+    if (a.D == 64) return a.in_fp32 ? launch_publish_t<64, true>(a, fp8, st) : launch_publish_t<64, false>(a, fp8, st);
+    return hipErrorInvalidValue;
 }
 
 }  // namespace wf
