@@ -8,8 +8,8 @@
 // key loop simply stops at the prefix end, so masked slot pairs are skipped as
 // whole tiles and their pages are never read.
 //
-// Per workgroup: 128 query rows of one (slot, head), 4 waves of 32 rows.
-// Per 64-key tile, each wave computes
+// Per workgroup: 256 query rows of one (slot, head), 8 waves of 32 rows, one
+// workgroup per CU. Per 64-key tile, each wave computes
 //   S^T[key][query] = K Q^T      (v_mfma_f32_32x32x16_bf16, K from LDS, Q in VGPRs)
 //   O^T[d][query]  += V^T P^T    (V^T from LDS, P^T from the S^T accumulators)
 // so a lane owns one query row throughout: the softmax max and sum are in-lane
@@ -17,9 +17,17 @@
 //
 // Tiles arrive by LDS DMA (buffer_load ... lds): each instruction moves 1 KB
 // of contiguous page memory, keys past the legal prefix read out of range and
-// land as zeros. K runs one tile ahead of V so that S(t+1) = K(t+1) Q^T is
-// issued while the softmax of tile t runs, and PV(t) while the row max of
-// tile t+1 runs.
+// land as zeros. Every K/V tile brought into LDS feeds all 8 waves (256 query
+// rows), which halves the L2-to-LDS traffic per flop of a 128-row tile. K and
+// V each cycle through NSTG tile buffers: a tile's DMA is issued NSTG-1 steps
+// before it is read, and a step waits only for the previous step's DMA. K runs
+// one tile ahead of V so that S(t+1) = K(t+1) Q^T is issued while the softmax
+// of tile t runs, and PV(t) while the row max of tile t+1 runs.
+//
+// On gfx950 the VALU work of the softmax (exp2, max, bf16 packing, row sums)
+// does not overlap MFMAs on the same SIMD, also across waves, so the step is
+// kept to one MFMA per LDS fragment read and the fewest VALU instructions per
+// score (one FMA + one exp2, a half v_max3, a half v_cvt_pk, a half v_dot2).
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
@@ -36,7 +44,15 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int BM = kAttnBM;     // query rows per workgroup
+constexpr int NW = BM / 32;     // waves per workgroup
+constexpr int NTH = 64 * NW;    // threads per workgroup
 constexpr int BN = 64;          // keys per tile
+#ifndef WF_ATTN_STAGES
+#define WF_ATTN_STAGES 3
+#endif
+constexpr int NSTG = WF_ATTN_STAGES;   // K and V tile buffers each
+static_assert(NSTG >= 2 && NSTG <= 4, "2 to 4 tile stages");
+static_assert(NW >= 4 && NW <= 8 && BM % 32 == 0, "4 to 8 waves of 32 query rows");
 constexpr int kRescaleLog2 = 8; // running max may lag the true max by up to 2^8
 constexpr uint32_t kOOB = 0x80000000u;   // buffer offset past every region: loads zeros
 
@@ -48,6 +64,76 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+template <int N>
+__device__ __forceinline__ void wait_vmem_n() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
+// Wait until at most n (wave-uniform, 0..7) vector memory operations of this
+// wave are outstanding: the n issued last may still be in flight.
+__device__ __forceinline__ void wait_vmem_upto(int n) {
+    switch (n) {
+        case 1: wait_vmem_n<1>(); break;
+        case 2: wait_vmem_n<2>(); break;
+        case 3: wait_vmem_n<3>(); break;
+        case 4: wait_vmem_n<4>(); break;
+        case 5: wait_vmem_n<5>(); break;
+        case 6: wait_vmem_n<6>(); break;
+        case 7: wait_vmem_n<7>(); break;
+        default: wait_vmem(); break;
+    }
+}
+
+// Workgroup barrier for the tile pipeline. __syncthreads() adds a release
+// fence, which waits for every outstanding LDS DMA (vmcnt(0)) and would drain
+// the prefetches in flight; here each wave has already waited for the DMA the
+// next step reads, and its own LDS reads have returned (lgkmcnt(0)), so a bare
+// s_barrier orders the buffers. The memory clobber keeps the compiler from
+// moving LDS or buffer accesses across it.
+__device__ __forceinline__ void tile_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        static_for<I + 1, N>(f);
+    }
+}
+
+// Tile buffers: separate LDS arrays, addressed with compile-time indices in
+// the steady-state loop, so the compiler can tell the buffer a DMA fills from
+// the ones being read and does not wait for the DMA before reading. Sized for
+// the largest head dimension (a K or V tile of 64 keys x 128 bf16 channels).
+constexpr int kTileElems = BN * 128;
+__shared__ __align__(16) uint16_t g_kt0[kTileElems];
+__shared__ __align__(16) uint16_t g_kt1[kTileElems];
+__shared__ __align__(16) uint16_t g_kt2[kTileElems];
+__shared__ __align__(16) uint16_t g_kt3[kTileElems];
+__shared__ __align__(16) uint16_t g_vt0[kTileElems];
+__shared__ __align__(16) uint16_t g_vt1[kTileElems];
+__shared__ __align__(16) uint16_t g_vt2[kTileElems];
+__shared__ __align__(16) uint16_t g_vt3[kTileElems];
+__shared__ int g_ptab[kMaxTablePages];
+
+template <int I>
+__device__ __forceinline__ uint16_t* kbuf() {
+    if constexpr (I == 0) return g_kt0;
+    else if constexpr (I == 1) return g_kt1;
+    else if constexpr (I == 2) return g_kt2;
+    else return g_kt3;
+}
+template <int I>
+__device__ __forceinline__ uint16_t* vbuf() {
+    if constexpr (I == 0) return g_vt0;
+    else if constexpr (I == 1) return g_vt1;
+    else if constexpr (I == 2) return g_vt2;
+    else return g_vt3;
+}
+__device__ __forceinline__ uint16_t* kbuf_rt(int i) {
+    return i == 0 ? kbuf<0>() : i == 1 ? kbuf<1>() : i == 2 ? kbuf<(NSTG > 2 ? 2 : 0)>() : kbuf<(NSTG > 3 ? 3 : 0)>();
+}
+__device__ __forceinline__ uint16_t* vbuf_rt(int i) {
+    return i == 0 ? vbuf<0>() : i == 1 ? vbuf<1>() : i == 2 ? vbuf<(NSTG > 2 ? 2 : 0)>() : vbuf<(NSTG > 3 ? 3 : 0)>();
+}
 
 #ifndef WF_SCHED
 #define WF_SCHED 1
@@ -104,51 +190,42 @@ __device__ __forceinline__ i32x8 as_i32x8(uint4 a, uint4 b) {
     return i32x8{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
 }
 
-// Position of a flat context key index, tracked incrementally tile by tile.
-struct KeyCursor {
-    int g;      // flat key index
-    int p;      // context position (chunk)
-    int pg;     // page within the chunk
-    int tok;    // token within the page
-    __device__ void init(int g0, int N, int pt) {
-        g = g0;
-        p = g0 / N;
-        const int r = g0 - p * N;
-        pg = r / pt;
-        tok = r - pg * pt;
-    }
-    __device__ void step(int n, int pt, int ppc) {
-        g += n;
-        tok += n;
-        while (tok >= pt) {
-            tok -= pt;
-            if (++pg == ppc) { pg = 0; ++p; }
-        }
-    }
+// Unsigned division by a run-time invariant divisor d >= 1 for any 32-bit
+// numerator: multiply by a precomputed 32-bit factor and shift (Granlund and
+// Montgomery, "Division by Invariant Integers using Multiplication", 1994,
+// section 4). Branch-free, so page lookups can be scheduled among MFMAs.
+struct FastDiv {
+    uint32_t m;
+    uint32_t s1, s2;
 };
+__device__ __forceinline__ FastDiv make_fastdiv(uint32_t d) {
+    const uint32_t l = d > 1 ? 32 - __clz(d - 1) : 0;              // ceil(log2 d)
+    const uint64_t m = ((uint64_t)1 << 32) * (((uint64_t)1 << l) - d) / d + 1;
+    return FastDiv{(uint32_t)m, l < 1 ? l : 1u, l > 1 ? l - 1 : 0u};
+}
+__device__ __forceinline__ uint32_t fast_div(uint32_t n, FastDiv f) {
+    const uint32_t t = __umulhi(n, f.m);
+    return (t + ((n - t) >> f.s1)) >> f.s2;
+}
 
 // FP8: Q and K are e4m3 codes with per-64-token-block scales and the chunk's
 // K mean removed; QK^T runs on v_mfma_f32_32x32x64_f8f6f4 and each raw score
 // becomes s_k * (q8 . k8) + q8 . mean(chunk); the query scale is folded into
 // the softmax's exp2 constant. V and PV stay bf16.
 template <int D, bool FP8>
-__global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
+__global__ __launch_bounds__(NTH, NW == 4 ? 2 : 1) void attn_kernel(AttnArgs a) {
     constexpr int DC = D / 8;       // 16-byte channel vectors per key
     constexpr int KSTEPS = D / 16;  // MFMA k-steps of QK^T
     constexpr int DB = D / 32;      // 32-wide d blocks of the output
-    constexpr int TILE = BN * D;    // bf16 elements of one K or V tile
-    constexpr int KDMA = DC / 4;    // K DMA instructions per wave per tile
     constexpr int VDH = D / 64;     // 64-channel halves of a V key-chunk
-
-    // K tile: [channel vector dc][key][8]; V tile: [key chunk kc][d][8]. Four
-    // separate arrays, selected by compile-time buffer indices, so the
-    // compiler can tell the tile being filled by DMA from the one being read
-    // and does not wait for the DMA before reading.
-    __shared__ __align__(16) uint16_t k0lds[TILE];
-    __shared__ __align__(16) uint16_t k1lds[TILE];
-    __shared__ __align__(16) uint16_t v0lds[TILE];
-    __shared__ __align__(16) uint16_t v1lds[TILE];
-    __shared__ int ptab[kMaxTablePages];
+    // DMA instructions per tile: K is [channel vector][key][16 B] with one
+    // instruction per vector (D/8 bf16 or D/16 fp8 vectors), V is [key chunk
+    // of 8][d][8] with one instruction per 64 channels of a chunk (8 * VDH).
+    constexpr int KV = FP8 ? D / 16 : DC;
+    constexpr int KPW = (KV + NW - 1) / NW;          // K instructions per wave (upper bound)
+    constexpr int VCW = 8 / NW;                      // V key chunks per wave
+    static_assert(KV <= NW * KPW && 8 % NW == 0 && D * BN <= kTileElems, "tile split");
+    int* const ptab = g_ptab;
 
     const int tid = threadIdx.x;
     const int32_t unit = a.work[blockIdx.x];
@@ -160,7 +237,7 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
     const int nkeys = (a.T - s) * N;               // legal prefix of slot s
     const int ntiles = (nkeys + BN - 1) / BN;
 
-    for (int i = tid; i < a.T * ppc; i += 256) ptab[i] = a.table[i];
+    for (int i = tid; i < a.T * ppc; i += NTH) ptab[i] = a.table[i];
 
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
@@ -201,55 +278,91 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
         cl = c * sq;
     }
 
-    KeyCursor kcur, vcur0, vcur1;
-    kcur.init(lane, N, pt);                        // K: lane loads key row `lane` of each tile
-    vcur0.init(8 * (2 * wave), N, pt);             // V: this wave loads key chunks 2w, 2w+1
-    vcur1.init(8 * (2 * wave + 1), N, pt);
+    // Flat key indices of the next tile this lane (K: key row `lane`) and this
+    // wave (V: key chunks wave*VCW ..) load. A chunk is ppc whole pages of pt
+    // tokens, so flat key g is token g % pt of context page g / pt.
+    int kg = lane;
+    int vg[VCW];
+#pragma unroll
+    for (int i = 0; i < VCW; ++i) vg[i] = 8 * (wave * VCW + i);
+    const FastDiv pdiv = make_fastdiv((uint32_t)pt);
+
+    // K instructions of this wave: vectors wave*KPW .. (wave+1)*KPW-1 below KV;
+    // fp8 key scales (64 x 4 B) go with the last wave
+    const int kmine = max(0, min(KPW, KV - wave * KPW));
+    const bool scale_wave = FP8 && wave == NW - 1;
+    // vector memory instructions one full step issues in this wave (the same
+    // in every wave, plus the scale load of the last wave, when KV % NW == 0)
+    const int ndma = kmine + (scale_wave ? 1 : 0) + VCW * VDH;
+    constexpr int kDmaUniform = KV % NW == 0 ? KPW + VCW * VDH : -1;
+    auto wait_older_dma = [&]() {
+        if constexpr (kDmaUniform < 0) {
+            wait_vmem_upto(ndma);
+        } else if constexpr (FP8) {
+            if (scale_wave) wait_vmem_n<kDmaUniform + 1>();
+            else wait_vmem_n<kDmaUniform>();
+        } else {
+            wait_vmem_n<kDmaUniform>();
+        }
+    };
 
     __syncthreads();                               // ptab visible
 
     const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<float*>(FP8 ? a.kscale : nullptr), (short)0, FP8 ? a.sbytes : 0, 0x00020000);
-    auto dma_k = [&](uint16_t* kl) {
-        uint32_t off = kOOB, soff = kOOB;
-        if (kcur.g < nkeys) {
-            const int phys = ptab[kcur.p * ppc + kcur.pg];
-            const int64_t ph = (int64_t)phys * a.heads + head;
-            off = FP8 ? (uint32_t)(ph * head_blk + (int64_t)kcur.tok * 16)
-                      : (uint32_t)((ph * head_blk + (int64_t)kcur.tok * 8) * 2);
-            soff = (uint32_t)((ph * pt + kcur.tok) * 4);
-        }
-        if constexpr (!FP8) {
-#pragma unroll
-            for (int i = 0; i < KDMA; ++i) {
-                const int dc = wave * KDMA + i;
-                dma16(krs, kl + dc * BN * 8, off == kOOB ? kOOB : off + (uint32_t)(dc * pt * 16));
-            }
-        } else {
-            // K8 tile [16-channel vector][key][16 B], then the 64 key scales
-            uint8_t* kb8 = reinterpret_cast<uint8_t*>(kl);
-#pragma unroll
-            for (int i = 0; i < D / 64; ++i) {
-                const int v16 = wave * (D / 64) + i;
-                dma16(krs, kb8 + v16 * BN * 16, off == kOOB ? kOOB : off + (uint32_t)(v16 * pt * 16));
-            }
-            if (wave == 0) dma4(srs, kb8 + D * BN, soff);
-        }
-        kcur.step(BN, pt, ppc);
+    // Offsets of the next tile's DMA are computed one tile ahead (page-table
+    // lookup in LDS plus the page arithmetic), right after the previous DMA is
+    // issued, so that their latency overlaps the step's MFMA work and the DMA
+    // issue after the barrier is a handful of scalar and buffer instructions.
+    uint32_t koff = kOOB, soff = kOOB;             // this lane's key row of the next K tile
+    uint32_t voff[VCW];                            // this wave's key chunks of the next V tile
+    auto k_addr = [&]() {
+        const uint32_t gi = (uint32_t)min(kg, nkeys - 1);       // clamped: the lookup stays in the table
+        const uint32_t pidx = fast_div(gi, pdiv);
+        const uint32_t tok = gi - pidx * (uint32_t)pt;
+        const int64_t ph = (int64_t)ptab[pidx] * a.heads + head;
+        const uint32_t off = FP8 ? (uint32_t)(ph * head_blk + (int64_t)tok * 16)
+                                 : (uint32_t)((ph * head_blk + (int64_t)tok * 8) * 2);
+        koff = kg < nkeys ? off : kOOB;
+        soff = kg < nkeys ? (uint32_t)((ph * pt + tok) * 4) : kOOB;
     };
-    auto dma_v_chunk = [&](uint16_t* vl, KeyCursor& vc, int kc) {
-        const bool ok = vc.g < nkeys;
-        const int phys = ok ? ptab[vc.p * ppc + vc.pg] : 0;
-        const uint32_t base =
-            (uint32_t)((((int64_t)phys * a.heads + head) * head_blk + (int64_t)vc.tok * D) * 2);
+    auto v_addr = [&](int i) {
+        const uint32_t gi = (uint32_t)min(vg[i], nkeys - 1);
+        const uint32_t pidx = fast_div(gi, pdiv);
+        const uint32_t tok = gi - pidx * (uint32_t)pt;
+        const uint32_t off =
+            (uint32_t)((((int64_t)ptab[pidx] * a.heads + head) * head_blk + (int64_t)tok * D) * 2);
+        voff[i] = vg[i] < nkeys ? off : kOOB;
+    };
+    k_addr();
 #pragma unroll
-        for (int h = 0; h < VDH; ++h)
-            dma16(vrs, vl + (kc * D + 64 * h) * 8, ok ? base + (uint32_t)((64 * h + lane) * 16) : kOOB);
-        vc.step(BN, pt, ppc);
+    for (int i = 0; i < VCW; ++i) v_addr(i);
+
+    auto dma_k = [&](uint16_t* kl) {
+        // one instruction per 16-byte vector: bf16 K [vector][key][8 ch],
+        // fp8 K8 [vector][key][16 ch] followed by the 64 key scales
+        uint8_t* kb8 = reinterpret_cast<uint8_t*>(kl);
+#pragma unroll
+        for (int i = 0; i < KPW; ++i) {
+            const int vec = wave * KPW + i;
+            if (KV % NW == 0 || i < kmine)
+                dma16(krs, kb8 + vec * BN * 16, koff == kOOB ? kOOB : koff + (uint32_t)(vec * pt * 16));
+        }
+        if (scale_wave) dma4(srs, kb8 + D * BN, soff);
+        kg += BN;
+        k_addr();
     };
     auto dma_v = [&](uint16_t* vl) {
-        dma_v_chunk(vl, vcur0, 2 * wave);
-        dma_v_chunk(vl, vcur1, 2 * wave + 1);
+#pragma unroll
+        for (int i = 0; i < VCW; ++i) {
+            const int kc = wave * VCW + i;
+#pragma unroll
+            for (int h = 0; h < VDH; ++h)
+                dma16(vrs, vl + (kc * D + 64 * h) * 8,
+                      voff[i] == kOOB ? kOOB : voff[i] + (uint32_t)((64 * h + lane) * 16));
+            vg[i] += BN;
+            v_addr(i);
+        }
     };
 
     f32x16 oacc[DB];
@@ -416,21 +529,25 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
                 oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, P[G], oacc[db], 0, 0, 0);
             }
     };
-    // One pipeline step for tile t: K(t+2) and V(t+1) are fetched (into the
-    // buffers freed last step) while S(t+1) is computed next to the softmax
-    // of tile t, then PV(t) runs next to the max of tile t+1. S(t+1) is
-    // computed even past the last tile (from stale LDS, never used) so that
-    // its MFMAs share a basic block with the softmax.
+    // One pipeline step for tile t: K(t+NSTG) and V(t+NSTG-1) are fetched
+    // into the buffers that K(t) and V(t-1) left free last step, while S(t+1)
+    // is computed next to the softmax of tile t, then PV(t) runs next to the
+    // max of tile t+1. Tile j lives in K and V buffer j % NSTG. At the end the
+    // wave waits only for the DMA issued one step earlier (K(t+2) and V(t+1),
+    // needed next step) and leaves this step's in flight. S(t+1) is computed
+    // even past the last tile (from stale LDS, never used) so that its MFMAs
+    // share a basic block with the softmax.
     using NoMask = std::integral_constant<bool, false>;
     using Mask = std::integral_constant<bool, true>;
-    using Main = std::integral_constant<bool, true>;   // tiles t+1, t+2 exist, neither is the last
-    using Tail = std::integral_constant<bool, false>;  // one of the last three steps
+    using Main = std::integral_constant<bool, true>;   // every fetch is issued; tile t+1 is not the last
+    using Tail = std::integral_constant<bool, false>;  // one of the last steps
     auto step = [&](int t, const uint16_t* k_next, uint16_t* k_fill, const uint16_t* v_cur,
-                    uint16_t* v_fill, f32x16 (&Scur)[2], f32x16 (&Snext)[2], auto mainc) {
+                    uint16_t* v_fill, f32x16 (&Scur)[2], f32x16 (&Snext)[2],
+                    auto mainc) __attribute__((always_inline)) {
         constexpr bool kMain = decltype(mainc)::value;
-        __syncthreads();
-        if (kMain || t + 2 < ntiles) dma_k(k_fill);
-        if (kMain || t + 1 < ntiles) dma_v(v_fill);
+        tile_barrier();
+        if (kMain || t + NSTG < ntiles) dma_k(k_fill);
+        if (kMain || t + NSTG - 1 < ntiles) dma_v(v_fill);
         bf16x8 P[4];
         compute_s(k_next, Snext);
         exp_pack(Scur, P);
@@ -438,33 +555,58 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
         if constexpr (kMain) {
             update_max(Snext, t + 1, NoMask{}, k_next);
             sched_pipeline<D, FP8>();
+            wait_older_dma();
         } else {
             sched_pipeline<D, FP8>();
             if (t + 1 < ntiles) update_max(Snext, t + 1, Mask{}, k_next);
+            wait_vmem();
         }
-        wait_vmem();
     };
 
-    f32x16 SA[2], SB[2];
-    dma_k(k0lds);
-    dma_v(v0lds);
-    if (ntiles > 1) dma_k(k1lds);
+    // prologue: K(0..NSTG-1) and V(0..NSTG-2) in flight, then S(0)
+    static_for<0, NSTG>([&](auto j) __attribute__((always_inline)) {
+        if (j < ntiles) dma_k(kbuf<j>());
+        if (j + 1 < NSTG && j < ntiles) dma_v(vbuf<j>());
+    });
     wait_vmem();
     __syncthreads();
-    compute_s(k0lds, SA);
-    update_max(SA, 0, Mask{}, k0lds);
+    f32x16 SA[2], SB[2];
+    compute_s(kbuf<0>(), SA);
+    update_max(SA, 0, Mask{}, kbuf<0>());
     int t = 0;
-    // steady state: the next tile is never the last one, buffers are fixed
-    // per parity (tile t in K/V buffer t % 2)
-    for (; t + 3 < ntiles; t += 2) {
-        step(t, k1lds, k0lds, v0lds, v1lds, SA, SB, Main{});
-        step(t + 1, k0lds, k1lds, v1lds, v0lds, SB, SA, Main{});
+    // steady state, NSTG steps per iteration with fixed buffers: step t + j
+    // reads K buffer (j+1) % NSTG and V buffer j, fills K buffer j and V
+    // buffer (j-1) % NSTG; the score accumulators alternate SA/SB
+    if constexpr (NSTG % 2 == 0) {
+        for (; t + 2 * NSTG - 1 < ntiles; t += NSTG)
+            static_for<0, NSTG>([&](auto j) __attribute__((always_inline)) {
+                constexpr int J = decltype(j)::value;
+                if constexpr (J % 2 == 0)
+                    step(t + J, kbuf<(J + 1) % NSTG>(), kbuf<J>(), vbuf<J>(), vbuf<(J + NSTG - 1) % NSTG>(),
+                         SA, SB, Main{});
+                else
+                    step(t + J, kbuf<(J + 1) % NSTG>(), kbuf<J>(), vbuf<J>(), vbuf<(J + NSTG - 1) % NSTG>(),
+                         SB, SA, Main{});
+            });
+    } else {
+        // odd stage count: unroll 2*NSTG steps so the accumulators return to SA
+        for (; t + 3 * NSTG - 1 < ntiles; t += 2 * NSTG)
+            static_for<0, 2 * NSTG>([&](auto j) __attribute__((always_inline)) {
+                constexpr int J = decltype(j)::value;
+                constexpr int B = J % NSTG;
+                if constexpr (J % 2 == 0)
+                    step(t + J, kbuf<(B + 1) % NSTG>(), kbuf<B>(), vbuf<B>(), vbuf<(B + NSTG - 1) % NSTG>(),
+                         SA, SB, Main{});
+                else
+                    step(t + J, kbuf<(B + 1) % NSTG>(), kbuf<B>(), vbuf<B>(), vbuf<(B + NSTG - 1) % NSTG>(),
+                         SB, SA, Main{});
+            });
     }
-    // last one to three tiles
+    // remaining steps, buffers chosen at run time
     for (; t < ntiles; ++t) {
-        const bool odd = t & 1;
-        step(t, odd ? k0lds : k1lds, odd ? k1lds : k0lds, odd ? v1lds : v0lds, odd ? v0lds : v1lds,
-             SA, SB, Tail{});
+        const int b = t % NSTG;
+        step(t, kbuf_rt((b + 1) % NSTG), kbuf_rt(b), vbuf_rt(b), vbuf_rt((b + NSTG - 1) % NSTG), SA, SB,
+             Tail{});
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) SA[kb] = SB[kb];
     }
@@ -505,7 +647,7 @@ hipError_t launch_attention(const AttnArgs& a0, bool fp8, hipStream_t st) {
     a.qtiles = (a.N + BM - 1) / BM;
     const int64_t blocks = a.nwork;
     if (blocks <= 0 || blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
-    const dim3 grid((unsigned)blocks), block(256);
+    const dim3 grid((unsigned)blocks), block(NTH);
     if (a.D == 128) {
         if (fp8) hipLaunchKernelGGL((attn_kernel<128, true>), grid, block, 0, st, a);
         else hipLaunchKernelGGL((attn_kernel<128, false>), grid, block, 0, st, a);

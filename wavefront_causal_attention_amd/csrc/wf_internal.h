@@ -9,7 +9,10 @@ namespace wf {
 constexpr int kMaxSlots = 64;      // context positions per round (bit per position)
 constexpr int kMaxTablePages = 1024;  // T * pages_per_chunk, staged in LDS by attention
 constexpr int kFp8Block = 64;      // tokens per fp8 scale block (restarts at each chunk)
-constexpr int kAttnBM = 128;       // query rows per attention workgroup
+#ifndef WF_ATTN_BM
+#define WF_ATTN_BM 256
+#endif
+constexpr int kAttnBM = WF_ATTN_BM;  // query rows per attention workgroup (32 per wave)
 constexpr int kXcds = 8;           // MI355X: workgroup b runs on XCD b % 8
 
 // Work-list entry of one attention workgroup: (slot, head, query tile), or -1.
