@@ -13,7 +13,10 @@
 //   S^T[key][query] = K Q^T      (v_mfma_f32_32x32x16_bf16, K from LDS, Q in VGPRs)
 //   O^T[d][query]  += V^T P^T    (V^T from LDS, P^T from the S^T accumulators)
 // so a lane owns one query row throughout: the softmax max and sum are in-lane
-// except one exchange between the two 32-lane halves (v_permlane32_swap).
+// except one exchange between the two 32-lane halves (v_permlane32_swap). The
+// K row that feeds accumulator row r is key r with bits 2 and 3 swapped, which
+// leaves each lane the scores of exactly the keys its half supplies to the PV
+// MFMA's B operand, so P^T is packed in place with no cross-lane moves.
 //
 // Tiles arrive by LDS DMA (buffer_load ... lds): each instruction moves 1 KB
 // of contiguous page memory, keys past the legal prefix read out of range and
@@ -242,6 +245,10 @@ __global__ __launch_bounds__(NTH, NW == 4 ? 2 : 1) void attn_kernel(AttnArgs a) 
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
     const int qrow = qt * BM + wave * 32 + l32;
+    // K row read for accumulator row l32: bits 2 and 3 swapped. Element j of a
+    // lane's S^T accumulator block kb then holds key 32*kb + key_in_block(j) +
+    // 8*hf, with key_in_block(j) = 16*(j/8) + j%8.
+    const int krow = (l32 & 0x13) | ((l32 & 4) << 1) | ((l32 & 8) >> 1);
     const __amdgpu_buffer_rsrc_t krs =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(a.kpage), (short)0, a.kbytes, 0x00020000);
     const __amdgpu_buffer_rsrc_t vrs =
@@ -384,7 +391,7 @@ __global__ __launch_bounds__(NTH, NW == 4 ? 2 : 1) void attn_kernel(AttnArgs a) 
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb) {
                     const bf16x8 ka = as_bf16x8(
-                        *reinterpret_cast<const uint4*>(kl + ((2 * ks + hf) * BN + 32 * kb + l32) * 8));
+                        *reinterpret_cast<const uint4*>(kl + ((2 * ks + hf) * BN + 32 * kb + krow) * 8));
                     S[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ks], S[kb], 0, 0, 0);
                 }
         } else {
@@ -393,8 +400,8 @@ __global__ __launch_bounds__(NTH, NW == 4 ? 2 : 1) void attn_kernel(AttnArgs a) 
             for (int ks = 0; ks < D / 64; ++ks)
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb) {
-                    const uint4 u0 = *reinterpret_cast<const uint4*>(kb8 + ((4 * ks + 2 * hf) * BN + 32 * kb + l32) * 16);
-                    const uint4 u1 = *reinterpret_cast<const uint4*>(kb8 + ((4 * ks + 2 * hf + 1) * BN + 32 * kb + l32) * 16);
+                    const uint4 u0 = *reinterpret_cast<const uint4*>(kb8 + ((4 * ks + 2 * hf) * BN + 32 * kb + krow) * 16);
+                    const uint4 u1 = *reinterpret_cast<const uint4*>(kb8 + ((4 * ks + 2 * hf + 1) * BN + 32 * kb + krow) * 16);
                     S[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(as_i32x8(u0, u1), qf8[ks], S[kb],
                                                                             0, 0, 0, 0, 0, 0);
                 }
@@ -440,17 +447,18 @@ __global__ __launch_bounds__(NTH, NW == 4 ? 2 : 1) void attn_kernel(AttnArgs a) 
             b1 = chunk_bias(bchunk + 1);
         }
         const float* ksc = reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(kl) + D * BN);
-        const int lim = bend - kbase - 4 * hf;         // lane-relative first key of the next chunk
+        const int lim = bend - kbase - 8 * hf;         // lane-relative first key of the next chunk
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int g4 = 0; g4 < 4; ++g4) {
-                const float4 sk = *reinterpret_cast<const float4*>(ksc + 32 * kb + 8 * g4 + 4 * hf);
+                // elements 4*g4 .. 4*g4+3 hold four consecutive keys
+                const int key0 = 32 * kb + 16 * (g4 >> 1) + 4 * (g4 & 1);
+                const float4 sk = *reinterpret_cast<const float4*>(ksc + key0 + 8 * hf);
                 const float skv[4] = {sk.x, sk.y, sk.z, sk.w};
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const int key = 32 * kb + 8 * g4 + e;
-                    const float b = key < lim ? b0 : b1;
+                    const float b = key0 + e < lim ? b0 : b1;
                     S[kb][4 * g4 + e] = fmaf(S[kb][4 * g4 + e], skv[e], b);
                 }
             }
@@ -463,13 +471,13 @@ __global__ __launch_bounds__(NTH, NW == 4 ? 2 : 1) void attn_kernel(AttnArgs a) 
     auto update_max = [&](f32x16 (&S)[2], int tile, auto maskc, const uint16_t* kl) {
         if constexpr (FP8) dequant_scores(kl, S, tile);
         if constexpr (decltype(maskc)::value) {
-            const int lim = nkeys - tile * BN - 4 * hf;     // keys >= lim (lane-relative) are masked
+            const int lim = nkeys - tile * BN - 8 * hf;     // keys >= lim (lane-relative) are masked
             if (lim < BN) {
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                     for (int j = 0; j < 16; ++j) {
-                        const int key = 32 * kb + 8 * (j >> 2) + (j & 3);
+                        const int key = 32 * kb + 16 * (j >> 3) + (j & 7);
                         S[kb][j] = key < lim ? S[kb][j] : -INFINITY;
                     }
             }
@@ -495,9 +503,9 @@ __global__ __launch_bounds__(NTH, NW == 4 ? 2 : 1) void attn_kernel(AttnArgs a) 
     };
     // P = exp2(S*c - m*c) rounded to bf16; the row sum adds the same rounded
     // values (v_dot2 with (1, 1)) so the weights applied to V are normalised
-    // exactly. The S^T accumulator gives lane half h keys {4h..4h+3, 8+4h..}
-    // of each 16-key group; two v_permlane32_swap per group put them in
-    // natural order (half 0 keys 0-7, half 1 keys 8-15), matching V^T in LDS.
+    // exactly. With the permuted K rows, elements 8g..8g+7 of accumulator
+    // block kb are keys 16*(2*kb+g) + 8*hf + 0..7: the B operand of PV group
+    // G = 2*kb+g as it stands, matching V^T in LDS (key chunk 2*G + hf).
     auto exp_pack = [&](f32x16 (&S)[2], bf16x8 (&P)[4]) {
         const float mb = m_run * cl;
         uint32_t w[2][8];
@@ -514,9 +522,7 @@ __global__ __launch_bounds__(NTH, NW == 4 ? 2 : 1) void attn_kernel(AttnArgs a) 
 #pragma unroll
         for (int G = 0; G < 4; ++G) {
             const uint32_t* src = w[G >> 1] + 4 * (G & 1);
-            const auto x = __builtin_amdgcn_permlane32_swap(src[0], src[2], false, false);
-            const auto y = __builtin_amdgcn_permlane32_swap(src[1], src[3], false, false);
-            P[G] = as_bf16x8(make_uint4(x[0], y[0], x[1], y[1]));
+            P[G] = as_bf16x8(make_uint4(src[0], src[1], src[2], src[3]));
         }
     };
     auto compute_pv = [&](const uint16_t* vl, const bf16x8 (&P)[4]) {
