@@ -18,6 +18,14 @@ namespace {
 constexpr int kTokTile = 64;                 // tokens per publish block
 constexpr int kMaxFramesPerTile = kTokTile + 2;
 
+// Time-axis (cos, sin) table of the frames one 64-token block touches, in
+// dynamic LDS sized per launch: frames_per_tile(HW) rows of 32 pairs.
+extern __shared__ float2 g_ttab_dyn[];
+__host__ __device__ inline int frames_per_tile(int hw) {
+    const int f = (kTokTile + hw - 1) / hw + 1;
+    return f < kMaxFramesPerTile ? f : kMaxFramesPerTile;
+}
+
 __device__ __forceinline__ float bf_to_f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
@@ -42,6 +50,15 @@ __device__ __forceinline__ void load8(const void* base, int64_t elem, float* x) 
             x[2 * i] = __uint_as_float(w[i] << 16);
             x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
         }
+    }
+}
+
+__device__ __forceinline__ void unpack8(uint4 u, float* x) {
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        x[2 * i] = __uint_as_float(w[i] << 16);
+        x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
     }
 }
 
@@ -73,7 +90,7 @@ __device__ __forceinline__ void rope8(float* x, int c0, const float2* ttab_f, co
 template <int D, bool IN_FP32>
 __global__ __launch_bounds__(256) void publish_bf16_kernel(PublishArgs a) {
     constexpr int CPR = D / 8;                       // 8-channel vectors per token row
-    __shared__ float2 ttab[kMaxFramesPerTile][32];   // time-axis (cos, sin), this tile's frames
+    float2 (*ttab)[32] = reinterpret_cast<float2 (*)[32]>(g_ttab_dyn);   // time-axis (cos, sin), this tile's frames
     __shared__ __align__(16) uint4 kst[CPR * kTokTile];       // K vectors, [ch][tok ^ (ch & 7)]
     __shared__ __align__(16) uint16_t vst[kTokTile * D];      // V rows, [tok][d]
 
@@ -89,42 +106,79 @@ __global__ __launch_bounds__(256) void publish_bf16_kernel(PublishArgs a) {
     const int nf = n_hi / HW - f_lo + 1;
     const int hp = a.dt >> 1;
 
-    // time-axis angles in fp64: positions grow with the stream
-    for (int i = tid; i < nf * hp; i += 256) {
-        const int fi = i / hp, m = i - fi * hp;
-        const double phi = (double)(a.t0[sr] + f_lo + fi) * a.omega_t[m];
-        double sn, cs;
-        sincos(phi, &sn, &cs);
-        ttab[fi][m] = make_float2((float)cs, (float)sn);
-    }
-    __syncthreads();
-
     const int64_t row0 = (int64_t)sr * a.N;
     const int64_t col = (int64_t)head * D;
-    for (int c = tid; c < kTokTile * CPR; c += 256) {
-        const int tk = c / CPR, ch = c - tk * CPR;
+    auto rotate_and_stage = [&](int tk, int ch, float (&x)[8], float (&y)[8], float (&z)[8]) {
+        // x = K, y = Q, z = V of token n0 + tk, channels ch*8 .. ch*8+7
         const int n = n0 + tk;
-        if (n >= a.N) continue;
         const int f = n / HW;
-        const int y = (n / a.frame_w) % a.frame_h;
+        const int yy = (n / a.frame_w) % a.frame_h;
         const int xw = n % a.frame_w;
         const float2* tf = ttab[f - f_lo];
-        const float2* hrow = a.htab + y * (a.dh >> 1);
+        const float2* hrow = a.htab + yy * (a.dh >> 1);
         const float2* wrow = a.wtab + xw * (a.dw >> 1);
-        const int64_t e = (row0 + n) * a.row_stride + col + ch * 8;
-        float x[8];
-        load8<IN_FP32>(a.k, e, x);
         rope8(x, ch * 8, tf, hrow, wrow, a.dt, a.dh);
         kst[ch * kTokTile + (tk ^ (ch & 7))] = pack8(x);
         if (a.q) {
-            load8<IN_FP32>(a.q, e, x);
-            rope8(x, ch * 8, tf, hrow, wrow, a.dt, a.dh);
-            uint16_t* qp = static_cast<uint16_t*>(a.q_out) +
-                           (((int64_t)s * a.heads + head) * a.N + n) * D + ch * 8;
-            *reinterpret_cast<uint4*>(qp) = pack8(x);
+            rope8(y, ch * 8, tf, hrow, wrow, a.dt, a.dh);
+            uint16_t* qp = static_cast<uint16_t*>(a.q_out) + (((int64_t)s * a.heads + head) * a.N + n) * D + ch * 8;
+            *reinterpret_cast<uint4*>(qp) = pack8(y);
         }
-        load8<IN_FP32>(a.v, e, x);
-        *reinterpret_cast<uint4*>(&vst[tk * D + ch * 8]) = pack8(x);
+        *reinterpret_cast<uint4*>(&vst[tk * D + ch * 8]) = pack8(z);
+    };
+
+    if constexpr (!IN_FP32) {
+        // Every load of this thread's rows is issued before the time-axis
+        // table is built, so the HBM latency overlaps the fp64 sincos work.
+        constexpr int IT = kTokTile * CPR / 256;
+        uint4 kr[IT], qr[IT], vr[IT];
+#pragma unroll
+        for (int i = 0; i < IT; ++i) {
+            const int c = tid + 256 * i, tk = c / CPR, ch = c - tk * CPR;
+            const int n = min(n0 + tk, a.N - 1);          // rows past the chunk are read but not used
+            const int64_t e = (row0 + n) * a.row_stride + col + ch * 8;
+            kr[i] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.k) + e);
+            vr[i] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.v) + e);
+            qr[i] = a.q ? *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.q) + e) : make_uint4(0, 0, 0, 0);
+        }
+        // time-axis angles in fp64: positions grow with the stream
+        for (int i = tid; i < nf * hp; i += 256) {
+            const int fi = i / hp, m = i - fi * hp;
+            const double phi = (double)(a.t0[sr] + f_lo + fi) * a.omega_t[m];
+            double sn, cs;
+            sincos(phi, &sn, &cs);
+            ttab[fi][m] = make_float2((float)cs, (float)sn);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < IT; ++i) {
+            const int c = tid + 256 * i, tk = c / CPR, ch = c - tk * CPR;
+            if (n0 + tk >= a.N) continue;
+            float x[8], y[8], z[8];
+            unpack8(kr[i], x);
+            unpack8(qr[i], y);
+            unpack8(vr[i], z);
+            rotate_and_stage(tk, ch, x, y, z);
+        }
+    } else {
+        for (int i = tid; i < nf * hp; i += 256) {
+            const int fi = i / hp, m = i - fi * hp;
+            const double phi = (double)(a.t0[sr] + f_lo + fi) * a.omega_t[m];
+            double sn, cs;
+            sincos(phi, &sn, &cs);
+            ttab[fi][m] = make_float2((float)cs, (float)sn);
+        }
+        __syncthreads();
+        for (int c = tid; c < kTokTile * CPR; c += 256) {
+            const int tk = c / CPR, ch = c - tk * CPR;
+            if (n0 + tk >= a.N) continue;
+            const int64_t e = (row0 + n0 + tk) * a.row_stride + col + ch * 8;
+            float x[8], y[8], z[8];
+            load8<true>(a.k, e, x);
+            if (a.q) load8<true>(a.q, e, y);
+            load8<true>(a.v, e, z);
+            rotate_and_stage(tk, ch, x, y, z);
+        }
     }
     __syncthreads();
 
@@ -203,7 +257,7 @@ template <int D, bool IN_FP32>
 __global__ __launch_bounds__(256) void kmean_partial_kernel(PublishArgs a) {
     constexpr int CPR = D / 8;
     constexpr int ROWS = 256 / CPR;                  // token lanes per channel vector
-    __shared__ float2 ttab[kMaxFramesPerTile][32];
+    float2 (*ttab)[32] = reinterpret_cast<float2 (*)[32]>(g_ttab_dyn);
     __shared__ float part[ROWS][D];
     const int tid = threadIdx.x;
     const int sr = blockIdx.z, s = a.slot_first + sr, head = blockIdx.y, n0 = blockIdx.x * kTokTile;
@@ -254,7 +308,7 @@ __global__ __launch_bounds__(256) void publish_fp8_kernel(PublishArgs a) {
     constexpr int CPR = D / 8;                       // 8-channel vectors per token row
     constexpr int ITEMS = kTokTile * CPR / 256;
     constexpr int C16 = D / 16;                      // 16-byte code vectors per token row
-    __shared__ float2 ttab[kMaxFramesPerTile][32];
+    float2 (*ttab)[32] = reinterpret_cast<float2 (*)[32]>(g_ttab_dyn);
     __shared__ float mu[D];
     __shared__ float red[2][4];
     __shared__ __align__(16) uint8_t kcodes[kTokTile * D];   // [tok][16-byte vector ^ (tok % C16)]
@@ -392,13 +446,14 @@ hipError_t launch_page_table(int32_t* table, int T, int A, int ppc, int64_t ring
 template <int D, bool IN_FP32>
 hipError_t launch_publish_t(const PublishArgs& a, bool fp8, hipStream_t st) {
     const dim3 grid((a.N + kTokTile - 1) / kTokTile, a.heads, a.nslots);
+    const size_t tbytes = (size_t)frames_per_tile(a.frame_h * a.frame_w) * 32 * sizeof(float2);
     if (!fp8) {
-        hipLaunchKernelGGL((publish_bf16_kernel<D, IN_FP32>), grid, dim3(256), 0, st, a);
+        hipLaunchKernelGGL((publish_bf16_kernel<D, IN_FP32>), grid, dim3(256), tbytes, st, a);
         return hipGetLastError();
     }
-    hipLaunchKernelGGL((kmean_partial_kernel<D, IN_FP32>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((kmean_partial_kernel<D, IN_FP32>), grid, dim3(256), tbytes, st, a);
     hipLaunchKernelGGL((kmean_reduce_kernel<D>), dim3(a.heads, a.nslots), dim3(D), 0, st, a);
-    hipLaunchKernelGGL((publish_fp8_kernel<D, IN_FP32>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((publish_fp8_kernel<D, IN_FP32>), grid, dim3(256), tbytes, st, a);
     return hipGetLastError();
 }
 
