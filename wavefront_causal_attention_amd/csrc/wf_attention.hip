@@ -409,7 +409,7 @@ __global__ __launch_bounds__(NTH, NW == 4 ? 2 : 1) void attn_kernel(AttnArgs a) 
     };
     // fp8: per-lane bias q8 . mean(chunk) of the chunk a tile starts in (b0)
     // and of the next one (b1); recomputed only when tiles enter a new chunk.
-    int bchunk = -1, bend = 0;
+    int bchunk = 0, bend = N;
     float b0 = 0.f, b1 = 0.f;
     auto chunk_bias = [&](int pos) -> float {
         if (pos >= a.T - s) return 0.f;
@@ -432,20 +432,22 @@ __global__ __launch_bounds__(NTH, NW == 4 ? 2 : 1) void attn_kernel(AttnArgs a) 
         const auto sw = __builtin_amdgcn_permlane32_swap(ab, ab, false, false);
         return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
     };
+    // Chunk state (bend, b0, b1) for the tile dequantised next. Advanced at
+    // the end of a step, outside the MFMA/VALU interleaving, since it
+    // branches and loads the means only when tiles enter a new chunk.
+    auto chunk_advance = [&](int tile) {
+        if constexpr (FP8) {
+            const int kbase = tile * BN;
+            while (kbase >= bend) {
+                ++bchunk;
+                bend += N;
+                b0 = b1;
+                b1 = chunk_bias(bchunk + 1);
+            }
+        }
+    };
     auto dequant_scores = [&](const uint16_t* kl, f32x16 (&S)[2], int tile) {
         const int kbase = tile * BN;
-        if (bchunk < 0) {
-            bchunk = 0;
-            bend = N;
-            b0 = chunk_bias(0);
-            b1 = chunk_bias(1);
-        }
-        while (kbase >= bend) {
-            ++bchunk;
-            bend += N;
-            b0 = b1;
-            b1 = chunk_bias(bchunk + 1);
-        }
         const float* ksc = reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(kl) + D * BN);
         const int lim = bend - kbase - 8 * hf;         // lane-relative first key of the next chunk
 #pragma unroll
@@ -567,6 +569,7 @@ __global__ __launch_bounds__(NTH, NW == 4 ? 2 : 1) void attn_kernel(AttnArgs a) 
             if (t + 1 < ntiles) update_max(Snext, t + 1, Mask{}, k_next);
             wait_vmem();
         }
+        chunk_advance(t + 2);
     };
 
     // prologue: K(0..NSTG-1) and V(0..NSTG-2) in flight, then S(0)
@@ -577,8 +580,13 @@ __global__ __launch_bounds__(NTH, NW == 4 ? 2 : 1) void attn_kernel(AttnArgs a) 
     wait_vmem();
     __syncthreads();
     f32x16 SA[2], SB[2];
+    if constexpr (FP8) {
+        b0 = chunk_bias(0);
+        b1 = chunk_bias(1);
+    }
     compute_s(kbuf<0>(), SA);
     update_max(SA, 0, Mask{}, kbuf<0>());
+    chunk_advance(1);
     int t = 0;
     // steady state, NSTG steps per iteration with fixed buffers: step t + j
     // reads K buffer (j+1) % NSTG and V buffer j, fills K buffer j and V
