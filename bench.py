@@ -62,7 +62,7 @@ def parse():
     ap.add_argument("--workload", default="wan1.3b_s4")
     ap.add_argument("--out-dtype", default="bf16", choices=["bf16", "fp32"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=24, help="query rows per (slot, head) in the CPU sample")
+    ap.add_argument("--cpu-rows", type=int, default=1024, help="query rows per (slot, head) in the CPU sample")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="also run one device copy of this many MiB (counter calibration)")
     return ap.parse_args()
