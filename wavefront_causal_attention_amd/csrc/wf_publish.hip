@@ -62,6 +62,31 @@ __device__ __forceinline__ void unpack8(uint4 u, float* x) {
     }
 }
 
+// Eight input elements as loaded (bf16: one 16-byte vector; fp32: two),
+// unpacked to fp32 only when used, so loads can be issued early cheaply.
+template <bool IN_FP32>
+struct Raw8 {
+    uint4 u[IN_FP32 ? 2 : 1];
+    __device__ __forceinline__ void load(const void* base, int64_t elem) {
+        if constexpr (IN_FP32) {
+            const uint4* p = reinterpret_cast<const uint4*>(static_cast<const float*>(base) + elem);
+            u[0] = p[0];
+            u[1] = p[1];
+        } else {
+            u[0] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + elem);
+        }
+    }
+    __device__ __forceinline__ void unpack(float* x) const {
+        if constexpr (IN_FP32) {
+            const uint32_t w[8] = {u[0].x, u[0].y, u[0].z, u[0].w, u[1].x, u[1].y, u[1].z, u[1].w};
+#pragma unroll
+            for (int i = 0; i < 8; ++i) x[i] = __uint_as_float(w[i]);
+        } else {
+            unpack8(u[0], x);
+        }
+    }
+};
+
 __device__ __forceinline__ uint4 pack8(const float* x) {
     return make_uint4(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]),
                       pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7]));
@@ -265,16 +290,26 @@ __global__ __launch_bounds__(256) void kmean_partial_kernel(PublishArgs a) {
     const int HW = a.frame_h * a.frame_w;
     const int f_lo = n0 / HW;
     const int nf = (min(n0 + kTokTile, a.N) - 1) / HW - f_lo + 1;
+    const int ch = tid % CPR, row = tid / CPR;
+    constexpr int IT = kTokTile / ROWS;
+    // rows of this thread, loaded before the time table is built (rows past
+    // the chunk are clamped to its last row and not summed)
+    Raw8<IN_FP32> kin[IT];
+#pragma unroll
+    for (int i = 0; i < IT; ++i) {
+        const int n = min(n0 + row + ROWS * i, a.N - 1);
+        kin[i].load(a.k, ((int64_t)sr * a.N + n) * a.row_stride + (int64_t)head * D + ch * 8);
+    }
     fill_ttab(ttab, a, sr, f_lo, nf);
     __syncthreads();
-    const int ch = tid % CPR, row = tid / CPR;
     float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    for (int tk = row; tk < kTokTile; tk += ROWS) {
-        const int n = n0 + tk;
+#pragma unroll
+    for (int i = 0; i < IT; ++i) {
+        const int n = n0 + row + ROWS * i;
         if (n >= a.N) break;
         const int y = (n / a.frame_w) % a.frame_h, xw = n % a.frame_w;
         float x[8];
-        load8<IN_FP32>(a.k, ((int64_t)sr * a.N + n) * a.row_stride + (int64_t)head * D + ch * 8, x);
+        kin[i].unpack(x);
         rope8(x, ch * 8, ttab[n / HW - f_lo], a.htab + y * (a.dh >> 1), a.wtab + xw * (a.dw >> 1), a.dt, a.dh);
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[e] += x[e];
@@ -320,13 +355,25 @@ __global__ __launch_bounds__(256) void publish_fp8_kernel(PublishArgs a) {
     const int HW = a.frame_h * a.frame_w;
     const int f_lo = n0 / HW;
     const int nf = (min(n0 + kTokTile, a.N) - 1) / HW - f_lo + 1;
+    const int64_t row0 = (int64_t)sr * a.N;
+    const int64_t col = (int64_t)head * D;
+    // K and V rows of this thread are loaded before the tables are built
+    // (rows past the chunk are clamped to its last row and not used)
+    Raw8<IN_FP32> kin[ITEMS], qin[ITEMS], vin[ITEMS];
+#pragma unroll
+    for (int i = 0; i < ITEMS; ++i) {
+        const int c = tid + 256 * i;
+        const int tk = c / CPR, ch = c - tk * CPR;
+        const int64_t e0 = (row0 + min(n0 + tk, a.N - 1)) * a.row_stride + col + ch * 8;
+        kin[i].load(a.k, e0);
+        vin[i].load(a.v, e0);
+        if (a.q) qin[i].load(a.q, e0);
+    }
     fill_ttab(ttab, a, sr, f_lo, nf);
     const int g = a.table[p * a.ppc] / a.ppc;
     if (tid < D) mu[tid] = a.kmean[((int64_t)g * a.heads + head) * D + tid];
     __syncthreads();
 
-    const int64_t row0 = (int64_t)sr * a.N;
-    const int64_t col = (int64_t)head * D;
     float kx[ITEMS][8], qx[ITEMS][8];
     float kmax = 0.f, qmax = 0.f;
 #pragma unroll
@@ -337,12 +384,11 @@ __global__ __launch_bounds__(256) void publish_fp8_kernel(PublishArgs a) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) kx[i][e] = qx[i][e] = 0.f;
         if (n >= a.N) continue;
+        kin[i].unpack(kx[i]);
         const int y = (n / a.frame_w) % a.frame_h, xw = n % a.frame_w;
         const float2* tf = ttab[n / HW - f_lo];
         const float2* hrow = a.htab + y * (a.dh >> 1);
         const float2* wrow = a.wtab + xw * (a.dw >> 1);
-        const int64_t e0 = (row0 + n) * a.row_stride + col + ch * 8;
-        load8<IN_FP32>(a.k, e0, kx[i]);
         rope8(kx[i], ch * 8, tf, hrow, wrow, a.dt, a.dh);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -350,14 +396,14 @@ __global__ __launch_bounds__(256) void publish_fp8_kernel(PublishArgs a) {
             kmax = fmaxf(kmax, fabsf(kx[i][e]));
         }
         if (a.q) {
-            load8<IN_FP32>(a.q, e0, qx[i]);
+            qin[i].unpack(qx[i]);
             rope8(qx[i], ch * 8, tf, hrow, wrow, a.dt, a.dh);
 #pragma unroll
             for (int e = 0; e < 8; ++e) qmax = fmaxf(qmax, fabsf(qx[i][e]));
         }
-        float v[8];
-        load8<IN_FP32>(a.v, e0, v);
-        *reinterpret_cast<uint4*>(&vst[tk * D + ch * 8]) = pack8(v);
+        float vx[8];
+        vin[i].unpack(vx);
+        *reinterpret_cast<uint4*>(&vst[tk * D + ch * 8]) = pack8(vx);
     }
     kmax = wave_max(kmax);
     qmax = wave_max(qmax);
