@@ -45,7 +45,6 @@ extern "C" {
 #define WF_E_SHAPE         2   /* configuration or buffer size not supported */
 #define WF_E_NOT_READY     3   /* a required context position is not published */
 #define WF_E_HIP           4   /* a HIP runtime call failed (see wf_last_error) */
-#define WF_E_NO_DEVICE     5   /* launching call on a host-model handle is not allowed here */
 
 /* element types */
 #define WF_DTYPE_BF16      0

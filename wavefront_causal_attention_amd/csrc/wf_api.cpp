@@ -444,7 +444,6 @@ const char* wf_status_string(int status) {
         case WF_E_SHAPE: return "unsupported shape or undersized buffer";
         case WF_E_NOT_READY: return "context position not published";
         case WF_E_HIP: return "HIP runtime error";
-        case WF_E_NO_DEVICE: return "no device behind this handle";
         default: return "unknown status";
     }
 }
