@@ -38,8 +38,8 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings(lib):
-    for st in range(6):
-        assert _lib.status_string(st)
+    names = [_lib.status_string(st) for st in range(5)]
+    assert all(names) and len(set(names)) == 5
 
 
 @pytest.mark.parametrize("name", list(W.WORKLOADS))
@@ -77,6 +77,20 @@ def test_config_validation(lib, field, value, status):
     assert e.value.status == status
 
 
+def test_fp8_needs_chunks_of_a_full_tile(lib):
+    # fp8 attention keeps the chunk means of at most two chunks per 64-key tile
+    import dataclasses
+    w8 = W.WORKLOADS["ragged_fp8_64"]
+    c = cfg_of(dataclasses.replace(w8, chunk_frames=1, frame_h=4, frame_w=6, page_tokens=24))  # 24-token chunks
+    with pytest.raises(wf.WfError) as e:
+        wf.wf_pool_bytes(c)
+    assert e.value.status == wf.WF_E_SHAPE
+    c.qk_dtype = wf.WF_DTYPE_BF16
+    wf.wf_pool_bytes(c)                                                  # bf16 takes any chunk size
+    c = cfg_of(dataclasses.replace(w8, chunk_frames=1, frame_h=8, frame_w=8, page_tokens=64))
+    wf.wf_pool_bytes(c)                                                  # exactly one tile per chunk
+
+
 def test_bad_rope_split(lib):
     c = cfg_of(W.WORKLOADS["wan1.3b_s4"])
     c.rope_split[2] = 40
@@ -97,7 +111,7 @@ def test_undersized_buffers_rejected_before_any_device_access(lib):
     assert e.value.status == wf.WF_E_INVALID_ARG
 
 
-@pytest.mark.parametrize("name", ["wan1.3b_s4", "wan1.3b_s5_30", "wan14b_s4", "tiny"])
+@pytest.mark.parametrize("name", ["wan1.3b_s4", "wan1.3b_s5_30", "wan14b_s4", "tiny", "edge_s1_h0"])
 def test_schedule_and_page_table_closed_form(lib, name):
     w = W.WORKLOADS[name]
     h = wf.wf_pool_create_host_model(cfg_of(w))

@@ -46,8 +46,9 @@ def _code_distance(a, b):
     return np.where(za & zb, 0, np.where(same_sign, mag, (a & 0x7F) + (b & 0x7F)))
 
 
-def test_fp8_publish_codes_scales_and_means():
-    w = W.WORKLOADS["ragged_fp8"]
+@pytest.mark.parametrize("name", ["ragged_fp8", "ragged_fp8_64"])
+def test_fp8_publish_codes_scales_and_means(name):
+    w = W.WORKLOADS[name]
     say("case", w.name, "fp8 publish")
     r = RoundRunner(w)
     r.seed_clean()
@@ -103,8 +104,9 @@ def test_fp8_publish_codes_scales_and_means():
     assert diff <= 1e-3 * total
 
 
-def test_fp8_round_parity_full():
-    w = W.WORKLOADS["ragged_fp8"]
+@pytest.mark.parametrize("name", ["ragged_fp8", "ragged_fp8_64"])
+def test_fp8_round_parity_full(name):
+    w = W.WORKLOADS[name]
     say("case", w.name, "fp8 full round")
     r = RoundRunner(w)
     r.seed_clean()

@@ -46,7 +46,7 @@ def _bf16_ulps(a, b):
     return np.abs(ia - ib)
 
 
-@pytest.mark.parametrize("name", ["tiny", "ragged128", "ragged64"])
+@pytest.mark.parametrize("name", ["tiny", "ragged128", "ragged64", "edge_s1_h0"])
 def test_round_parity_full(name):
     w = W.WORKLOADS[name]
     say("case", name, "full round")
@@ -70,7 +70,7 @@ def test_round_parity_full(name):
     assert np.array_equal(gb, bf16_round(g))
 
 
-@pytest.mark.parametrize("name", ["tiny", "ragged128", "ragged64"])
+@pytest.mark.parametrize("name", ["tiny", "ragged128", "ragged64", "edge_s1_h0"])
 def test_page_table_and_publish_placement(name):
     w = W.WORKLOADS[name]
     say("case", name, "placement")
@@ -126,7 +126,7 @@ def test_page_table_and_publish_placement(name):
     assert diff <= 1e-3 * total
 
 
-@pytest.mark.parametrize("name", ["ragged128", "tiny"])
+@pytest.mark.parametrize("name", ["ragged128", "tiny", "edge_s1_h0"])
 def test_noisier_slots_poisoned_with_nan_do_not_change_cleaner_outputs(name):
     w = W.WORKLOADS[name]
     say("case", name, "nan poison")
@@ -205,8 +205,8 @@ def test_slot_subset_launch_matches_full_round():
 
 def _sample_rows(N, seed, extra=16):
     rng = np.random.default_rng(seed)
-    fixed = [0, 1, 63, 64, 127, 128, 129, N // 2, N - 73, N - 72, N - 71, N - 2, N - 1]
-    fixed += [(N // 128) * 128 - 1, (N // 128) * 128]
+    fixed = [0, 1, 63, 64, 127, 128, 129, 255, 256, 257, N // 2, N - 73, N - 72, N - 71, N - 2, N - 1]
+    fixed += [(N // 128) * 128 - 1, (N // 128) * 128, (N // 256) * 256 - 1, (N // 256) * 256]
     return np.array(sorted(set(int(x) for x in fixed + list(rng.integers(0, N, extra)) if 0 <= x < N)))
 
 
@@ -261,3 +261,22 @@ def test_thirty_layer_rounds_with_rotation():
         r.advance()
         say("round", i, "ok max_abs %.2e rel %.2e" % (mx, rel))
     say("30 rounds worst max_abs %.3e rel_l2 %.3e" % worst)
+
+
+@pytest.mark.parametrize("name", ["edge_s1_h0", "tiny"])
+def test_rotated_rounds_full_output(name):
+    """Every output row of several consecutive rounds, advancing in between,
+    so each page group visits every position of the ring."""
+    w = W.WORKLOADS[name]
+    say("case", name, "rotated rounds, full output")
+    r = RoundRunner(w)
+    r.seed_clean()
+    for i in range(2 * (w.H + w.S + 1) + 1):
+        r.publish_live(live=W.draw_slots(w, r.k, range(w.S + 1)))
+        out = r.attention("fp32")
+        ref = oracle_round(w, r.k, r.live, r.clean_for_round(), storage="bf16")
+        g = gpu_rows(out, w, np.arange(w.N))
+        mx, rel = err_stats(g, ref)
+        say(name, "round", r.k, "max_abs %.3e rel_l2 %.3e" % (mx, rel))
+        assert mx <= BF16_MAX_ABS and rel <= BF16_REL_L2, (i, mx, rel)
+        r.advance()

@@ -115,6 +115,17 @@ WORKLOADS = {
                          frame_h=6, frame_w=12, page_tokens=72, in_dtype="bf16", qk_dtype="bf16",
                          rope_split=_split(64), rope_theta=1e4, seed=12,
                          description="S=3, chunk 216 (3x6x12), page 72, 2x64, bf16"),
+    # Degenerate schedule: one denoising slot, two anchor chunks, no history;
+    # 24-token pages, so 64-key tiles straddle pages and chunks.
+    "edge_s1_h0": Workload("edge_s1_h0", S=1, A=2, H=0, heads=2, head_dim=64, chunk_frames=1,
+                           frame_h=8, frame_w=9, page_tokens=24, in_dtype="bf16", qk_dtype="bf16",
+                           rope_split=_split(64), rope_theta=1e4, seed=14,
+                           description="S=1, A=2, H=0, chunk 72 (1x8x9), page 24, 2x64, bf16"),
+    # fp8 QK at head_dim 64 from separate Q/K/V inputs.
+    "ragged_fp8_64": Workload("ragged_fp8_64", S=2, A=1, H=1, heads=2, head_dim=64, chunk_frames=2,
+                              frame_h=6, frame_w=10, page_tokens=40, in_dtype="bf16", qk_dtype="fp8",
+                              rope_split=_split(64), rope_theta=1e4, seed=15,
+                              description="fp8 QK, chunk 120 (2x6x10), page 40, 2x64, separate inputs"),
     "ragged_fp8": Workload("ragged_fp8", S=3, A=1, H=2, heads=3, head_dim=128, chunk_frames=2,
                            frame_h=12, frame_w=13, page_tokens=104, in_dtype="bf16",
                            qk_dtype="fp8", rope_split=(44, 42, 42), rope_theta=1e4, seed=13,
