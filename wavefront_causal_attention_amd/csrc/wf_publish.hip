@@ -28,6 +28,16 @@ __host__ __device__ inline int frames_per_tile(int hw) {
 
 __device__ __forceinline__ float bf_to_f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
+// Projection rows are read exactly once, so their loads take the
+// non-temporal path. Page and Q stores stay ordinary: non-temporal stores
+// measured 7% slower here (the attention that follows reads the pages).
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld_stream16(const void* p) {
+    const u32x4 v = __builtin_nontemporal_load(static_cast<const u32x4*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void st16(void* p, uint4 v) { *static_cast<uint4*>(p) = v; }
+
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     // v_cvt_pk_bf16_f32: round to nearest even, NaN stays NaN
     typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
@@ -73,7 +83,7 @@ struct Raw8 {
             u[0] = p[0];
             u[1] = p[1];
         } else {
-            u[0] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + elem);
+            u[0] = ld_stream16(static_cast<const uint16_t*>(base) + elem);
         }
     }
     __device__ __forceinline__ void unpack(float* x) const {
@@ -147,7 +157,7 @@ __global__ __launch_bounds__(256) void publish_bf16_kernel(PublishArgs a) {
         if (a.q) {
             rope8(y, ch * 8, tf, hrow, wrow, a.dt, a.dh);
             uint16_t* qp = static_cast<uint16_t*>(a.q_out) + (((int64_t)s * a.heads + head) * a.N + n) * D + ch * 8;
-            *reinterpret_cast<uint4*>(qp) = pack8(y);
+            st16(qp, pack8(y));
         }
         *reinterpret_cast<uint4*>(&vst[tk * D + ch * 8]) = pack8(z);
     };
@@ -162,9 +172,9 @@ __global__ __launch_bounds__(256) void publish_bf16_kernel(PublishArgs a) {
             const int c = tid + 256 * i, tk = c / CPR, ch = c - tk * CPR;
             const int n = min(n0 + tk, a.N - 1);          // rows past the chunk are read but not used
             const int64_t e = (row0 + n) * a.row_stride + col + ch * 8;
-            kr[i] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.k) + e);
-            vr[i] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.v) + e);
-            qr[i] = a.q ? *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.q) + e) : make_uint4(0, 0, 0, 0);
+            kr[i] = ld_stream16(static_cast<const uint16_t*>(a.k) + e);
+            vr[i] = ld_stream16(static_cast<const uint16_t*>(a.v) + e);
+            qr[i] = a.q ? ld_stream16(static_cast<const uint16_t*>(a.q) + e) : make_uint4(0, 0, 0, 0);
         }
         // time-axis angles in fp64: positions grow with the stream
         for (int i = tid; i < nf * hp; i += 256) {
@@ -215,8 +225,8 @@ __global__ __launch_bounds__(256) void publish_bf16_kernel(PublishArgs a) {
         const int pg = n / a.pt, tok = n - pg * a.pt;
         const int phys = a.table[p * a.ppc + pg];
         const int64_t base = ((int64_t)phys * a.heads + head) * a.pt * D;
-        *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.kpage) + k_elem(base, a.pt, tok, ch * 8)) =
-            kst[ch * kTokTile + (tk ^ (ch & 7))];
+        st16(static_cast<uint16_t*>(a.kpage) + k_elem(base, a.pt, tok, ch * 8),
+                    kst[ch * kTokTile + (tk ^ (ch & 7))]);
     }
     // V pages: one vector of 8 consecutive tokens of one channel per thread,
     // channels fastest. N and pages are multiples of 8, so a group never
@@ -232,7 +242,7 @@ __global__ __launch_bounds__(256) void publish_bf16_kernel(PublishArgs a) {
         const int pg = n / a.pt, tok = n - pg * a.pt;
         const int phys = a.table[p * a.ppc + pg];
         const int64_t base = ((int64_t)phys * a.heads + head) * a.pt * D;
-        *reinterpret_cast<uint4*>(a.vpage + v_elem(base, D, tok, d)) = make_uint4(w[0], w[1], w[2], w[3]);
+        st16(a.vpage + v_elem(base, D, tok, d), make_uint4(w[0], w[1], w[2], w[3]));
     }
 }
 
@@ -445,8 +455,8 @@ __global__ __launch_bounds__(256) void publish_fp8_kernel(PublishArgs a) {
         const int pg = n / a.pt, tok = n - pg * a.pt;
         const int phys = a.table[p * a.ppc + pg];
         const int64_t base = ((int64_t)phys * a.heads + head) * a.pt * D;
-        *reinterpret_cast<uint4*>(static_cast<uint8_t*>(a.kpage) + k8_byte(base, a.pt, tok, v16 * 16)) =
-            *reinterpret_cast<const uint4*>(&kcodes[(tk * C16 + (v16 ^ (tk % C16))) * 16]);
+        st16(static_cast<uint8_t*>(a.kpage) + k8_byte(base, a.pt, tok, v16 * 16),
+                    *reinterpret_cast<const uint4*>(&kcodes[(tk * C16 + (v16 ^ (tk % C16))) * 16]));
     }
     if (tid < kTokTile && n0 + tid < a.N) {
         const int n = n0 + tid;
@@ -466,7 +476,7 @@ __global__ __launch_bounds__(256) void publish_fp8_kernel(PublishArgs a) {
         const int pg = n / a.pt, tok = n - pg * a.pt;
         const int phys = a.table[p * a.ppc + pg];
         const int64_t base = ((int64_t)phys * a.heads + head) * a.pt * D;
-        *reinterpret_cast<uint4*>(a.vpage + v_elem(base, D, tok, d)) = make_uint4(w[0], w[1], w[2], w[3]);
+        st16(a.vpage + v_elem(base, D, tok, d), make_uint4(w[0], w[1], w[2], w[3]));
     }
 }
 
