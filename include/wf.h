@@ -64,7 +64,7 @@ typedef struct wf_config {
     int32_t page_tokens;     /* tokens per page; divides the chunk, multiple of 8   */
     int32_t in_dtype;        /* projected Q/K/V input: WF_DTYPE_BF16 | WF_DTYPE_FP32 */
     int32_t qk_dtype;        /* published Q/K: WF_DTYPE_BF16 | WF_DTYPE_FP8_E4M3
-                                (fp8 needs chunks of at least 64 tokens)           */
+                                (fp8: T * ceil(chunk tokens / 64) <= 4096)         */
     int32_t rope_split[3];   /* (d_t, d_h, d_w), even, summing to head_dim          */
     int32_t first_round;     /* round index k of the pool's first round, >= S+H+A   */
     double  rope_theta;      /* RoPE base, e.g. 10000                               */

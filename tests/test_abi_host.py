@@ -77,18 +77,23 @@ def test_config_validation(lib, field, value, status):
     assert e.value.status == status
 
 
-def test_fp8_needs_chunks_of_a_full_tile(lib):
-    # fp8 attention keeps the chunk means of at most two chunks per 64-key tile
+def test_fp8_tile_scale_table_limit(lib):
+    # fp8 attention tiles every chunk into its 64-token quantisation blocks and
+    # stages one key scale per tile of the context (at most 4096) in LDS
     import dataclasses
-    w8 = W.WORKLOADS["ragged_fp8_64"]
-    c = cfg_of(dataclasses.replace(w8, chunk_frames=1, frame_h=4, frame_w=6, page_tokens=24))  # 24-token chunks
+    w = W.WORKLOADS["wan1.3b_s4_fp8"]                       # T = 8
+    fits = dataclasses.replace(w, chunk_frames=21)          # 32760 tokens: 8 x 512 tiles
+    wf.wf_pool_bytes(cfg_of(fits))
+    big = dataclasses.replace(w, chunk_frames=22)           # 34320 tokens: 8 x 537 tiles
     with pytest.raises(wf.WfError) as e:
-        wf.wf_pool_bytes(c)
+        wf.wf_pool_bytes(cfg_of(big))
     assert e.value.status == wf.WF_E_SHAPE
-    c.qk_dtype = wf.WF_DTYPE_BF16
-    wf.wf_pool_bytes(c)                                                  # bf16 takes any chunk size
-    c = cfg_of(dataclasses.replace(w8, chunk_frames=1, frame_h=8, frame_w=8, page_tokens=64))
-    wf.wf_pool_bytes(c)                                                  # exactly one tile per chunk
+    c = cfg_of(big)
+    c.qk_dtype = wf.WF_DTYPE_BF16                            # bf16 has no such table
+    wf.wf_pool_bytes(c)
+    small = dataclasses.replace(W.WORKLOADS["ragged_fp8_64"], chunk_frames=1, frame_h=4, frame_w=6,
+                                page_tokens=24)             # a chunk shorter than one tile
+    wf.wf_pool_bytes(cfg_of(small))
 
 
 def test_bad_rope_split(lib):

@@ -46,7 +46,7 @@ def _code_distance(a, b):
     return np.where(za & zb, 0, np.where(same_sign, mag, (a & 0x7F) + (b & 0x7F)))
 
 
-@pytest.mark.parametrize("name", ["ragged_fp8", "ragged_fp8_64"])
+@pytest.mark.parametrize("name", ["ragged_fp8", "ragged_fp8_64", "tiny_fp8"])
 def test_fp8_publish_codes_scales_and_means(name):
     w = W.WORKLOADS[name]
     say("case", w.name, "fp8 publish")
@@ -104,7 +104,7 @@ def test_fp8_publish_codes_scales_and_means(name):
     assert diff <= 1e-3 * total
 
 
-@pytest.mark.parametrize("name", ["ragged_fp8", "ragged_fp8_64"])
+@pytest.mark.parametrize("name", ["ragged_fp8", "ragged_fp8_64", "tiny_fp8"])
 def test_fp8_round_parity_full(name):
     w = W.WORKLOADS[name]
     say("case", w.name, "fp8 full round")

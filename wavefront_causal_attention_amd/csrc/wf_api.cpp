@@ -76,8 +76,10 @@ int validate(const wf_config* c, Layout* L) {
     const int64_t N = (int64_t)c->chunk_frames * c->frame_h * c->frame_w;
     if (N > (1 << 20)) return WF_E_SHAPE;
     if (c->page_tokens < 8 || c->page_tokens % 8 != 0 || N % c->page_tokens != 0) return WF_E_SHAPE;
-    // fp8 attention tracks the chunk means of at most two chunks per 64-key tile
-    if (c->qk_dtype == WF_DTYPE_FP8_E4M3 && N < 64) return WF_E_SHAPE;
+    // fp8 attention tiles each chunk into its 64-token quantisation blocks and
+    // stages one key scale per tile of the context in LDS
+    if (c->qk_dtype == WF_DTYPE_FP8_E4M3 && (int64_t)T * ((N + 63) / 64) > wf::kMaxFp8Tiles)
+        return WF_E_SHAPE;
     const int ppc = (int)(N / c->page_tokens);
     if ((int64_t)T * ppc > wf::kMaxTablePages) return WF_E_SHAPE;
     if (c->in_dtype != WF_DTYPE_BF16 && c->in_dtype != WF_DTYPE_FP32) return WF_E_INVALID_ARG;

@@ -116,6 +116,7 @@ __shared__ __align__(16) uint16_t g_vt1[kTileElems];
 __shared__ __align__(16) uint16_t g_vt2[kTileElems];
 __shared__ __align__(16) uint16_t g_vt3[kTileElems];
 __shared__ int g_ptab[kMaxTablePages];
+__shared__ float g_stab[kMaxFp8Tiles];   // fp8: key scale of every tile of the prefix
 
 template <int I>
 __device__ __forceinline__ uint16_t* kbuf() {
@@ -214,7 +215,19 @@ __device__ __forceinline__ uint32_t fast_div(uint32_t n, FastDiv f) {
 // FP8: Q and K are e4m3 codes with per-64-token-block scales and the chunk's
 // K mean removed; QK^T runs on v_mfma_f32_32x32x64_f8f6f4 and each raw score
 // becomes s_k * (q8 . k8) + q8 . mean(chunk); the query scale is folded into
-// the softmax's exp2 constant. V and PV stay bf16.
+// the softmax's exp2 constant. V and PV stay bf16. Key tiles are the 64-token
+// quantisation blocks of each chunk, so a tile has one key scale and one
+// chunk mean: the affine dequantisation folds into the exp2 argument (one FMA
+// per score, as for bf16) and the row max is taken on the raw accumulator
+// (the scale is positive). The last block of a chunk is partial unless 64
+// divides the chunk; its missing keys are masked.
+
+// Scores of one key tile: the S^T accumulators and, for fp8, the tile's key
+// scale and this lane's chunk bias.
+struct TileS {
+    f32x16 s[2];
+    float sk, b;
+};
 template <int D, bool FP8>
 __global__ __launch_bounds__(NTH, NW == 4 ? 2 : 1) void attn_kernel(AttnArgs a) {
     constexpr int DC = D / 8;       // 16-byte channel vectors per key
@@ -238,7 +251,10 @@ __global__ __launch_bounds__(NTH, NW == 4 ? 2 : 1) void attn_kernel(AttnArgs a) 
     const int qt = work_qtile(unit);
     const int N = a.N, pt = a.pt, ppc = a.ppc;
     const int nkeys = (a.T - s) * N;               // legal prefix of slot s
-    const int ntiles = (nkeys + BN - 1) / BN;
+    // bf16: tiles cover the flat prefix; fp8: tpc tiles per chunk
+    const int tpc = FP8 ? (N + BN - 1) / BN : 1;
+    const int ntiles = FP8 ? (a.T - s) * tpc : (nkeys + BN - 1) / BN;
+    const FastDiv tdiv = make_fastdiv((uint32_t)tpc);
 
     for (int i = tid; i < a.T * ppc; i += NTH) ptab[i] = a.table[i];
 
@@ -285,61 +301,73 @@ __global__ __launch_bounds__(NTH, NW == 4 ? 2 : 1) void attn_kernel(AttnArgs a) 
         cl = c * sq;
     }
 
-    // Flat key indices of the next tile this lane (K: key row `lane`) and this
-    // wave (V: key chunks wave*VCW ..) load. A chunk is ppc whole pages of pt
-    // tokens, so flat key g is token g % pt of context page g / pt.
-    int kg = lane;
-    int vg[VCW];
-#pragma unroll
-    for (int i = 0; i < VCW; ++i) vg[i] = 8 * (wave * VCW + i);
+    // Tiles of the next K and V DMA. This lane loads key row `lane` of each K
+    // tile, this wave key chunks wave*VCW .. of each V tile. A chunk is ppc
+    // whole pages of pt tokens, so flat key g is token g % pt of context page
+    // g / pt.
+    int ktile = 0, vtile = 0;
     const FastDiv pdiv = make_fastdiv((uint32_t)pt);
-
-    // K instructions of this wave: vectors wave*KPW .. (wave+1)*KPW-1 below KV;
-    // fp8 key scales (64 x 4 B) go with the last wave
-    const int kmine = max(0, min(KPW, KV - wave * KPW));
-    const bool scale_wave = FP8 && wave == NW - 1;
-    // vector memory instructions one full step issues in this wave (the same
-    // in every wave, plus the scale load of the last wave, when KV % NW == 0)
-    const int ndma = kmine + (scale_wave ? 1 : 0) + VCW * VDH;
-    constexpr int kDmaUniform = KV % NW == 0 ? KPW + VCW * VDH : -1;
-    auto wait_older_dma = [&]() {
-        if constexpr (kDmaUniform < 0) {
-            wait_vmem_upto(ndma);
-        } else if constexpr (FP8) {
-            if (scale_wave) wait_vmem_n<kDmaUniform + 1>();
-            else wait_vmem_n<kDmaUniform>();
+    // flat key index of offset o (< 64) in tile t, and whether it is legal
+    auto tile_key = [&](int t, int o, bool& ok) -> int {
+        if constexpr (FP8) {
+            const int c = (int)fast_div((uint32_t)t, tdiv);
+            const int o64 = (t - c * tpc) * BN + o;
+            ok = c < a.T - s && o64 < N;
+            return c * N + o64;
         } else {
-            wait_vmem_n<kDmaUniform>();
+            const int g = t * BN + o;
+            ok = g < nkeys;
+            return g;
         }
     };
 
-    __syncthreads();                               // ptab visible
+    // K instructions of this wave: vectors wave*KPW .. (wave+1)*KPW-1 below KV
+    const int kmine = max(0, min(KPW, KV - wave * KPW));
+    // vector memory instructions one full step issues in this wave (the same
+    // in every wave when KV % NW == 0)
+    const int ndma = kmine + VCW * VDH;
+    constexpr int kDmaUniform = KV % NW == 0 ? KPW + VCW * VDH : -1;
+    auto wait_older_dma = [&]() {
+        if constexpr (kDmaUniform < 0) wait_vmem_upto(ndma);
+        else wait_vmem_n<kDmaUniform>();
+    };
 
-    const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<float*>(FP8 ? a.kscale : nullptr), (short)0, FP8 ? a.sbytes : 0, 0x00020000);
+    __syncthreads();                               // ptab visible
+    if constexpr (FP8) {
+        // key scale of every tile: the scale of its block's first token
+        for (int i = tid; i < ntiles; i += NTH) {
+            const int c = (int)fast_div((uint32_t)i, tdiv);
+            const int n = (i - c * tpc) * BN;
+            const int pg = n / pt, tok = n - pg * pt;
+            g_stab[i] = a.kscale[((int64_t)ptab[c * ppc + pg] * a.heads + head) * pt + tok];
+        }
+    }
     // Offsets of the next tile's DMA are computed one tile ahead (page-table
     // lookup in LDS plus the page arithmetic), right after the previous DMA is
     // issued, so that their latency overlaps the step's MFMA work and the DMA
     // issue after the barrier is a handful of scalar and buffer instructions.
-    uint32_t koff = kOOB, soff = kOOB;             // this lane's key row of the next K tile
+    uint32_t koff = kOOB;                          // this lane's key row of the next K tile
     uint32_t voff[VCW];                            // this wave's key chunks of the next V tile
     auto k_addr = [&]() {
-        const uint32_t gi = (uint32_t)min(kg, nkeys - 1);       // clamped: the lookup stays in the table
+        bool ok;
+        const int g = tile_key(ktile, lane, ok);
+        const uint32_t gi = ok ? (uint32_t)g : 0u;              // the lookup stays in the table
         const uint32_t pidx = fast_div(gi, pdiv);
         const uint32_t tok = gi - pidx * (uint32_t)pt;
         const int64_t ph = (int64_t)ptab[pidx] * a.heads + head;
         const uint32_t off = FP8 ? (uint32_t)(ph * head_blk + (int64_t)tok * 16)
                                  : (uint32_t)((ph * head_blk + (int64_t)tok * 8) * 2);
-        koff = kg < nkeys ? off : kOOB;
-        soff = kg < nkeys ? (uint32_t)((ph * pt + tok) * 4) : kOOB;
+        koff = ok ? off : kOOB;
     };
     auto v_addr = [&](int i) {
-        const uint32_t gi = (uint32_t)min(vg[i], nkeys - 1);
+        bool ok;
+        const int g = tile_key(vtile, 8 * (wave * VCW + i), ok);
+        const uint32_t gi = ok ? (uint32_t)g : 0u;
         const uint32_t pidx = fast_div(gi, pdiv);
         const uint32_t tok = gi - pidx * (uint32_t)pt;
         const uint32_t off =
             (uint32_t)((((int64_t)ptab[pidx] * a.heads + head) * head_blk + (int64_t)tok * D) * 2);
-        voff[i] = vg[i] < nkeys ? off : kOOB;
+        voff[i] = ok ? off : kOOB;
     };
     k_addr();
 #pragma unroll
@@ -347,7 +375,7 @@ __global__ __launch_bounds__(NTH, NW == 4 ? 2 : 1) void attn_kernel(AttnArgs a) 
 
     auto dma_k = [&](uint16_t* kl) {
         // one instruction per 16-byte vector: bf16 K [vector][key][8 ch],
-        // fp8 K8 [vector][key][16 ch] followed by the 64 key scales
+        // fp8 K8 [vector][key][16 ch]
         uint8_t* kb8 = reinterpret_cast<uint8_t*>(kl);
 #pragma unroll
         for (int i = 0; i < KPW; ++i) {
@@ -355,8 +383,7 @@ __global__ __launch_bounds__(NTH, NW == 4 ? 2 : 1) void attn_kernel(AttnArgs a) 
             if (KV % NW == 0 || i < kmine)
                 dma16(krs, kb8 + vec * BN * 16, koff == kOOB ? kOOB : koff + (uint32_t)(vec * pt * 16));
         }
-        if (scale_wave) dma4(srs, kb8 + D * BN, soff);
-        kg += BN;
+        ++ktile;
         k_addr();
     };
     auto dma_v = [&](uint16_t* vl) {
@@ -367,9 +394,10 @@ __global__ __launch_bounds__(NTH, NW == 4 ? 2 : 1) void attn_kernel(AttnArgs a) 
             for (int h = 0; h < VDH; ++h)
                 dma16(vrs, vl + (kc * D + 64 * h) * 8,
                       voff[i] == kOOB ? kOOB : voff[i] + (uint32_t)((64 * h + lane) * 16));
-            vg[i] += BN;
-            v_addr(i);
         }
+        ++vtile;
+#pragma unroll
+        for (int i = 0; i < VCW; ++i) v_addr(i);
     };
 
     f32x16 oacc[DB];
@@ -380,7 +408,8 @@ __global__ __launch_bounds__(NTH, NW == 4 ? 2 : 1) void attn_kernel(AttnArgs a) 
     float m_run = -INFINITY;   // running max of raw scores (may lag by < 2^8 in exp2 units)
     float l_run = 0.f;         // this lane's partial row sum (of the bf16-rounded weights)
 
-    auto compute_s = [&](const uint16_t* kl, f32x16 (&S)[2]) {
+    auto compute_s = [&](const uint16_t* kl, TileS& T) {
+        f32x16 (&S)[2] = T.s;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -407,10 +436,10 @@ __global__ __launch_bounds__(NTH, NW == 4 ? 2 : 1) void attn_kernel(AttnArgs a) 
                 }
         }
     };
-    // fp8: per-lane bias q8 . mean(chunk) of the chunk a tile starts in (b0)
-    // and of the next one (b1); recomputed only when tiles enter a new chunk.
-    int bchunk = 0, bend = N;
-    float b0 = 0.f, b1 = 0.f;
+    // fp8: this lane's bias q8 . mean(chunk) for the chunk of the tile
+    // dequantised next; recomputed only when tiles enter a new chunk.
+    int bchunk = 0;
+    float bcur = 0.f;
     auto chunk_bias = [&](int pos) -> float {
         if (pos >= a.T - s) return 0.f;
         const int g = ptab[pos * ppc] / ppc;
@@ -432,49 +461,34 @@ __global__ __launch_bounds__(NTH, NW == 4 ? 2 : 1) void attn_kernel(AttnArgs a) 
         const auto sw = __builtin_amdgcn_permlane32_swap(ab, ab, false, false);
         return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
     };
-    // Chunk state (bend, b0, b1) for the tile dequantised next. Advanced at
-    // the end of a step, outside the MFMA/VALU interleaving, since it
-    // branches and loads the means only when tiles enter a new chunk.
+    // Advanced at the end of a step, outside the MFMA/VALU interleaving,
+    // since it branches and loads the means only when tiles enter a new chunk.
     auto chunk_advance = [&](int tile) {
         if constexpr (FP8) {
-            const int kbase = tile * BN;
-            while (kbase >= bend) {
-                ++bchunk;
-                bend += N;
-                b0 = b1;
-                b1 = chunk_bias(bchunk + 1);
+            const int c = (int)fast_div((uint32_t)tile, tdiv);
+            if (c != bchunk) {
+                bchunk = c;
+                bcur = chunk_bias(c);
             }
         }
     };
-    auto dequant_scores = [&](const uint16_t* kl, f32x16 (&S)[2], int tile) {
-        const int kbase = tile * BN;
-        const float* ksc = reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(kl) + D * BN);
-        const int lim = bend - kbase - 8 * hf;         // lane-relative first key of the next chunk
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int g4 = 0; g4 < 4; ++g4) {
-                // elements 4*g4 .. 4*g4+3 hold four consecutive keys
-                const int key0 = 32 * kb + 16 * (g4 >> 1) + 4 * (g4 & 1);
-                const float4 sk = *reinterpret_cast<const float4*>(ksc + key0 + 8 * hf);
-                const float skv[4] = {sk.x, sk.y, sk.z, sk.w};
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float b = key0 + e < lim ? b0 : b1;
-                    S[kb][4 * g4 + e] = fmaf(S[kb][4 * g4 + e], skv[e], b);
-                }
-            }
-    };
     // Row max of tile `tile`, then the running-max update; O and l are
     // rescaled only when the max grows by more than 2^8 in exp2 units (a
-    // wave-uniform, rare branch). Only the last tile of a prefix can hold keys
-    // past it; the masking variant (maskc = true) is instantiated outside the
-    // main loop only, so the steady-state loop carries no masking code.
-    auto update_max = [&](f32x16 (&S)[2], int tile, auto maskc, const uint16_t* kl) {
-        if constexpr (FP8) dequant_scores(kl, S, tile);
-        if constexpr (decltype(maskc)::value) {
-            const int lim = nkeys - tile * BN - 8 * hf;     // keys >= lim (lane-relative) are masked
-            if (lim < BN) {
+    // wave-uniform, rare branch). bf16: only the last tile of a prefix can
+    // hold keys past it; the masking variant (maskc = true) is instantiated
+    // outside the main loop only, so the steady-state loop carries no masking
+    // code. fp8: the last tile of every chunk is masked when partial (a
+    // uniform branch), and the max of the raw accumulator maps through the
+    // tile's affine dequantisation.
+    auto update_max = [&](TileS& T, int tile, auto maskc) {
+        f32x16 (&S)[2] = T.s;
+        constexpr bool kMaskBf16 = !FP8 && decltype(maskc)::value;
+        int rem = BN;                                  // legal keys of this tile (wave-uniform)
+        if constexpr (FP8) rem = N - (tile - (int)fast_div((uint32_t)tile, tdiv) * tpc) * BN;
+        else if constexpr (kMaskBf16) rem = nkeys - tile * BN;
+        if (FP8 || kMaskBf16) {
+            if (rem < BN) {
+                const int lim = rem - 8 * hf;          // keys >= lim (lane-relative) are masked
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -492,6 +506,11 @@ __global__ __launch_bounds__(NTH, NW == 4 ? 2 : 1) void attn_kernel(AttnArgs a) 
         const uint32_t mb = __float_as_uint(mx);
         const auto sw = __builtin_amdgcn_permlane32_swap(mb, mb, false, false);
         mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+        if constexpr (FP8) {
+            T.sk = g_stab[tile];
+            T.b = bcur;
+            mx = fmaf(mx, T.sk, T.b);
+        }
         const float m_new = fmaxf(m_run, mx);
         if (__any((m_new - m_run) * cl > (float)kRescaleLog2)) {
             const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * cl);
@@ -508,15 +527,19 @@ __global__ __launch_bounds__(NTH, NW == 4 ? 2 : 1) void attn_kernel(AttnArgs a) 
     // exactly. With the permuted K rows, elements 8g..8g+7 of accumulator
     // block kb are keys 16*(2*kb+g) + 8*hf + 0..7: the B operand of PV group
     // G = 2*kb+g as it stands, matching V^T in LDS (key chunk 2*G + hf).
-    auto exp_pack = [&](f32x16 (&S)[2], bf16x8 (&P)[4]) {
-        const float mb = m_run * cl;
+    auto exp_pack = [&](TileS& T, bf16x8 (&P)[4]) {
+        f32x16 (&S)[2] = T.s;
+        // exp2 argument = A * acc + B: bf16 A = c, B = -m c; fp8 A = s_k c,
+        // B = (bias - m) c (the tile's affine dequantisation folded in)
+        const float A = FP8 ? T.sk * cl : cl;
+        const float B = FP8 ? (T.b - m_run) * cl : -m_run * cl;
         uint32_t w[2][8];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int j = 0; j < 16; j += 2) {
-                const float p0 = __builtin_amdgcn_exp2f(fmaf(S[kb][j], cl, -mb));
-                const float p1 = __builtin_amdgcn_exp2f(fmaf(S[kb][j + 1], cl, -mb));
+                const float p0 = __builtin_amdgcn_exp2f(fmaf(S[kb][j], A, B));
+                const float p1 = __builtin_amdgcn_exp2f(fmaf(S[kb][j + 1], A, B));
                 w[kb][j >> 1] = pack_bf16x2(p0, p1);
                 l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[kb][j >> 1]),
                                                         kOnes, l_run, false);
@@ -550,7 +573,7 @@ __global__ __launch_bounds__(NTH, NW == 4 ? 2 : 1) void attn_kernel(AttnArgs a) 
     using Main = std::integral_constant<bool, true>;   // every fetch is issued; tile t+1 is not the last
     using Tail = std::integral_constant<bool, false>;  // one of the last steps
     auto step = [&](int t, const uint16_t* k_next, uint16_t* k_fill, const uint16_t* v_cur,
-                    uint16_t* v_fill, f32x16 (&Scur)[2], f32x16 (&Snext)[2],
+                    uint16_t* v_fill, TileS& Scur, TileS& Snext,
                     auto mainc) __attribute__((always_inline)) {
         constexpr bool kMain = decltype(mainc)::value;
         tile_barrier();
@@ -561,12 +584,12 @@ __global__ __launch_bounds__(NTH, NW == 4 ? 2 : 1) void attn_kernel(AttnArgs a) 
         exp_pack(Scur, P);
         compute_pv(v_cur, P);
         if constexpr (kMain) {
-            update_max(Snext, t + 1, NoMask{}, k_next);
+            update_max(Snext, t + 1, NoMask{});
             sched_pipeline<D, FP8>();
             wait_older_dma();
         } else {
             sched_pipeline<D, FP8>();
-            if (t + 1 < ntiles) update_max(Snext, t + 1, Mask{}, k_next);
+            if (t + 1 < ntiles) update_max(Snext, t + 1, Mask{});
             wait_vmem();
         }
         chunk_advance(t + 2);
@@ -579,13 +602,10 @@ __global__ __launch_bounds__(NTH, NW == 4 ? 2 : 1) void attn_kernel(AttnArgs a) 
     });
     wait_vmem();
     __syncthreads();
-    f32x16 SA[2], SB[2];
-    if constexpr (FP8) {
-        b0 = chunk_bias(0);
-        b1 = chunk_bias(1);
-    }
+    TileS SA, SB;
+    if constexpr (FP8) bcur = chunk_bias(0);
     compute_s(kbuf<0>(), SA);
-    update_max(SA, 0, Mask{}, kbuf<0>());
+    update_max(SA, 0, Mask{});
     chunk_advance(1);
     int t = 0;
     // steady state, NSTG steps per iteration with fixed buffers: step t + j
@@ -621,8 +641,7 @@ __global__ __launch_bounds__(NTH, NW == 4 ? 2 : 1) void attn_kernel(AttnArgs a) 
         const int b = t % NSTG;
         step(t, kbuf_rt((b + 1) % NSTG), kbuf_rt(b), vbuf_rt(b), vbuf_rt((b + NSTG - 1) % NSTG), SA, SB,
              Tail{});
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) SA[kb] = SB[kb];
+        SA = SB;
     }
 
     // normalise and store: lane holds O[qrow][32*db + 8*(j/4) + 4*hf + j%4]

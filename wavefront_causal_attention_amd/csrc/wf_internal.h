@@ -9,6 +9,7 @@ namespace wf {
 constexpr int kMaxSlots = 64;      // context positions per round (bit per position)
 constexpr int kMaxTablePages = 1024;  // T * pages_per_chunk, staged in LDS by attention
 constexpr int kFp8Block = 64;      // tokens per fp8 scale block (restarts at each chunk)
+constexpr int kMaxFp8Tiles = 4096;  // (context chunks) x (64-token blocks per chunk), fp8 attention
 #ifndef WF_ATTN_BM
 #define WF_ATTN_BM 256
 #endif

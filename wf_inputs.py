@@ -121,6 +121,11 @@ WORKLOADS = {
                            frame_h=8, frame_w=9, page_tokens=24, in_dtype="bf16", qk_dtype="bf16",
                            rope_split=_split(64), rope_theta=1e4, seed=14,
                            description="S=1, A=2, H=0, chunk 72 (1x8x9), page 24, 2x64, bf16"),
+    # fp8 QK with chunks shorter than one 64-key tile.
+    "tiny_fp8": Workload("tiny_fp8", S=2, A=1, H=1, heads=2, head_dim=64, chunk_frames=1,
+                         frame_h=6, frame_w=8, page_tokens=24, in_dtype="bf16", qk_dtype="fp8",
+                         rope_split=_split(64), rope_theta=1e4, seed=16,
+                         description="fp8 QK, chunk 48 (1x6x8), page 24, 2x64, separate inputs"),
     # fp8 QK at head_dim 64 from separate Q/K/V inputs.
     "ragged_fp8_64": Workload("ragged_fp8_64", S=2, A=1, H=1, heads=2, head_dim=64, chunk_frames=2,
                               frame_h=6, frame_w=10, page_tokens=40, in_dtype="bf16", qk_dtype="fp8",
