@@ -342,8 +342,17 @@ __global__ void kmean_reduce_kernel(PublishArgs a) {
     const int s = a.slot_first + blockIdx.y, head = blockIdx.x, d = threadIdx.x;
     const int g = a.table[(a.T - 1 - s) * a.ppc] / a.ppc;
     const float* src = a.kpart + ((int64_t)g * a.heads + head) * a.nblk * D + d;
+    // eight loads in flight per iteration, summed in block order
     float sum = 0.f;
-    for (int b = 0; b < a.nblk; ++b) sum += src[(int64_t)b * D];
+    int b = 0;
+    for (; b + 8 <= a.nblk; b += 8) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = src[(int64_t)(b + u) * D];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) sum += v[u];
+    }
+    for (; b < a.nblk; ++b) sum += src[(int64_t)b * D];
     a.kmean[((int64_t)g * a.heads + head) * D + d] = sum / (float)a.N;
 }
 
