@@ -365,7 +365,6 @@ int wf_attention_round(wf_handle* h, int32_t layer, int32_t slot_first, int32_t 
     a.vbytes = (int32_t)L.v_layer;
     a.kscale = fp8 ? (const float*)(h->pool + L.scale_off + L.scale_layer * layer) : nullptr;
     a.kmean = fp8 ? (const float*)(h->pool + L.mean_off + L.mean_layer * layer) : nullptr;
-    a.sbytes = fp8 ? (int32_t)L.scale_layer : 0;
     a.table = h->table;
     const int wl = slot_first * (c.S + 1) + nslots - 1;
     a.work = (const int32_t*)(h->pool + L.work_off + L.work_stride * wl);

@@ -79,7 +79,6 @@ struct AttnArgs {
     int32_t kbytes, vbytes;   // bytes of this layer's K / V regions (< 2^31)
     const float* kscale;      // fp8: per-token K scale [phys][head][pt]
     const float* kmean;       // fp8: [group][head][D]
-    int32_t sbytes;           // fp8: bytes of this layer's kscale region
     const int32_t* table;     // [T][ppc]
     const int32_t* work;      // per-workgroup (slot, head, qtile), -1 = idle
     int nwork;                // workgroups in the launch (multiple of kXcds)
