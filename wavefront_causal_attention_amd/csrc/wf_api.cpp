@@ -31,30 +31,129 @@ struct Layout {
 };
 
 // Attention work order for query slots [first, first + n): every (slot, head,
-// query tile) unit, cost = keys it reads. Units are laid out head-major and cut
-// into kXcds contiguous pieces of equal cost, so one head's K/V is streamed by
-// one or two XCDs (each XCD has its own L2); inside a piece, longest first.
-// Workgroup b runs piece b % kXcds, entry b / kXcds. Returns the padded list.
-std::vector<int32_t> build_work_list(int first, int n, int heads, int qtiles, int T) {
-    struct U { int s, h, q; int64_t cost; };
-    std::vector<U> u;
+// query tile) unit, cost = key chunks it reads. Units are laid out head-major
+// and cut into kXcds contiguous pieces of equal cost (each unit goes to the
+// piece holding its cost midpoint), so one head's K/V is streamed by one or
+// two XCDs (each XCD has its own L2). Workgroup b runs piece b % kXcds, entry
+// b / kXcds. Returns the padded list.
+//
+// Inside a piece the order serves the hardware dispatcher, which hands the
+// next workgroup to the first CU that frees up (one workgroup per CU here):
+// the units are first packed onto the XCD's CUs (longest first onto the least
+// loaded CU, then moves and swaps that lower the most loaded CU), and then
+// emitted by their planned start times, so that dispatch replays the packing
+// when run times follow the cost model and still adapts when they do not.
+struct WorkUnit {
+    int s, h, q;
+    int64_t cost;
+};
+
+static void order_piece(std::vector<WorkUnit>& p, int bins) {
+    const int n = (int)p.size();
+    std::vector<int> idx(n);
+    for (int i = 0; i < n; ++i) idx[i] = i;
+    std::stable_sort(idx.begin(), idx.end(), [&](int x, int y) { return p[x].cost > p[y].cost; });
+    if (bins <= 1 || n <= 1) {
+        std::vector<WorkUnit> out;
+        for (int i : idx) out.push_back(p[i]);
+        p.swap(out);
+        return;
+    }
+    std::vector<std::vector<int>> bin(bins);
+    std::vector<int64_t> load(bins, 0);
+    for (int i : idx) {
+        const int b = (int)(std::min_element(load.begin(), load.end()) - load.begin());
+        bin[b].push_back(i);
+        load[b] += p[i].cost;
+    }
+    // descent on the most loaded bin; every accepted move or swap makes the
+    // pair's loads more even, so the sum of squared loads strictly falls
+    std::vector<int> by_load(bins);
+    for (int iter = 0; iter < 100000; ++iter) {
+        const int hi = (int)(std::max_element(load.begin(), load.end()) - load.begin());
+        for (int b = 0; b < bins; ++b) by_load[b] = b;
+        std::stable_sort(by_load.begin(), by_load.end(), [&](int x, int y) { return load[x] < load[y]; });
+        bool moved = false;
+        for (int lo : by_load) {
+            if (lo == hi) continue;
+            int64_t best = load[hi];
+            int bi = -1, bj = -1;
+            for (size_t i = 0; i < bin[hi].size(); ++i) {
+                const int64_t ci = p[bin[hi][i]].cost;
+                if (std::max(load[hi] - ci, load[lo] + ci) < best) {
+                    best = std::max(load[hi] - ci, load[lo] + ci);
+                    bi = (int)i;
+                    bj = -1;
+                }
+                for (size_t j = 0; j < bin[lo].size(); ++j) {
+                    const int64_t d = ci - p[bin[lo][j]].cost;
+                    if (d > 0 && std::max(load[hi] - d, load[lo] + d) < best) {
+                        best = std::max(load[hi] - d, load[lo] + d);
+                        bi = (int)i;
+                        bj = (int)j;
+                    }
+                }
+            }
+            if (bi < 0) continue;
+            const int ui = bin[hi][bi];
+            if (bj < 0) {
+                bin[hi].erase(bin[hi].begin() + bi);
+                bin[lo].push_back(ui);
+                load[hi] -= p[ui].cost;
+                load[lo] += p[ui].cost;
+            } else {
+                const int uj = bin[lo][bj];
+                bin[hi][bi] = uj;
+                bin[lo][bj] = ui;
+                load[hi] += p[uj].cost - p[ui].cost;
+                load[lo] += p[ui].cost - p[uj].cost;
+            }
+            moved = true;
+            break;
+        }
+        if (!moved) break;
+    }
+    // planned start times: each CU runs its units longest first
+    struct Start { int64_t t, neg_cost; int i; };
+    std::vector<Start> st;
+    st.reserve(n);
+    for (auto& b : bin) {
+        std::stable_sort(b.begin(), b.end(), [&](int x, int y) { return p[x].cost > p[y].cost; });
+        int64_t t = 0;
+        for (int i : b) {
+            st.push_back({t, -p[i].cost, i});
+            t += p[i].cost;
+        }
+    }
+    std::sort(st.begin(), st.end(), [](const Start& x, const Start& y) {
+        return x.t != y.t ? x.t < y.t : x.neg_cost != y.neg_cost ? x.neg_cost < y.neg_cost : x.i < y.i;
+    });
+    std::vector<WorkUnit> out;
+    out.reserve(n);
+    for (const Start& x : st) out.push_back(p[x.i]);
+    p.swap(out);
+}
+
+// cus_per_xcd <= 0 skips the ordering (list sizes do not depend on it).
+std::vector<int32_t> build_work_list(int first, int n, int heads, int qtiles, int T, int cus_per_xcd) {
+    std::vector<WorkUnit> u;
     u.reserve((size_t)n * heads * qtiles);
     for (int h = 0; h < heads; ++h)
         for (int s = first; s < first + n; ++s)
             for (int q = 0; q < qtiles; ++q) u.push_back({s, h, q, (int64_t)(T - s)});
     int64_t total = 0;
-    for (const U& x : u) total += x.cost;
-    std::vector<std::vector<U>> piece(wf::kXcds);
+    for (const WorkUnit& x : u) total += x.cost;
+    std::vector<std::vector<WorkUnit>> piece(wf::kXcds);
     int64_t acc = 0;
-    for (const U& x : u) {
-        int xcd = (int)((acc * wf::kXcds + total / 2 / wf::kXcds) / std::max<int64_t>(total, 1));
+    for (const WorkUnit& x : u) {
+        int xcd = (int)((2 * acc + x.cost) * wf::kXcds / std::max<int64_t>(2 * total, 1));
         xcd = std::min(std::max(xcd, 0), wf::kXcds - 1);
         piece[xcd].push_back(x);
         acc += x.cost;
     }
     size_t M = 0;
     for (auto& p : piece) {
-        std::stable_sort(p.begin(), p.end(), [](const U& a, const U& b) { return a.cost > b.cost; });
+        if (cus_per_xcd > 0) order_piece(p, cus_per_xcd);
         M = std::max(M, p.size());
     }
     std::vector<int32_t> out(M * wf::kXcds, -1);
@@ -129,7 +228,7 @@ int validate(const wf_config* c, Layout* L) {
         size_t longest = 0;
         for (int first = 0; first <= c->S; ++first)
             for (int n = 1; first + n <= c->S + 1; ++n)
-                longest = std::max(longest, build_work_list(first, n, c->heads, qtiles, T).size());
+                longest = std::max(longest, build_work_list(first, n, c->heads, qtiles, T, 0).size());
         L->work_len = (int)longest;
         L->work_stride = align_up(longest * 4, 256);
         L->work_off = off;
@@ -258,9 +357,16 @@ int wf_pool_create(const wf_config* cfg, void* pool_dev, size_t pool_bytes,
     if (e == hipSuccess)
         e = hipMemcpy(h->pool + L.omega_off, om.data(), om.size() * 8, hipMemcpyHostToDevice);
     const int qtiles = (L.N + wf::kAttnBM - 1) / wf::kAttnBM;
+    int cus = 0;
+    if (e == hipSuccess) {
+        int dev = 0;
+        e = hipGetDevice(&dev);
+        if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    }
+    const int cus_per_xcd = std::max(1, cus / wf::kXcds);
     for (int first = 0; first <= cfg->S && e == hipSuccess; ++first)
         for (int n = 1; first + n <= cfg->S + 1 && e == hipSuccess; ++n) {
-            std::vector<int32_t> wl = build_work_list(first, n, cfg->heads, qtiles, L.T);
+            std::vector<int32_t> wl = build_work_list(first, n, cfg->heads, qtiles, L.T, cus_per_xcd);
             if ((int)wl.size() > L.work_len) { e = hipErrorInvalidValue; break; }
             h->work_count[first * (cfg->S + 1) + n - 1] = (int)wl.size();
             e = hipMemcpy(h->pool + L.work_off + L.work_stride * (first * (cfg->S + 1) + n - 1),
