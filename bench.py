@@ -25,8 +25,10 @@ METRIC = "wavefront-round attention TFLOP/s + rounds/sec, 1 MI355X, Wan2.1-1.3B 
 PEAK_BF16_TFLOPS = 2500.0          # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0             # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_bf16_wan1.3b_s4_traffic.txt")
+# the attention kernel and the host code that orders its work (the order
+# decides which K/V reads hit L2, so it changes the traffic)
 ATTN_SOURCES = [os.path.join(ROOT, "wavefront_causal_attention_amd", "csrc", f)
-                for f in ("wf_attention.hip", "wf_internal.h")]
+                for f in ("wf_attention.hip", "wf_internal.h", "wf_api.cpp")]
 
 
 def kernel_source_hash() -> str:
