@@ -41,7 +41,7 @@ def slot_attention(q, k_ctx, v_ctx, scale, block=512, return_p=False):
     return out
 
 
-def round_attention(Qs, ctx_k, ctx_v, S, A, H, rows=None, slots=None, scale=None):
+def round_attention(Qs, ctx_k, ctx_v, S, A, H, rows=None, slots=None, scale=None, kind="wavefront"):
     """Per-slot gather formulation.
 
     Qs:     [S+1, N, heads, d]     post-storage queries of live slots s = 0..S
@@ -59,7 +59,7 @@ def round_attention(Qs, ctx_k, ctx_v, S, A, H, rows=None, slots=None, scale=None
     heads = Qs.shape[2]
     out = np.zeros((len(slots), len(rows), heads, ctx_v.shape[-1]), dtype=np.float64)
     for si, s in enumerate(slots):
-        pos = legal_positions(s, S, A, H)
+        pos = legal_positions(s, S, A, H, kind)
         for h in range(heads):
             kc = np.concatenate([ctx_k[p][:, h, :] for p in pos], axis=0)
             vc = np.concatenate([ctx_v[p][:, h, :] for p in pos], axis=0)
@@ -67,16 +67,16 @@ def round_attention(Qs, ctx_k, ctx_v, S, A, H, rows=None, slots=None, scale=None
     return out
 
 
-def dense_round_attention(Qs, ctx_k, ctx_v, S, A, H, scale=None, return_p=False):
+def dense_round_attention(Qs, ctx_k, ctx_v, S, A, H, scale=None, return_p=False, kind="wavefront"):
     """Second formulation: one dense softmax per head over every query row of the
-    round against every key of the context, with M_WF expanded to a token mask.
-    Small inputs only.
+    round against every key of the context, with the live mask (M_WF by
+    default) expanded to a token mask. Small inputs only.
     """
     Qs = np.asarray(Qs, dtype=np.float64)
     S1, N, heads, d = Qs.shape
     T = ctx_k.shape[0]
     scale = 1.0 / np.sqrt(d) if scale is None else scale
-    M = live_mask(S)
+    M = live_mask(S, kind)
     # chunk-level visibility [query slot, context position]
     vis = np.zeros((S + 1, T), dtype=bool)
     for s in range(S + 1):

@@ -88,10 +88,11 @@ def rotated_context(shape, k, live, clean, storage="bf16"):
     return Qs, ctx_k, ctx_v, ids
 
 
-def oracle_round(shape, k, live, clean, storage="bf16", rows=None, slots=None):
+def oracle_round(shape, k, live, clean, storage="bf16", rows=None, slots=None, mask="wavefront"):
     """O[slots, rows, heads, d] (fp64) of one wavefront round.
 
-    See rotated_context for the inputs; rows/slots restrict what is evaluated.
+    See rotated_context for the inputs; rows/slots restrict what is evaluated;
+    mask selects the live-slot visibility (see schedule.live_mask).
     """
     Qs, ctx_k, ctx_v, _ = rotated_context(shape, k, live, clean, storage)
-    return round_attention(Qs, ctx_k, ctx_v, shape.S, shape.A, shape.H, rows=rows, slots=slots)
+    return round_attention(Qs, ctx_k, ctx_v, shape.S, shape.A, shape.H, rows=rows, slots=slots, kind=mask)

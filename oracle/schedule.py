@@ -18,12 +18,20 @@ from collections import deque
 import numpy as np
 
 
-def live_mask(S: int) -> np.ndarray:
-    """M_WF over the S+1 live slots (store included), indexed [query s][key j]."""
+def live_mask(S: int, kind: str = "wavefront") -> np.ndarray:
+    """Visibility among the S+1 live slots (store included), indexed [query s][key j].
+
+    "wavefront": M_WF(s, j) = 1[j >= s] (hyper.ai summary, "Method").
+    "all": every live slot sees every live slot, the bidirectional live K/V of
+    Rolling Forcing that the pages contrast Wave Forcing with (thelatestinai.com
+    listing, Table 9; e-cogni.com.br, "Como funciona").
+    """
+    if kind not in ("wavefront", "all"):
+        raise ValueError("unknown live mask %r" % kind)
     M = np.zeros((S + 1, S + 1), dtype=np.int64)
     for s in range(S + 1):
         for j in range(S + 1):
-            M[s, j] = 1 if j >= s else 0
+            M[s, j] = 1 if (kind == "all" or j >= s) else 0
     return M
 
 
@@ -36,13 +44,13 @@ def slot_position(s: int, S: int, A: int, H: int) -> int:
     return A + H + 1 + (S - 1 - s)
 
 
-def legal_positions(s: int, S: int, A: int, H: int) -> list:
+def legal_positions(s: int, S: int, A: int, H: int, kind: str = "wavefront") -> list:
     """Context positions query slot s may read, in context order.
 
     Anchor and clean history are cleaner than every live slot and are read by
-    all of them; among live slots the mask M_WF decides.
+    all of them; among live slots the live mask (M_WF by default) decides.
     """
-    M = live_mask(S)
+    M = live_mask(S, kind)
     out = list(range(A)) + list(range(A, A + H))
     live = [j for j in range(S, -1, -1) if M[s, j]]          # store first, then S-1 .. 0
     out += [slot_position(j, S, A, H) for j in live]

@@ -170,3 +170,39 @@ def test_rope_positions_follow_the_schedule():
     out = oracle_round(w, k, live, clean, storage="exact")
     for s in range(w.S + 1):
         assert np.max(np.abs(out[s] - sch.slot_chunk(s))) <= 1e-9, s
+
+
+# --- the all-live mask (bidirectional live K/V, the Rolling Forcing contrast) ---
+
+@pytest.mark.parametrize("S,A,H", [(2, 1, 2), (3, 1, 0), (4, 2, 1)])
+def test_all_live_gather_equals_dense(S, A, H):
+    Qs, ck, cv = _random_ctx(S, A, H, 12, 2, 8, seed=100 + S)
+    a = round_attention(Qs, ck, cv, S, A, H, kind="all")
+    b = dense_round_attention(Qs, ck, cv, S, A, H, kind="all")
+    assert np.max(np.abs(a - b)) <= 1e-12
+
+
+@pytest.mark.parametrize("S", [1, 3])
+def test_all_live_each_slot_is_sdpa_over_the_whole_context(S):
+    # every slot attends to every context position: plain library attention
+    # over the concatenation of all T chunks, no mask
+    A, H, N, heads, d = 1, 1, 20, 2, 16
+    Qs, ck, cv = _random_ctx(S, A, H, N, heads, d, seed=200 + S)
+    T = A + H + S + 1
+    out = round_attention(Qs, ck, cv, S, A, H, kind="all")
+    k = torch.from_numpy(ck.reshape(T * N, heads, d)).permute(1, 0, 2)
+    v = torch.from_numpy(cv.reshape(T * N, heads, d)).permute(1, 0, 2)
+    for s in range(S + 1):
+        q = torch.from_numpy(Qs[s]).permute(1, 0, 2)
+        ref = torch.nn.functional.scaled_dot_product_attention(q, k, v).permute(1, 0, 2).numpy()
+        assert np.max(np.abs(out[s] - ref)) <= 1e-12
+
+
+def test_noisiest_slot_reads_the_same_under_both_masks():
+    # M_WF(0, j) = 1 for every live j, so slot 0 already sees everything
+    S, A, H = 3, 1, 2
+    Qs, ck, cv = _random_ctx(S, A, H, 10, 2, 8, seed=300)
+    wf_ = round_attention(Qs, ck, cv, S, A, H)
+    al = round_attention(Qs, ck, cv, S, A, H, kind="all")
+    assert np.array_equal(wf_[0], al[0])
+    assert all(np.max(np.abs(wf_[s] - al[s])) > 1e-3 for s in range(1, S + 1))

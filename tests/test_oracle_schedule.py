@@ -109,3 +109,14 @@ def test_table8_chunk_bytes():
     # head_dim 128 for both standard Wan2.1 models
     assert shapes["1.3B"]["hidden"] // shapes["1.3B"]["heads"] == 128
     assert shapes["14B"]["hidden"] // shapes["14B"]["heads"] == 128
+
+
+def test_all_live_mask_is_all_ones_and_every_slot_reads_everything():
+    for S in (1, 2, 4):
+        assert (live_mask(S, "all") == 1).all()
+        A, H = 1, 2
+        T = A + H + S + 1
+        for s in range(S + 1):
+            assert legal_positions(s, S, A, H, "all") == list(range(T))
+    with pytest.raises(ValueError):
+        live_mask(2, "rolling")
