@@ -63,6 +63,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="wan1.3b_s4")
     ap.add_argument("--out-dtype", default="bf16", choices=["bf16", "fp32"])
+    ap.add_argument("--live-mask", default="wavefront", choices=["wavefront", "all"],
+                    help="all: every live slot reads every live slot (no tile skipped), for "
+                         "measuring what the wavefront mask saves")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=1024, help="query rows per (slot, head) in the CPU sample")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -87,13 +90,16 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     wf.load()
     w = W.WORKLOADS[args.workload]
+    if args.live_mask != w.live_mask:
+        import dataclasses
+        w = dataclasses.replace(w, live_mask=args.live_mask)
     dev = torch.device("cuda:0")
     k0 = w.steady_round
     cfg = wf.make_config(S=w.S, anchor_chunks=w.A, history_chunks=w.H, heads=w.heads,
                          head_dim=w.head_dim, chunk_frames=w.chunk_frames, frame_h=w.frame_h,
                          frame_w=w.frame_w, page_tokens=w.page_tokens, in_dtype=w.in_dtype,
                          qk_dtype=w.qk_dtype, rope_split=w.rope_split, rope_theta=w.rope_theta,
-                         first_round=k0)
+                         first_round=k0, live_mask=w.live_mask)
     pool = wf.Pool(cfg, device=dev)
     tdt = torch.bfloat16 if w.in_dtype == "bf16" else torch.float32
 
@@ -186,7 +192,8 @@ def main():
         "config": {"workload": w.name, "S": w.S, "anchor_chunks": w.A, "history_chunks": w.H,
                    "chunk_tokens": w.N, "chunk_shape": [w.chunk_frames, w.frame_h, w.frame_w],
                    "heads": w.heads, "head_dim": w.head_dim, "page_tokens": w.page_tokens,
-                   "mask_aware_flops_per_round": F, "out_dtype": args.out_dtype},
+                   "mask_aware_flops_per_round": F, "out_dtype": args.out_dtype,
+                   "live_mask": w.live_mask},
         "rounds_per_sec": round(1e3 / ms_step, 3),
         "attention_ms": round(att_avg, 4),
         "attention_ms_minmax": [round(min(att_ms), 4), round(max(att_ms), 4)],

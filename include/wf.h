@@ -46,6 +46,10 @@ extern "C" {
 #define WF_E_NOT_READY     3   /* a required context position is not published */
 #define WF_E_HIP           4   /* a HIP runtime call failed (see wf_last_error) */
 
+/* live-slot visibility (wf_config.live_mask) */
+#define WF_MASK_WAVEFRONT  0   /* M_WF(s, j) = 1[j >= s]: slot s reads the prefix [0, T-s)    */
+#define WF_MASK_ALL_LIVE   1   /* every live slot reads every live slot: the whole context   */
+
 /* element types */
 #define WF_DTYPE_BF16      0
 #define WF_DTYPE_FP32      1
@@ -68,6 +72,11 @@ typedef struct wf_config {
     int32_t rope_split[3];   /* (d_t, d_h, d_w), even, summing to head_dim          */
     int32_t first_round;     /* round index k of the pool's first round, >= S+H+A   */
     double  rope_theta;      /* RoPE base, e.g. 10000                               */
+    int32_t live_mask;       /* WF_MASK_WAVEFRONT (default) | WF_MASK_ALL_LIVE: the
+                                bidirectional live K/V of Rolling Forcing that the
+                                pages contrast the wavefront mask with
+                                (thelatestinai.com listing, Table 9); no tile is
+                                skipped, for measuring what the mask saves         */
 } wf_config;
 
 typedef struct wf_handle wf_handle;
@@ -134,7 +143,7 @@ int wf_kv_publish(wf_handle* h, int32_t layer, int32_t slot_first, int32_t nslot
  * M_WF(s, j) = 1[j >= s], full attention inside a chunk). One launch computes
  * O = softmax(Q K^T / sqrt(d)) V for query slots [slot_first, slot_first+nslots)
  * of one layer, each over its legal prefix; tiles of noisier slots are never
- * read.
+ * read. With live_mask = WF_MASK_ALL_LIVE every slot reads the whole context.
  *
  * q:        device, as q_out of wf_kv_publish (full [S+1] buffer).
  * q_scales: device fp8 query scales, NULL for bf16.

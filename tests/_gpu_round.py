@@ -15,7 +15,7 @@ def config_of(w: W.Workload, first_round=None, num_layers=1):
                           head_dim=w.head_dim, chunk_frames=w.chunk_frames, frame_h=w.frame_h,
                           frame_w=w.frame_w, page_tokens=w.page_tokens, in_dtype=w.in_dtype,
                           qk_dtype=w.qk_dtype, rope_split=w.rope_split, rope_theta=w.rope_theta,
-                          first_round=first_round, num_layers=num_layers)
+                          first_round=first_round, num_layers=num_layers, live_mask=w.live_mask)
 
 
 def to_dev(x: np.ndarray, in_dtype: str):
@@ -121,7 +121,7 @@ def oracle_rows(w, k, live, clean, rows, heads=None, storage=None, slots=None):
         live = [tuple(take_heads(a, w, heads) for a in x) for x in live]
         clean = {c: tuple(take_heads(a, w, heads) for a in kv) for c, kv in clean.items()}
         w = ws
-    return oracle_round(w, k, live, clean, storage=storage, rows=rows, slots=slots)
+    return oracle_round(w, k, live, clean, storage=storage, rows=rows, slots=slots, mask=w.live_mask)
 
 
 def gpu_rows(out: torch.Tensor, w: W.Workload, rows, heads=None, slots=None):

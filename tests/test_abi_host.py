@@ -67,7 +67,7 @@ def test_wan13b_pool_size_matches_pages(lib):
     ("page_tokens", 100, wf.WF_E_SHAPE), ("page_tokens", 4, wf.WF_E_SHAPE),
     ("in_dtype", 7, wf.WF_E_INVALID_ARG), ("qk_dtype", 1, wf.WF_E_INVALID_ARG),
     ("first_round", 6, wf.WF_E_SHAPE), ("rope_theta", 0.0, wf.WF_E_INVALID_ARG),
-    ("S", 70, wf.WF_E_SHAPE),
+    ("S", 70, wf.WF_E_SHAPE), ("live_mask", 2, wf.WF_E_INVALID_ARG),
 ])
 def test_config_validation(lib, field, value, status):
     c = cfg_of(W.WORKLOADS["wan1.3b_s4"])
@@ -242,5 +242,33 @@ def test_explicit_rope_offsets_validated(lib):
             wf.wf_kv_publish(h, 0, 0, 1, FAKE, FAKE, FAKE, w.hd, [-3], FAKE, None, None)
         assert e.value.status == wf.WF_E_INVALID_ARG
         wf.wf_kv_publish(h, 0, 0, 2, FAKE, FAKE, FAKE, w.hd, [5, 6], FAKE, None, None)
+    finally:
+        wf.wf_pool_destroy(h)
+
+
+def test_all_live_attention_needs_the_whole_context(lib):
+    import dataclasses
+    w = dataclasses.replace(W.WORKLOADS["wan1.3b_s4"], live_mask="all")
+    h = wf.wf_pool_create_host_model(cfg_of(w))
+    T, S = w.T, w.S
+    try:
+        # clean positions and the store only: under M_WF the store would be
+        # ready, under the all-live mask it reads every live slot too
+        wf.wf_kv_publish(h, 0, S + 1, T - S - 1, None, FAKE, FAKE, w.hd, None, None, None, None)
+        wf.wf_kv_publish(h, 0, S, 1, FAKE, FAKE, FAKE, w.hd, None, FAKE, FAKE, None)
+        with pytest.raises(wf.WfError) as e:
+            wf.wf_attention_round(h, 0, S, 1, FAKE, FAKE, FAKE, wf.WF_DTYPE_BF16, None)
+        assert e.value.status == wf.WF_E_NOT_READY
+        wf.wf_kv_publish(h, 0, 0, S, FAKE, FAKE, FAKE, w.hd, None, FAKE, FAKE, None)
+        wf.wf_attention_round(h, 0, S, 1, FAKE, FAKE, FAKE, wf.WF_DTYPE_BF16, None)
+        assert wf.wf_ready_mask(h, 0) == (1 << T) - 1
+    finally:
+        wf.wf_pool_destroy(h)
+    # the wavefront mask accepts the store with only its prefix published
+    h = wf.wf_pool_create_host_model(cfg_of(W.WORKLOADS["wan1.3b_s4"]))
+    try:
+        wf.wf_kv_publish(h, 0, S + 1, T - S - 1, None, FAKE, FAKE, w.hd, None, None, None, None)
+        wf.wf_kv_publish(h, 0, S, 1, FAKE, FAKE, FAKE, w.hd, None, FAKE, FAKE, None)
+        wf.wf_attention_round(h, 0, S, 1, FAKE, FAKE, FAKE, wf.WF_DTYPE_BF16, None)
     finally:
         wf.wf_pool_destroy(h)

@@ -153,3 +153,19 @@ def test_fp8_full_size_sampled():
     say(w.name, "max_abs %.3e rel_l2 %.3e" % (mx, rel))
     assert mx <= FP8_MAX_ABS and rel <= FP8_REL_L2
     assert torch.isfinite(out).all().item()
+
+
+def test_fp8_all_live_mask_round_parity():
+    import dataclasses
+    w = dataclasses.replace(W.WORKLOADS["ragged_fp8"], live_mask="all")
+    say("case", w.name, "fp8 all-live mask")
+    r = RoundRunner(w)
+    r.seed_clean()
+    r.publish_live()
+    out = r.attention("fp32")
+    g = gpu_rows(out, w, np.arange(w.N))
+    assert not np.isnan(g).any()
+    ref = oracle_round(w, r.k, r.live, r.clean_for_round(), storage="fp8", mask="all")
+    mx, rel = err_stats(g, ref)
+    say("fp8 all-live vs storage=fp8: max_abs %.3e rel_l2 %.3e" % (mx, rel))
+    assert mx <= FP8_MAX_ABS and rel <= FP8_REL_L2

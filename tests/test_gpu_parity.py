@@ -280,3 +280,30 @@ def test_rotated_rounds_full_output(name):
         say(name, "round", r.k, "max_abs %.3e rel_l2 %.3e" % (mx, rel))
         assert mx <= BF16_MAX_ABS and rel <= BF16_REL_L2, (i, mx, rel)
         r.advance()
+
+
+@pytest.mark.parametrize("name", ["tiny", "ragged128", "edge_s1_h0"])
+def test_all_live_mask_round_parity(name):
+    """Every live slot sees every live slot (bidirectional live K/V): parity
+    against the oracle's all-live mask; the noisiest slot reads the whole
+    context under either mask, so its output is the wavefront pool's, bit for
+    bit."""
+    import dataclasses
+    w = dataclasses.replace(W.WORKLOADS[name], live_mask="all")
+    say("case", name, "all-live mask")
+    r = RoundRunner(w)
+    r.seed_clean()
+    r.publish_live()
+    out = r.attention("fp32")
+    ref = oracle_round(w, r.k, r.live, r.clean_for_round(), storage="bf16", mask="all")
+    g = gpu_rows(out, w, np.arange(w.N))
+    assert not np.isnan(g).any()
+    mx, rel = err_stats(g, ref)
+    say(name, "all-live fp32-out max_abs %.3e rel_l2 %.3e" % (mx, rel))
+    assert mx <= BF16_MAX_ABS and rel <= BF16_REL_L2
+    rw = RoundRunner(W.WORKLOADS[name])
+    rw.seed_clean()
+    rw.publish_live(live=r.live)
+    outw = rw.attention("fp32")
+    assert torch.equal(outw[0], out[0])
+    assert not torch.equal(outw[1:], out[1:])

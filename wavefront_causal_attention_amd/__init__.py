@@ -8,7 +8,8 @@ All computation runs in the HIP kernels of libwf.so; there is no fallback.
 from __future__ import annotations
 
 from ._lib import (WF_DTYPE_BF16, WF_DTYPE_FP32, WF_DTYPE_FP8_E4M3, WF_E_HIP, WF_E_INVALID_ARG,
-                   WF_E_NOT_READY, WF_E_SHAPE, WF_OK, WfError, load, wf_attention_round, wf_config,
+                   WF_E_NOT_READY, WF_E_SHAPE, WF_MASK_ALL_LIVE, WF_MASK_WAVEFRONT, WF_OK, WfError,
+                   load, wf_attention_round, wf_config,
                    wf_geometry, wf_kv_publish, wf_page_table_host, wf_pool_bytes, wf_pool_create,
                    wf_pool_create_host_model, wf_pool_destroy, wf_ready_mask, wf_round_advance,
                    wf_round_index, wf_schedule_chunk_ids)
@@ -18,7 +19,9 @@ _DT = {"bf16": WF_DTYPE_BF16, "fp32": WF_DTYPE_FP32, "fp8": WF_DTYPE_FP8_E4M3}
 
 def make_config(S, anchor_chunks, history_chunks, heads, head_dim, chunk_frames, frame_h, frame_w,
                 page_tokens, in_dtype="bf16", qk_dtype="bf16", rope_split=None, rope_theta=1e4,
-                first_round=None, num_layers=1) -> wf_config:
+                first_round=None, num_layers=1, live_mask="wavefront") -> wf_config:
+    """live_mask: "wavefront" (M_WF, the default) or "all" (every live slot sees
+    every live slot; no tile is skipped)."""
     c = wf_config()
     c.S, c.anchor_chunks, c.history_chunks = S, anchor_chunks, history_chunks
     c.heads, c.head_dim, c.num_layers = heads, head_dim, num_layers
@@ -30,6 +33,7 @@ def make_config(S, anchor_chunks, history_chunks, heads, head_dim, chunk_frames,
     c.rope_split[0], c.rope_split[1], c.rope_split[2] = rope_split
     c.rope_theta = float(rope_theta)
     c.first_round = S + history_chunks + anchor_chunks if first_round is None else first_round
+    c.live_mask = {"wavefront": WF_MASK_WAVEFRONT, "all": WF_MASK_ALL_LIVE}[live_mask]
     return c
 
 

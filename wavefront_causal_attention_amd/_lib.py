@@ -19,6 +19,9 @@ WF_E_SHAPE = 2
 WF_E_NOT_READY = 3
 WF_E_HIP = 4
 
+WF_MASK_WAVEFRONT = 0
+WF_MASK_ALL_LIVE = 1
+
 WF_DTYPE_BF16 = 0
 WF_DTYPE_FP32 = 1
 WF_DTYPE_FP8_E4M3 = 2
@@ -41,6 +44,7 @@ class wf_config(ctypes.Structure):
         ("rope_split", ctypes.c_int32 * 3),
         ("first_round", ctypes.c_int32),
         ("rope_theta", ctypes.c_double),
+        ("live_mask", ctypes.c_int32),
     ]
 
 

@@ -135,12 +135,13 @@ static void order_piece(std::vector<WorkUnit>& p, int bins) {
 }
 
 // cus_per_xcd <= 0 skips the ordering (list sizes do not depend on it).
-std::vector<int32_t> build_work_list(int first, int n, int heads, int qtiles, int T, int cus_per_xcd) {
+std::vector<int32_t> build_work_list(int first, int n, int heads, int qtiles, int T, bool all_live,
+                                     int cus_per_xcd) {
     std::vector<WorkUnit> u;
     u.reserve((size_t)n * heads * qtiles);
     for (int h = 0; h < heads; ++h)
         for (int s = first; s < first + n; ++s)
-            for (int q = 0; q < qtiles; ++q) u.push_back({s, h, q, (int64_t)(T - s)});
+            for (int q = 0; q < qtiles; ++q) u.push_back({s, h, q, (int64_t)(all_live ? T : T - s)});
     int64_t total = 0;
     for (const WorkUnit& x : u) total += x.cost;
     std::vector<std::vector<WorkUnit>> piece(wf::kXcds);
@@ -183,6 +184,7 @@ int validate(const wf_config* c, Layout* L) {
     if ((int64_t)T * ppc > wf::kMaxTablePages) return WF_E_SHAPE;
     if (c->in_dtype != WF_DTYPE_BF16 && c->in_dtype != WF_DTYPE_FP32) return WF_E_INVALID_ARG;
     if (c->qk_dtype != WF_DTYPE_BF16 && c->qk_dtype != WF_DTYPE_FP8_E4M3) return WF_E_INVALID_ARG;
+    if (c->live_mask != WF_MASK_WAVEFRONT && c->live_mask != WF_MASK_ALL_LIVE) return WF_E_INVALID_ARG;
     const int dt = c->rope_split[0], dh = c->rope_split[1], dw = c->rope_split[2];
     if (dt < 0 || dh < 0 || dw < 0 || (dt | dh | dw) & 1 || dt + dh + dw != c->head_dim) return WF_E_SHAPE;
     if (dt > 64) return WF_E_SHAPE;
@@ -228,7 +230,8 @@ int validate(const wf_config* c, Layout* L) {
         size_t longest = 0;
         for (int first = 0; first <= c->S; ++first)
             for (int n = 1; first + n <= c->S + 1; ++n)
-                longest = std::max(longest, build_work_list(first, n, c->heads, qtiles, T, 0).size());
+                longest = std::max(longest, build_work_list(first, n, c->heads, qtiles, T,
+                                                            c->live_mask == WF_MASK_ALL_LIVE, 0).size());
         L->work_len = (int)longest;
         L->work_stride = align_up(longest * 4, 256);
         L->work_off = off;
@@ -366,7 +369,8 @@ int wf_pool_create(const wf_config* cfg, void* pool_dev, size_t pool_bytes,
     const int cus_per_xcd = std::max(1, cus / wf::kXcds);
     for (int first = 0; first <= cfg->S && e == hipSuccess; ++first)
         for (int n = 1; first + n <= cfg->S + 1 && e == hipSuccess; ++n) {
-            std::vector<int32_t> wl = build_work_list(first, n, cfg->heads, qtiles, L.T, cus_per_xcd);
+            std::vector<int32_t> wl = build_work_list(first, n, cfg->heads, qtiles, L.T,
+                                                      cfg->live_mask == WF_MASK_ALL_LIVE, cus_per_xcd);
             if ((int)wl.size() > L.work_len) { e = hipErrorInvalidValue; break; }
             h->work_count[first * (cfg->S + 1) + n - 1] = (int)wl.size();
             e = hipMemcpy(h->pool + L.work_off + L.work_stride * (first * (cfg->S + 1) + n - 1),
@@ -455,8 +459,10 @@ int wf_attention_round(wf_handle* h, int32_t layer, int32_t slot_first, int32_t 
     if (fp8 && !q_scales) return WF_E_INVALID_ARG;
     if (((uintptr_t)q % 16) || ((uintptr_t)out % 16)) return WF_E_INVALID_ARG;
     // readiness check made just before attention: the union of the requested
-    // slots' legal contexts is the prefix [0, T - slot_first)
-    const uint64_t need = h->prefix_bits(L.T - slot_first);
+    // slots' legal contexts is the prefix [0, T - slot_first) (the whole
+    // context with the all-live mask)
+    const bool all_live = c.live_mask == WF_MASK_ALL_LIVE;
+    const uint64_t need = h->prefix_bits(all_live ? L.T : L.T - slot_first);
     if ((h->ready[layer] & need) != need) {
         snprintf(h->err, sizeof h->err, "layer %d: positions 0x%llx not published", layer,
                  (unsigned long long)(need & ~h->ready[layer]));
@@ -480,6 +486,7 @@ int wf_attention_round(wf_handle* h, int32_t layer, int32_t slot_first, int32_t 
     a.slot_first = slot_first; a.nslots = nslots;
     a.out_fp32 = out_dtype == WF_DTYPE_FP32;
     a.nblk = L.nblk;
+    a.all_live = all_live ? 1 : 0;
     a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)c.head_dim));
     const hipError_t e = wf::launch_attention(a, fp8, (hipStream_t)stream);
     if (e != hipSuccess) return h->fail_hip(e, "wf_attention_round launch");

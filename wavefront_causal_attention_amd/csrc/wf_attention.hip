@@ -7,7 +7,9 @@
 // M_WF(s, j) = 1[j >= s] with full attention inside each chunk (Wave Forcing,
 // hyper.ai summary, section "Method"; e-cogni.com.br, "Como funciona"). The
 // key loop simply stops at the prefix end, so masked slot pairs are skipped as
-// whole tiles and their pages are never read.
+// whole tiles and their pages are never read. With the all-live mask (the
+// bidirectional live K/V the pages contrast it with) every slot reads the
+// whole context.
 //
 // Per workgroup: 256 query rows of one (slot, head), 8 waves of 32 rows, one
 // workgroup per CU. Per 64-key tile, each wave computes
@@ -240,10 +242,11 @@ __global__ __launch_bounds__(NTH, NW == 4 ? 2 : 1) void attn_kernel(AttnArgs a) 
     const int head = work_head(unit);
     const int qt = work_qtile(unit);
     const int N = a.N, pt = a.pt, ppc = a.ppc;
-    const int nkeys = (a.T - s) * N;               // legal prefix of slot s
+    const int nctx = a.all_live ? a.T : a.T - s;   // context chunks slot s reads
+    const int nkeys = nctx * N;                    // legal prefix of slot s
     // bf16: tiles cover the flat prefix; fp8: tpc tiles per chunk
     const int tpc = FP8 ? (N + BN - 1) / BN : 1;
-    const int ntiles = FP8 ? (a.T - s) * tpc : (nkeys + BN - 1) / BN;
+    const int ntiles = FP8 ? nctx * tpc : (nkeys + BN - 1) / BN;
     const FastDiv tdiv = make_fastdiv((uint32_t)tpc);
 
     for (int i = tid; i < a.T * ppc; i += NTH) ptab[i] = a.table[i];
@@ -302,7 +305,7 @@ __global__ __launch_bounds__(NTH, NW == 4 ? 2 : 1) void attn_kernel(AttnArgs a) 
         if constexpr (FP8) {
             const int c = (int)fast_div((uint32_t)t, tdiv);
             const int o64 = (t - c * tpc) * BN + o;
-            ok = c < a.T - s && o64 < N;
+            ok = c < nctx && o64 < N;
             return c * N + o64;
         } else {
             const int g = t * BN + o;
@@ -431,7 +434,7 @@ __global__ __launch_bounds__(NTH, NW == 4 ? 2 : 1) void attn_kernel(AttnArgs a) 
     int bchunk = 0;
     float bcur = 0.f;
     auto chunk_bias = [&](int pos) -> float {
-        if (pos >= a.T - s) return 0.f;
+        if (pos >= nctx) return 0.f;
         const int g = ptab[pos * ppc] / ppc;
         const float* mu = a.kmean + ((int64_t)g * a.heads + head) * D + 32 * hf;
         float acc = 0.f;

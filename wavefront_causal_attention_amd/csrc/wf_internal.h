@@ -87,6 +87,7 @@ struct AttnArgs {
     int qtiles;               // query tiles per (slot, head)
     int out_fp32;
     int nblk;
+    int all_live;             // 1: every slot reads the whole context (no mask)
     float scale_log2;         // log2(e) / sqrt(D)
 };
 

@@ -42,6 +42,7 @@ class Workload:
     outlier_scale: float = 1.0
     fused_qkv: bool = False       # input is one [tokens, 3*h*d] projection output
     layer_rounds: int = 1         # consecutive rounds of one layer's pool
+    live_mask: str = "wavefront"  # "wavefront" (M_WF) or "all" (every live slot sees every live slot)
     description: str = ""
 
     @property
@@ -64,6 +65,8 @@ class Workload:
 
     def key_chunk_pairs(self) -> int:
         """Legal (query chunk, key chunk) pairs in one round (all slots)."""
+        if self.live_mask == "all":
+            return (self.S + 1) * self.T
         return (self.S + 1) * (self.A + self.H) + (self.S + 1) * (self.S + 2) // 2
 
     def attention_flops(self) -> float:
