@@ -307,3 +307,56 @@ def test_all_live_mask_round_parity(name):
     outw = rw.attention("fp32")
     assert torch.equal(outw[0], out[0])
     assert not torch.equal(outw[1:], out[1:])
+
+
+def test_two_layers_share_one_page_table():
+    """A pool of two layers with one page table: each layer's round equals the
+    oracle on its own data, across an advance (which needs the store of every
+    layer), and the layers' pages never mix."""
+    import dataclasses
+    from _gpu_round import config_of, stack_dev
+    import wavefront_causal_attention_amd as wf
+    base = W.WORKLOADS["ragged128"]
+    ws = [dataclasses.replace(base, seed=base.seed + 100 * l) for l in range(2)]
+    k0 = base.steady_round
+    pool = wf.Pool(config_of(base, first_round=k0, num_layers=2))
+    q = pool.q_buffer()
+    clean = [{}, {}]
+    for l, w in enumerate(ws):                                   # seed anchor + history per layer
+        sch = RoundSchedule(w.S, w.A, w.H, k0)
+        ks, vs = [], []
+        for slot in range(w.S + 1, w.T):
+            c = sch.chunk_at(w.T - 1 - slot)
+            _, kk, vv = W.stored_draw(w, c)
+            clean[l][c] = (kk, vv)
+            ks.append(kk)
+            vs.append(vv)
+        pool.publish(l, w.S + 1, w.T - w.S - 1, None, stack_dev(ks, w.in_dtype), stack_dev(vs, w.in_dtype), w.hd)
+    for rnd in range(2):
+        k = k0 + rnd
+        say("case two layers, round", k)
+        outs, lives = [], []
+        for l, w in enumerate(ws):
+            live = W.draw_slots(w, k, range(w.S + 1))
+            lives.append(live)
+            pool.publish(l, 0, w.S + 1, stack_dev([x[0] for x in live], w.in_dtype),
+                         stack_dev([x[1] for x in live], w.in_dtype), stack_dev([x[2] for x in live], w.in_dtype),
+                         w.hd, q_out=q)
+            out = pool.out_buffer("fp32")
+            out.fill_(float("nan"))
+            pool.attention(l, 0, w.S + 1, q, out)
+            torch.cuda.synchronize()
+            outs.append(out.cpu().numpy())
+        for l, w in enumerate(ws):
+            sch = RoundSchedule(w.S, w.A, w.H, k)
+            ref = oracle_round(w, k, lives[l], {c: clean[l][c] for c in sch.chunk_ids()[:w.A + w.H]},
+                               storage="bf16")
+            g = outs[l].reshape(w.S + 1, w.N, w.heads, w.head_dim)
+            mx, rel = err_stats(g, ref)
+            say("layer", l, "round", k, "max_abs %.3e rel_l2 %.3e" % (mx, rel))
+            assert mx <= BF16_MAX_ABS and rel <= BF16_REL_L2
+        assert not np.allclose(outs[0], outs[1])
+        for l, w in enumerate(ws):                               # the store becomes history
+            c = RoundSchedule(w.S, w.A, w.H, k).chunk_at(w.A + w.H)
+            clean[l][c] = tuple(lives[l][w.S][1:])
+        pool.advance()
