@@ -41,7 +41,8 @@ def slot_attention(q, k_ctx, v_ctx, scale, block=512, return_p=False):
     return out
 
 
-def round_attention(Qs, ctx_k, ctx_v, S, A, H, rows=None, slots=None, scale=None, kind="wavefront"):
+def round_attention(Qs, ctx_k, ctx_v, S, A, H, rows=None, slots=None, scale=None, kind="wavefront",
+                    legal=None):
     """Per-slot gather formulation.
 
     Qs:     [S+1, N, heads, d]     post-storage queries of live slots s = 0..S
@@ -49,6 +50,8 @@ def round_attention(Qs, ctx_k, ctx_v, S, A, H, rows=None, slots=None, scale=None
     ctx_v:  [T, N, heads, d]       values by context position
     rows:   optional query row indices (within a chunk) to evaluate
     slots:  optional subset of slots
+    legal:  optional mapping slot -> context positions it reads (default: the
+            live mask's legal positions)
     Returns O[S+1 (or len(slots)), len(rows) or N, heads, d] in fp64.
     """
     Qs = np.asarray(Qs)
@@ -59,7 +62,10 @@ def round_attention(Qs, ctx_k, ctx_v, S, A, H, rows=None, slots=None, scale=None
     heads = Qs.shape[2]
     out = np.zeros((len(slots), len(rows), heads, ctx_v.shape[-1]), dtype=np.float64)
     for si, s in enumerate(slots):
-        pos = legal_positions(s, S, A, H, kind)
+        pos = legal[s] if legal is not None else legal_positions(s, S, A, H, kind)
+        if not pos:                                    # a slot with no chunk this round
+            out[si] = np.nan
+            continue
         for h in range(heads):
             kc = np.concatenate([ctx_k[p][:, h, :] for p in pos], axis=0)
             vc = np.concatenate([ctx_v[p][:, h, :] for p in pos], axis=0)

@@ -58,15 +58,18 @@ def store(x: np.ndarray, storage: str, kind: str) -> np.ndarray:
     raise ValueError("unknown storage model " + storage)
 
 
-def rotated_context(shape, k, live, clean, storage="bf16"):
+def rotated_context(shape, k, live, clean, storage="bf16", sched=None):
     """Post-storage Q of live slots and K/V of every context position.
 
     live:  sequence over slots s = 0..S of pre-RoPE (q, k, v) [N, heads*d]
+           (None for a slot that holds no chunk in a fill or drain round)
     clean: mapping chunk_id -> pre-RoPE (k, v) for the anchor and history chunks
-    Returns (Qs [S+1, N, heads, d], ctx_k [T, ...], ctx_v [T, ...], chunk_ids).
+    sched: the round's RoundSchedule (default: a steady-state round k)
+    Returns (Qs [S+1, N, heads, d], ctx_k [T, ...], ctx_v [T, ...], chunk_ids);
+    positions and slots without a chunk are NaN.
     """
     S, A, H = shape.S, shape.A, shape.H
-    sched = RoundSchedule(S, A, H, k)
+    sched = RoundSchedule(S, A, H, k) if sched is None else sched
     T = sched.T
     N, h, d = shape.N, shape.heads, shape.head_dim
     ids = sched.chunk_ids()
@@ -75,6 +78,10 @@ def rotated_context(shape, k, live, clean, storage="bf16"):
     ctx_v = np.empty((T, N, h, d))
     for p in range(T):
         c = ids[p]
+        if not sched.present(p):
+            ctx_k[p] = np.nan
+            ctx_v[p] = np.nan
+            continue
         if p in pos_of_slot:
             _, kk, vv = live[pos_of_slot[p]]
         else:
@@ -84,15 +91,29 @@ def rotated_context(shape, k, live, clean, storage="bf16"):
         ctx_v[p] = vv if storage == "exact" else bf16_round(vv)     # V pages are bf16
     Qs = np.empty((S + 1, N, h, d))
     for s in range(S + 1):
+        if not sched.slot_present(s):
+            Qs[s] = np.nan
+            continue
         Qs[s] = store(rotate_chunk(shape, sched.slot_chunk(s), live[s][0]), storage, "q")
     return Qs, ctx_k, ctx_v, ids
 
 
-def oracle_round(shape, k, live, clean, storage="bf16", rows=None, slots=None, mask="wavefront"):
+def oracle_round(shape, k, live, clean, storage="bf16", rows=None, slots=None, mask="wavefront",
+                 fill=False, total_chunks=None):
     """O[slots, rows, heads, d] (fp64) of one wavefront round.
 
     See rotated_context for the inputs; rows/slots restrict what is evaluated;
-    mask selects the live-slot visibility (see schedule.live_mask).
+    mask selects the live-slot visibility (see schedule.live_mask); fill and
+    total_chunks admit the rounds that fill and drain the pipeline, where each
+    slot reads only the positions that hold a chunk (slots without one are NaN).
     """
-    Qs, ctx_k, ctx_v, _ = rotated_context(shape, k, live, clean, storage)
-    return round_attention(Qs, ctx_k, ctx_v, shape.S, shape.A, shape.H, rows=rows, slots=slots, kind=mask)
+    sched = RoundSchedule(shape.S, shape.A, shape.H, k, fill=fill, total_chunks=total_chunks)
+    Qs, ctx_k, ctx_v, _ = rotated_context(shape, k, live, clean, storage, sched=sched)
+    legal = {s: sched.legal_present(s, mask) for s in range(shape.S + 1)}
+    out = round_attention(Qs, ctx_k, ctx_v, shape.S, shape.A, shape.H, rows=rows, slots=slots, kind=mask,
+                          legal=legal)
+    slots = list(range(shape.S + 1)) if slots is None else list(slots)
+    for i, s in enumerate(slots):
+        if not sched.slot_present(s):
+            out[i] = np.nan
+    return out

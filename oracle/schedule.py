@@ -58,16 +58,28 @@ def legal_positions(s: int, S: int, A: int, H: int, kind: str = "wavefront") -> 
 
 
 class RoundSchedule:
-    """Chunk ids of every context position in round k (steady state only).
+    """Chunk ids of every context position in round k.
 
-    Fill and drain rounds, where some positions hold no chunk yet, are not
-    modelled: the schedule raises for k below the first full round.
+    By default only steady-state rounds are modelled (the schedule raises for k
+    below the first full round). With fill=True the schedule also covers the
+    rounds that fill the pipeline, and with total_chunks = C the rounds that
+    drain it after the last chunk (rounds run from 0 to C-1+S). In those rounds
+    some positions hold no chunk (present() is False) and are left out of every
+    legal context. The pages mention the fill and its latency (thelatestinai.com
+    listing, Figure 1 caption) without detail; the reading here: chunk i enters
+    slot 0 in round i and moves one stage per round (k = i + s), is stored in
+    round i + S, and from then on is clean: anchor chunk a (a < A) sits at
+    anchor position a, every later chunk enters the history ring, which keeps
+    the H most recently stored non-anchor chunks.
     """
 
-    def __init__(self, S: int, A: int, H: int, k: int):
-        if k < S + H + A:
+    def __init__(self, S: int, A: int, H: int, k: int, fill: bool = False, total_chunks=None):
+        if k < 0 or (not fill and k < S + H + A):
             raise ValueError("round %d is a fill round; first full round is %d" % (k, S + H + A))
+        if total_chunks is not None and k > total_chunks - 1 + S:
+            raise ValueError("round %d is past the last round %d" % (k, total_chunks - 1 + S))
         self.S, self.A, self.H, self.k = S, A, H, k
+        self.C = total_chunks
         self.T = A + H + S + 1
 
     def chunk_at(self, p: int) -> int:
@@ -81,8 +93,29 @@ class RoundSchedule:
         s = S - 1 - (p - A - H - 1)
         return k - s                                   # live slot s holds chunk i = k - s
 
+    def present(self, p: int) -> bool:
+        """Whether position p holds a chunk in this round."""
+        c = self.chunk_at(p)
+        last = self.C - 1 if self.C is not None else None
+        if p < self.A:
+            return self.k >= c + self.S + 1 and (last is None or c <= last)   # stored already
+        if p < self.A + self.H:
+            return c >= self.A and (last is None or c <= last)               # non-anchor, stored
+        return c >= 0 and (last is None or c <= last)                       # live: store and slots
+
     def chunk_ids(self) -> list:
         return [self.chunk_at(p) for p in range(self.T)]
+
+    def present_chunk_ids(self) -> list:
+        """Chunk id per position, None where the position is empty."""
+        return [self.chunk_at(p) if self.present(p) else None for p in range(self.T)]
+
+    def slot_present(self, s: int) -> bool:
+        return self.present(slot_position(s, self.S, self.A, self.H))
+
+    def legal_present(self, s: int, kind: str = "wavefront") -> list:
+        """Positions query slot s reads in this round: its legal ones that hold a chunk."""
+        return [p for p in legal_positions(s, self.S, self.A, self.H, kind) if self.present(p)]
 
     def slot_chunk(self, s: int) -> int:
         return self.chunk_at(slot_position(s, self.S, self.A, self.H))

@@ -206,3 +206,28 @@ def test_noisiest_slot_reads_the_same_under_both_masks():
     al = round_attention(Qs, ck, cv, S, A, H, kind="all")
     assert np.array_equal(wf_[0], al[0])
     assert all(np.max(np.abs(wf_[s] - al[s])) > 1e-3 for s in range(1, S + 1))
+
+
+@pytest.mark.parametrize("S,A,H,C", [(2, 1, 2, 5), (3, 2, 1, 6)])
+def test_fill_and_drain_rounds_read_exactly_the_present_chunks(S, A, H, C):
+    # Q = 0 gives uniform weights, V = chunk id: each present slot's output is
+    # the exact mean of the ids of the chunks it reads, which a brute-force
+    # pipeline fixes (stage k - i for chunk i, clean after its store round)
+    import dataclasses
+    w = dataclasses.replace(W.WORKLOADS["tiny"], S=S, A=A, H=H, heads=1)
+    N, hd = w.N, w.hd
+    for k in range(C + S):
+        sch = RoundSchedule(S, A, H, k, fill=True, total_chunks=C)
+        live = [None if not sch.slot_present(s) else
+                (np.zeros((N, hd)), np.zeros((N, hd)), np.full((N, hd), float(k - s))) for s in range(S + 1)]
+        stored = [i for i in range(C) if i + S + 1 <= k]
+        clean = {i: (np.zeros((N, hd)), np.full((N, hd), float(i))) for i in stored}
+        out = oracle_round(w, k, live, clean, storage="exact", fill=True, total_chunks=C)
+        hist = [i for i in stored if i >= A][-H:] if H else []
+        anchors = [i for i in stored if i < A]
+        for s in range(S + 1):
+            if not sch.slot_present(s):
+                assert np.isnan(out[s]).all()
+                continue
+            reads = anchors + hist + [k - j for j in range(s, S + 1) if 0 <= k - j <= C - 1]
+            assert np.max(np.abs(out[s] - np.mean(reads))) <= 1e-12, (k, s)

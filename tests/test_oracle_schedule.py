@@ -120,3 +120,63 @@ def test_all_live_mask_is_all_ones_and_every_slot_reads_everything():
             assert legal_positions(s, S, A, H, "all") == list(range(T))
     with pytest.raises(ValueError):
         live_mask(2, "rolling")
+
+
+# --- fill and drain rounds ---------------------------------------------------
+
+def _pipeline(S, A, H, C, k):
+    """Brute force: follow every chunk through the pipeline to round k.
+    Chunk i is at stage k - i while 0 <= k - i <= S (stage S is the store) and
+    is clean from round i + S + 1 on: an anchor if i < A, else it joins the
+    history, which keeps the H most recently stored non-anchor chunks."""
+    stage = {i: k - i for i in range(C) if 0 <= k - i <= S}
+    stored = [i for i in range(C) if i + S + 1 <= k]
+    anchors = sorted(i for i in stored if i < A)
+    hist = [i for i in stored if i >= A][-H:] if H else []
+    return stage, anchors, hist
+
+
+@pytest.mark.parametrize("S,A,H,C", [(2, 1, 2, 6), (4, 1, 2, 9), (3, 2, 1, 7), (1, 1, 0, 4), (4, 2, 3, 3)])
+def test_fill_and_drain_presence_matches_the_pipeline(S, A, H, C):
+    T = A + H + S + 1
+    for k in range(C + S):                                   # every round of a C-chunk video
+        sch = RoundSchedule(S, A, H, k, fill=True, total_chunks=C)
+        stage, anchors, hist = _pipeline(S, A, H, C, k)
+        ids = sch.present_chunk_ids()
+        live = {s: c for c, s in stage.items()}
+        for s in range(S + 1):
+            p = slot_position(s, S, A, H)
+            assert (ids[p] is not None) == (s in live)
+            if s in live:
+                assert ids[p] == live[s]
+        assert [ids[a] for a in range(A) if ids[a] is not None] == anchors
+        assert sorted(c for c in ids[A:A + H] if c is not None) == hist
+        for s in range(S + 1):                               # what each present slot reads
+            if s not in live:
+                continue
+            got = sorted(ids[p] for p in sch.legal_present(s))
+            want = sorted(anchors + hist + [c for c, st in stage.items() if st >= s])
+            assert got == want, (k, s)
+    with pytest.raises(ValueError):
+        RoundSchedule(S, A, H, C + S, fill=True, total_chunks=C)
+
+
+def test_steady_rounds_have_every_position():
+    S, A, H = 4, 1, 2
+    for k in range(S + H + A, S + H + A + 10):
+        sch = RoundSchedule(S, A, H, k, fill=True)
+        assert all(sch.present(p) for p in range(sch.T))
+        assert sch.present_chunk_ids() == sch.chunk_ids()
+
+
+def test_fig1_first_output_after_fill():
+    # Figure 1 caption (S=4): the first chunk is emitted after the pipeline
+    # fills, then one chunk per round
+    g = json.load(open(os.path.join(GOLD, "fig1_wavefront_s4.json")))
+    S, A, H = g["S"], 1, 2
+    stored = []
+    for k in range(S + g["rounds_observed"]):
+        sch = RoundSchedule(S, A, H, k, fill=True)
+        stored.append(sch.present_chunk_ids()[A + H])
+    assert stored[:S] == [None] * S
+    assert stored[S:] == list(range(g["chunks_emitted"]))
