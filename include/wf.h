@@ -70,14 +70,28 @@ typedef struct wf_config {
     int32_t qk_dtype;        /* published Q/K: WF_DTYPE_BF16 | WF_DTYPE_FP8_E4M3
                                 (fp8: T * ceil(chunk tokens / 64) <= 4096)         */
     int32_t rope_split[3];   /* (d_t, d_h, d_w), even, summing to head_dim          */
-    int32_t first_round;     /* round index k of the pool's first round, >= S+H+A   */
+    int32_t first_round;     /* round index k of the pool's first round, >= 0; rounds
+                                below S+H+A fill the pipeline (see live positions) */
     double  rope_theta;      /* RoPE base, e.g. 10000                               */
     int32_t live_mask;       /* WF_MASK_WAVEFRONT (default) | WF_MASK_ALL_LIVE: the
                                 bidirectional live K/V of Rolling Forcing that the
                                 pages contrast the wavefront mask with
                                 (thelatestinai.com listing, Table 9); no tile is
                                 skipped, for measuring what the mask saves         */
+    int32_t total_chunks;    /* chunks in the video, 0 = unbounded stream; with C > 0
+                                rounds run to C-1+S and the last S drain the pipeline */
 } wf_config;
+
+/*
+ * Live positions. Chunk i enters slot 0 in round i and moves one stage per
+ * round (k = i + s), is stored in round i+S and is clean afterwards: anchor
+ * chunk a at anchor position a, later chunks in the history ring (the H most
+ * recently stored). In the rounds that fill (k < S+H+A) and drain (k > C-1)
+ * the pipeline some positions hold no chunk: they are not published, not
+ * read and report chunk id -1 (thelatestinai.com listing, Figure 1 caption,
+ * mentions the fill and its latency). A store that holds an anchor chunk is
+ * published straight into that anchor's pages.
+ */
 
 typedef struct wf_handle wf_handle;
 
@@ -132,7 +146,8 @@ void wf_pool_destroy(wf_handle* h);
  * The K pages of the slot's context position receive RoPE'd K (bf16, or fp8
  * with per-64-token-block scales after subtracting the chunk's per-channel
  * mean); the V pages receive V in bf16. Marks the slots published for this
- * layer and round.
+ * layer and round. WF_E_INVALID_ARG if a slot in the range holds no chunk in
+ * this round (fill and drain rounds).
  */
 int wf_kv_publish(wf_handle* h, int32_t layer, int32_t slot_first, int32_t nslots,
                   const void* q, const void* k, const void* v, int64_t row_stride_elems,
@@ -152,7 +167,9 @@ int wf_kv_publish(wf_handle* h, int32_t layer, int32_t slot_first, int32_t nslot
  *           slots are written.
  * Returns WF_E_NOT_READY, launching nothing, unless every context position the
  * slots read is published for this layer in this round (the readiness check
- * made just before attention).
+ * made just before attention); WF_E_INVALID_ARG if a requested slot holds no
+ * chunk in this round. In fill and drain rounds each slot reads only the
+ * positions that hold a chunk.
  */
 int wf_attention_round(wf_handle* h, int32_t layer, int32_t slot_first, int32_t nslots,
                        const void* q, const float* q_scales, void* out, int32_t out_dtype,
@@ -164,14 +181,16 @@ int wf_attention_round(wf_handle* h, int32_t layer, int32_t slot_first, int32_t 
  * the oldest history's pages are handed to slot 0 (re-published next round),
  * and the anchor stays. After r advances, non-anchor position p maps to page
  * group A + ((p - A + r) mod (H+S+1)); group g owns pages g*ppc .. g*ppc+ppc-1.
- * Requires the store published in every layer (WF_E_NOT_READY otherwise).
- * Live slots become unpublished; history keeps its readiness.
+ * Requires the store published in every layer (WF_E_NOT_READY otherwise)
+ * when the store holds a chunk; WF_E_INVALID_ARG past the last round of a
+ * C-chunk video. Live slots become unpublished; history keeps its readiness; a
+ * stored anchor chunk stays published at its anchor position.
  */
 int wf_round_advance(wf_handle* h, void* stream);
 
 /* Host queries (no device access). */
 int wf_round_index(const wf_handle* h, int64_t* k);
-int wf_schedule_chunk_ids(const wf_handle* h, int64_t* ids /* [T] */);
+int wf_schedule_chunk_ids(const wf_handle* h, int64_t* ids /* [T], -1 = no chunk */);
 int wf_page_table_host(const wf_handle* h, int32_t* table /* [T * pages_per_chunk] */);
 int wf_ready_mask(const wf_handle* h, int32_t layer, uint64_t* mask /* bit p = position p */);
 /* Pool geometry, out[12]: N, T, pages_per_chunk, K region offset, V region

@@ -10,12 +10,13 @@ import wavefront_causal_attention_amd as wf
 from oracle import RoundSchedule, oracle_round
 
 
-def config_of(w: W.Workload, first_round=None, num_layers=1):
+def config_of(w: W.Workload, first_round=None, num_layers=1, total_chunks=0):
     return wf.make_config(S=w.S, anchor_chunks=w.A, history_chunks=w.H, heads=w.heads,
                           head_dim=w.head_dim, chunk_frames=w.chunk_frames, frame_h=w.frame_h,
                           frame_w=w.frame_w, page_tokens=w.page_tokens, in_dtype=w.in_dtype,
                           qk_dtype=w.qk_dtype, rope_split=w.rope_split, rope_theta=w.rope_theta,
-                          first_round=first_round, num_layers=num_layers, live_mask=w.live_mask)
+                          first_round=first_round, num_layers=num_layers, live_mask=w.live_mask,
+                          total_chunks=total_chunks)
 
 
 def to_dev(x: np.ndarray, in_dtype: str):
@@ -100,6 +101,43 @@ class RoundRunner:
     def clean_for_round(self):
         sch = RoundSchedule(self.w.S, self.w.A, self.w.H, self.k)
         return {c: self.clean[c] for c in sch.chunk_ids()[:self.w.A + self.w.H]}
+
+
+def run_whole_video(w, C, check_round):
+    """Drive one pool through every round of a C-chunk video, from the first
+    fill round to the last drain round, publishing and attending only the
+    slots that hold a chunk; check_round(k, out, live, clean, lo, hi) checks
+    each round. Anchor and history are never seeded: they are what the store
+    slot published in earlier rounds."""
+    pool = wf.Pool(config_of(w, first_round=0, total_chunks=C))
+    q, qs = pool.q_buffer(), pool.q_scale_buffer()
+    clean = {}
+    for k in range(C + w.S):
+        sch = RoundSchedule(w.S, w.A, w.H, k, fill=True, total_chunks=C)
+        assert pool.chunk_ids() == [-1 if x is None else x for x in sch.present_chunk_ids()]
+        present = [s for s in range(w.S + 1) if sch.slot_present(s)]
+        lo, hi = present[0], present[-1]
+        assert present == list(range(lo, hi + 1))
+        live = [W.draw(w, k, s) if s in present else None for s in range(w.S + 1)]
+        sel = live[lo:hi + 1]
+        if w.fused_qkv:
+            fd = stack_dev([np.concatenate(x, axis=1) for x in sel], w.in_dtype)
+            pool.publish(0, lo, hi - lo + 1, fd[:, :w.hd], fd[:, w.hd:2 * w.hd], fd[:, 2 * w.hd:], 3 * w.hd,
+                         q_out=q, q_scales=qs)
+        else:
+            pool.publish(0, lo, hi - lo + 1, stack_dev([x[0] for x in sel], w.in_dtype),
+                         stack_dev([x[1] for x in sel], w.in_dtype), stack_dev([x[2] for x in sel], w.in_dtype),
+                         w.hd, q_out=q, q_scales=qs)
+        out = pool.out_buffer("fp32")
+        out.fill_(float("nan"))
+        pool.attention(0, lo, hi - lo + 1, q, out, q_scales=qs)
+        torch.cuda.synchronize()
+        check_round(k, out, live, {c: clean[c] for c in sch.present_chunk_ids()[:w.A + w.H] if c is not None},
+                    lo, hi)
+        if w.S in present:                       # the store's chunk becomes anchor or history
+            clean[sch.slot_chunk(w.S)] = tuple(live[w.S][1:])
+        if k < C - 1 + w.S:
+            pool.advance()
 
 
 def head_subset(w: W.Workload, heads):

@@ -66,10 +66,12 @@ def test_wan13b_pool_size_matches_pages(lib):
     ("head_dim", 96, wf.WF_E_SHAPE), ("heads", 0, wf.WF_E_SHAPE), ("num_layers", 0, wf.WF_E_SHAPE),
     ("page_tokens", 100, wf.WF_E_SHAPE), ("page_tokens", 4, wf.WF_E_SHAPE),
     ("in_dtype", 7, wf.WF_E_INVALID_ARG), ("qk_dtype", 1, wf.WF_E_INVALID_ARG),
-    ("first_round", 6, wf.WF_E_SHAPE), ("rope_theta", 0.0, wf.WF_E_INVALID_ARG),
+    ("first_round", -1, wf.WF_E_SHAPE), ("total_chunks", -1, wf.WF_E_SHAPE),
+    ("rope_theta", 0.0, wf.WF_E_INVALID_ARG),
     ("S", 70, wf.WF_E_SHAPE), ("live_mask", 2, wf.WF_E_INVALID_ARG),
 ])
 def test_config_validation(lib, field, value, status):
+    # wan1.3b_s4 bench config: first_round 7 (first full round), unbounded video
     c = cfg_of(W.WORKLOADS["wan1.3b_s4"])
     setattr(c, field, value)
     with pytest.raises(wf.WfError) as e:
@@ -270,5 +272,69 @@ def test_all_live_attention_needs_the_whole_context(lib):
         wf.wf_kv_publish(h, 0, S + 1, T - S - 1, None, FAKE, FAKE, w.hd, None, None, None, None)
         wf.wf_kv_publish(h, 0, S, 1, FAKE, FAKE, FAKE, w.hd, None, FAKE, FAKE, None)
         wf.wf_attention_round(h, 0, S, 1, FAKE, FAKE, FAKE, wf.WF_DTYPE_BF16, None)
+    finally:
+        wf.wf_pool_destroy(h)
+
+
+def test_first_round_past_the_video_is_rejected(lib):
+    c = cfg_of(W.WORKLOADS["wan1.3b_s4"], first_round=10)
+    c.total_chunks = 7                         # last round 7 - 1 + S = 10
+    wf.wf_pool_bytes(c)
+    c.first_round = 11
+    with pytest.raises(wf.WfError) as e:
+        wf.wf_pool_bytes(c)
+    assert e.value.status == wf.WF_E_SHAPE
+
+
+@pytest.mark.parametrize("S,A,H,C", [(2, 1, 2, 6), (4, 1, 2, 9), (3, 2, 1, 7), (2, 2, 0, 5)])
+def test_fill_and_drain_whole_video(lib, S, A, H, C):
+    """Host state over every round of a C-chunk video: chunk ids follow the
+    oracle's occupancy, occupied positions never share pages, a stored chunk
+    is read later from the pages it was written to (anchors included), empty
+    slots refuse publish and attention, and the video ends after C-1+S."""
+    import dataclasses
+    w = dataclasses.replace(W.WORKLOADS["tiny"], S=S, A=A, H=H)
+    c = cfg_of(w, first_round=0)
+    c.total_chunks = C
+    h = wf.wf_pool_create_host_model(c)
+    T, ppc = w.T, w.N // w.page_tokens
+    written = {}                                   # chunk -> page group its store wrote
+    try:
+        for k in range(C + S):
+            assert wf.wf_round_index(h) == k
+            sch = RoundSchedule(S, A, H, k, fill=True, total_chunks=C)
+            ids = [-1 if x is None else x for x in sch.present_chunk_ids()]
+            assert wf.wf_schedule_chunk_ids(h, T) == ids
+            table = wf.wf_page_table_host(h, T * ppc)
+            group = [table[p * ppc] // ppc for p in range(T)]
+            occupied = [p for p in range(T) if ids[p] >= 0]
+            assert len({group[p] for p in occupied}) == len(occupied)
+            for p in range(A + H):                 # clean chunks sit where their store wrote them
+                if ids[p] >= 0:
+                    assert group[p] == written[ids[p]], (k, p)
+            present = [s for s in range(S + 1) if sch.slot_present(s)]
+            for s in range(S + 1):
+                if s not in present:
+                    with pytest.raises(wf.WfError) as e:
+                        wf.wf_kv_publish(h, 0, s, 1, FAKE, FAKE, FAKE, w.hd, None, FAKE, FAKE, None)
+                    assert e.value.status == wf.WF_E_INVALID_ARG
+            lo, hi = present[0], present[-1]
+            wf.wf_kv_publish(h, 0, lo, hi - lo + 1, FAKE, FAKE, FAKE, w.hd, None, FAKE, FAKE, None)
+            wf.wf_attention_round(h, 0, lo, hi - lo + 1, FAKE, FAKE, FAKE, wf.WF_DTYPE_BF16, None)
+            if lo > 0:
+                with pytest.raises(wf.WfError) as e:
+                    wf.wf_attention_round(h, 0, 0, lo + 1, FAKE, FAKE, FAKE, wf.WF_DTYPE_BF16, None)
+                assert e.value.status == wf.WF_E_INVALID_ARG
+            if S in present:
+                written[ids[A + H]] = group[A + H]
+            if k < C - 1 + S:
+                wf.wf_round_advance(h, None)
+                mask = wf.wf_ready_mask(h, 0)
+                nxt = RoundSchedule(S, A, H, k + 1, fill=True, total_chunks=C).present_chunk_ids()
+                for p in range(A + H):             # clean positions with a chunk stay published
+                    assert bool(mask >> p & 1) == (nxt[p] is not None), (k, p)
+        with pytest.raises(wf.WfError) as e:
+            wf.wf_round_advance(h, None)
+        assert e.value.status == wf.WF_E_INVALID_ARG
     finally:
         wf.wf_pool_destroy(h)

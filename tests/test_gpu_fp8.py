@@ -169,3 +169,24 @@ def test_fp8_all_live_mask_round_parity():
     mx, rel = err_stats(g, ref)
     say("fp8 all-live vs storage=fp8: max_abs %.3e rel_l2 %.3e" % (mx, rel))
     assert mx <= FP8_MAX_ABS and rel <= FP8_REL_L2
+
+
+@pytest.mark.parametrize("name,C", [("ragged_fp8_64", 5), ("tiny_fp8", 5)])
+def test_fp8_fill_and_drain_whole_video(name, C):
+    """Every round of a short video on the fp8 QK path: per-tile key scales
+    and chunk means follow each chunk to whichever position it occupies while
+    the pipeline fills and drains."""
+    from _gpu_round import run_whole_video
+    w = W.WORKLOADS[name]
+    say("case", name, "fp8 whole video of", C, "chunks")
+
+    def check(k, out, live, clean, lo, hi):
+        ref = oracle_round(w, k, live, clean, storage="fp8", fill=True, total_chunks=C,
+                           slots=range(lo, hi + 1))
+        o = out.cpu().numpy().reshape(w.S + 1, w.N, w.heads, w.head_dim).astype(np.float64)
+        assert np.isnan(np.delete(o, list(range(lo, hi + 1)), axis=0)).all()
+        mx, rel = err_stats(o[lo:hi + 1], ref)
+        say(name, "round", k, "slots", lo, "..", hi, "max_abs %.3e rel_l2 %.3e" % (mx, rel))
+        assert mx <= FP8_MAX_ABS and rel <= FP8_REL_L2, (k, mx, rel)
+
+    run_whole_video(w, C, check)

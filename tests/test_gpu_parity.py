@@ -14,7 +14,7 @@ import torch
 import wf_inputs as W
 from oracle import GroupRing, RoundSchedule, bf16_round, oracle_round, rotate_chunk
 
-from _gpu_round import RoundRunner, err_stats, gpu_rows, oracle_rows
+from _gpu_round import RoundRunner, err_stats, gpu_rows, oracle_rows, run_whole_video
 
 pytestmark = pytest.mark.gpu
 
@@ -359,4 +359,65 @@ def test_two_layers_share_one_page_table():
         for l, w in enumerate(ws):                               # the store becomes history
             c = RoundSchedule(w.S, w.A, w.H, k).chunk_at(w.A + w.H)
             clean[l][c] = tuple(lives[l][w.S][1:])
+        pool.advance()
+
+
+@pytest.mark.parametrize("name,C", [("tiny", 6), ("edge_s1_h0", 5), ("ragged128", 7)])
+def test_fill_and_drain_whole_video(name, C):
+    """Every round of a short video, the pipeline filling and draining: each
+    slot that holds a chunk matches the oracle over the positions that hold
+    one; slots without a chunk are left untouched."""
+    w = W.WORKLOADS[name]
+    say("case", name, "whole video of", C, "chunks")
+
+    def check(k, out, live, clean, lo, hi):
+        ref = oracle_round(w, k, live, clean, storage="bf16", fill=True, total_chunks=C,
+                           slots=range(lo, hi + 1))
+        o = out.cpu().numpy().reshape(w.S + 1, w.N, w.heads, w.head_dim).astype(np.float64)
+        untouched = np.delete(o, list(range(lo, hi + 1)), axis=0)
+        assert np.isnan(untouched).all()
+        g = o[lo:hi + 1]
+        assert not np.isnan(g).any()
+        mx, rel = err_stats(g, ref)
+        say(name, "round", k, "slots", lo, "..", hi, "max_abs %.3e rel_l2 %.3e" % (mx, rel))
+        assert mx <= BF16_MAX_ABS and rel <= BF16_REL_L2, (k, mx, rel)
+
+    run_whole_video(w, C, check)
+
+
+def test_fill_rounds_of_an_open_ended_video_reach_the_steady_state():
+    """With no video length the pool starts in the first fill round and, once
+    the ring is full, runs the same rounds as a pool created steady."""
+    w = W.WORKLOADS["tiny"]
+    say("case tiny, open-ended video from round 0")
+    from _gpu_round import config_of, stack_dev
+    import wavefront_causal_attention_amd as wf
+    pool = wf.Pool(config_of(w, first_round=0))
+    q = pool.q_buffer()
+    clean = {}
+    for k in range(w.steady_round + 2):
+        sch = RoundSchedule(w.S, w.A, w.H, k, fill=True)
+        present = [s for s in range(w.S + 1) if sch.slot_present(s)]
+        lo, hi = present[0], present[-1]
+        live = [W.draw(w, k, s) if s in present else None for s in range(w.S + 1)]
+        sel = live[lo:hi + 1]
+        pool.publish(0, lo, hi - lo + 1, stack_dev([x[0] for x in sel], w.in_dtype),
+                     stack_dev([x[1] for x in sel], w.in_dtype), stack_dev([x[2] for x in sel], w.in_dtype),
+                     w.hd, q_out=q)
+        out = pool.out_buffer("fp32")
+        out.fill_(float("nan"))
+        pool.attention(0, lo, hi - lo + 1, q, out)
+        torch.cuda.synchronize()
+        cl = {c: clean[c] for c in sch.present_chunk_ids()[:w.A + w.H] if c is not None}
+        ref = oracle_round(w, k, live, cl, storage="bf16", fill=True, slots=range(lo, hi + 1))
+        g = out.cpu().numpy().reshape(w.S + 1, w.N, w.heads, w.head_dim)[lo:hi + 1].astype(np.float64)
+        mx, rel = err_stats(g, ref)
+        say("round", k, "max_abs %.3e rel_l2 %.3e" % (mx, rel))
+        assert mx <= BF16_MAX_ABS and rel <= BF16_REL_L2, (k, mx, rel)
+        if k >= w.steady_round:
+            assert (lo, hi) == (0, w.S)
+            steady = oracle_round(w, k, live, cl, storage="bf16")
+            assert np.allclose(steady, ref, equal_nan=False)
+        if w.S in present:
+            clean[sch.slot_chunk(w.S)] = tuple(live[w.S][1:])
         pool.advance()

@@ -19,9 +19,11 @@ _DT = {"bf16": WF_DTYPE_BF16, "fp32": WF_DTYPE_FP32, "fp8": WF_DTYPE_FP8_E4M3}
 
 def make_config(S, anchor_chunks, history_chunks, heads, head_dim, chunk_frames, frame_h, frame_w,
                 page_tokens, in_dtype="bf16", qk_dtype="bf16", rope_split=None, rope_theta=1e4,
-                first_round=None, num_layers=1, live_mask="wavefront") -> wf_config:
+                first_round=None, num_layers=1, live_mask="wavefront", total_chunks=0) -> wf_config:
     """live_mask: "wavefront" (M_WF, the default) or "all" (every live slot sees
-    every live slot; no tile is skipped)."""
+    every live slot; no tile is skipped). first_round below S+H+A starts in the
+    rounds that fill the pipeline; total_chunks > 0 ends the video (its last S
+    rounds drain the pipeline)."""
     c = wf_config()
     c.S, c.anchor_chunks, c.history_chunks = S, anchor_chunks, history_chunks
     c.heads, c.head_dim, c.num_layers = heads, head_dim, num_layers
@@ -34,6 +36,7 @@ def make_config(S, anchor_chunks, history_chunks, heads, head_dim, chunk_frames,
     c.rope_theta = float(rope_theta)
     c.first_round = S + history_chunks + anchor_chunks if first_round is None else first_round
     c.live_mask = {"wavefront": WF_MASK_WAVEFRONT, "all": WF_MASK_ALL_LIVE}[live_mask]
+    c.total_chunks = int(total_chunks)
     return c
 
 

@@ -45,6 +45,7 @@ class wf_config(ctypes.Structure):
         ("first_round", ctypes.c_int32),
         ("rope_theta", ctypes.c_double),
         ("live_mask", ctypes.c_int32),
+        ("total_chunks", ctypes.c_int32),
     ]
 
 

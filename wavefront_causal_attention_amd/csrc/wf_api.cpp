@@ -189,7 +189,8 @@ int validate(const wf_config* c, Layout* L) {
     if (dt < 0 || dh < 0 || dw < 0 || (dt | dh | dw) & 1 || dt + dh + dw != c->head_dim) return WF_E_SHAPE;
     if (dt > 64) return WF_E_SHAPE;
     if (!(c->rope_theta > 0.0) || !std::isfinite(c->rope_theta)) return WF_E_INVALID_ARG;
-    if (c->first_round < c->S + c->history_chunks + c->anchor_chunks) return WF_E_SHAPE;
+    if (c->first_round < 0 || c->total_chunks < 0) return WF_E_SHAPE;
+    if (c->total_chunks > 0 && (int64_t)c->first_round > (int64_t)c->total_chunks - 1 + c->S) return WF_E_SHAPE;
     if ((int64_t)c->first_round + 1000000000LL > INT32_MAX / std::max(1, c->chunk_frames)) {
         // keep chunk_frames * chunk id representable for a very long stream
         if ((int64_t)c->chunk_frames * (c->first_round + 1) > INT32_MAX / 2) return WF_E_SHAPE;
@@ -261,18 +262,40 @@ struct wf_handle {
     int64_t round() const { return cfg.first_round + ring; }
     int position_of_slot(int s) const { return L.T - 1 - s; }
 
-    // Chunk id at context position p in the current round (k = i + s).
-    int64_t chunk_at(int p) const {
-        const int64_t k = round();
+    // Chunk id at context position p in round k (k = i + s).
+    int64_t chunk_at_round(int p, int64_t k) const {
         if (p < A()) return p;
         if (p < A() + H()) return k - S() - H() + (p - A());
         const int s = L.T - 1 - p;       // live slot index, store = S
         return k - s;
     }
+    int64_t chunk_at(int p) const { return chunk_at_round(p, round()); }
+    // Whether position p holds a chunk in round k: chunk i is stored in round
+    // i + S and clean afterwards (anchor chunks at the anchor, later ones in
+    // the history ring); C = total_chunks bounds the video when positive.
+    bool present_at_round(int p, int64_t k) const {
+        const int64_t c = chunk_at_round(p, k);
+        const bool in_video = cfg.total_chunks <= 0 || c <= (int64_t)cfg.total_chunks - 1;
+        if (p < A()) return k >= c + S() + 1 && in_video;
+        if (p < A() + H()) return c >= A() && in_video;
+        return c >= 0 && in_video;
+    }
+    bool present(int p) const { return present_at_round(p, round()); }
+    // Anchor chunk held by the store in round k, or -1: it is published
+    // straight into that anchor's pages.
+    int store_anchor_at_round(int64_t k) const {
+        const int64_t c = k - S();
+        return present_at_round(A() + H(), k) && c < A() ? (int)c : -1;
+    }
     // Page group of context position p: the anchor is fixed; the ring of
-    // H+S+1 groups rotates by one per advance.
+    // H+S+1 groups rotates by one per advance; a store holding an anchor
+    // chunk writes that anchor's group.
     int group_at(int p) const {
         if (p < A()) return p;
+        if (p == A() + H()) {
+            const int a = store_anchor_at_round(round());
+            if (a >= 0) return a;
+        }
         return A() + (int)(((int64_t)(p - A()) + ring) % L.R);
     }
     uint64_t prefix_bits(int n) const { return n >= 64 ? ~0ull : ((1ull << n) - 1); }
@@ -377,7 +400,9 @@ int wf_pool_create(const wf_config* cfg, void* pool_dev, size_t pool_bytes,
                           wl.data(), wl.size() * 4, hipMemcpyHostToDevice);
         }
     if (e == hipSuccess)
-        e = wf::launch_page_table(h->table, L.T, cfg->anchor_chunks, L.ppc, h->ring, nullptr);
+        e = wf::launch_page_table(h->table, L.T, cfg->anchor_chunks, L.ppc, h->ring,
+                                  cfg->anchor_chunks + cfg->history_chunks,
+                                  h->store_anchor_at_round(h->round()), nullptr);
     if (e == hipSuccess) e = hipDeviceSynchronize();
     if (e != hipSuccess) {
         delete h;
@@ -409,6 +434,12 @@ int wf_kv_publish(wf_handle* h, int32_t layer, int32_t slot_first, int32_t nslot
         return WF_E_INVALID_ARG;      // 8-element vector loads
     if (q_out && ((uintptr_t)q_out % 16)) return WF_E_INVALID_ARG;
 
+    for (int i = 0; i < nslots; ++i)
+        if (!h->present(h->position_of_slot(slot_first + i))) {
+            snprintf(h->err, sizeof h->err, "slot %d holds no chunk in round %lld", slot_first + i,
+                     (long long)h->round());
+            return WF_E_INVALID_ARG;
+        }
     wf::PublishArgs a{};
     for (int i = 0; i < nslots; ++i) {
         const int64_t t0 = chunk_t0_host
@@ -458,11 +489,36 @@ int wf_attention_round(wf_handle* h, int32_t layer, int32_t slot_first, int32_t 
     const bool fp8 = c.qk_dtype == WF_DTYPE_FP8_E4M3;
     if (fp8 && !q_scales) return WF_E_INVALID_ARG;
     if (((uintptr_t)q % 16) || ((uintptr_t)out % 16)) return WF_E_INVALID_ARG;
+    for (int s = slot_first; s < slot_first + nslots; ++s)
+        if (!h->present(h->position_of_slot(s))) {
+            snprintf(h->err, sizeof h->err, "slot %d holds no chunk in round %lld", s, (long long)h->round());
+            return WF_E_INVALID_ARG;
+        }
+    // The positions that hold a chunk form at most two runs: the anchors
+    // stored so far, [0, anc), and [p2, T - s_lo), from the first occupied
+    // non-anchor position to the noisiest occupied slot s_lo (every position
+    // in steady rounds: anc = A, p2 = A, s_lo = 0).
+    int anc = 0;
+    while (anc < h->A() && h->present(anc)) ++anc;
+    int p2 = h->A();
+    while (p2 < L.T && !h->present(p2)) ++p2;
+    int s_lo = 0;
+    while (s_lo <= c.S && !h->present(h->position_of_slot(s_lo))) ++s_lo;
+    for (int p = 0; p < L.T; ++p) {
+        const bool in_runs = p < anc || (p >= p2 && p < L.T - s_lo);
+        if (in_runs != h->present(p)) {
+            snprintf(h->err, sizeof h->err, "round %lld: occupied positions are not two runs",
+                     (long long)h->round());
+            return WF_E_SHAPE;
+        }
+    }
     // readiness check made just before attention: the union of the requested
     // slots' legal contexts is the prefix [0, T - slot_first) (the whole
-    // context with the all-live mask)
+    // context with the all-live mask), less the positions without a chunk
     const bool all_live = c.live_mask == WF_MASK_ALL_LIVE;
-    const uint64_t need = h->prefix_bits(all_live ? L.T : L.T - slot_first);
+    uint64_t need = h->prefix_bits(all_live ? L.T - s_lo : L.T - slot_first);
+    for (int p = 0; p < L.T; ++p)
+        if (!h->present(p)) need &= ~(1ull << p);
     if ((h->ready[layer] & need) != need) {
         snprintf(h->err, sizeof h->err, "layer %d: positions 0x%llx not published", layer,
                  (unsigned long long)(need & ~h->ready[layer]));
@@ -487,6 +543,9 @@ int wf_attention_round(wf_handle* h, int32_t layer, int32_t slot_first, int32_t 
     a.out_fp32 = out_dtype == WF_DTYPE_FP32;
     a.nblk = L.nblk;
     a.all_live = all_live ? 1 : 0;
+    a.anc = anc;
+    a.p2 = p2;
+    a.end_all = L.T - s_lo;
     a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)c.head_dim));
     const hipError_t e = wf::launch_attention(a, fp8, (hipStream_t)stream);
     if (e != hipSuccess) return h->fail_hip(e, "wf_attention_round launch");
@@ -497,14 +556,23 @@ int wf_round_advance(wf_handle* h, void* stream) {
     if (!h) return WF_E_INVALID_ARG;
     const int A = h->A(), H = h->H();
     const int store = A + H;
-    for (int l = 0; l < h->cfg.num_layers; ++l)
-        if (!(h->ready[l] >> store & 1)) {
-            snprintf(h->err, sizeof h->err, "layer %d: store not published", l);
-            return WF_E_NOT_READY;
-        }
+    const int64_t k = h->round();
+    if (h->cfg.total_chunks > 0 && k + 1 > (int64_t)h->cfg.total_chunks - 1 + h->S()) {
+        snprintf(h->err, sizeof h->err, "round %lld is the last of a %d-chunk video", (long long)k,
+                 h->cfg.total_chunks);
+        return WF_E_INVALID_ARG;
+    }
+    const bool store_held = h->present(store);
+    const int store_anchor = h->store_anchor_at_round(k);
+    if (store_held)
+        for (int l = 0; l < h->cfg.num_layers; ++l)
+            if (!(h->ready[l] >> store & 1)) {
+                snprintf(h->err, sizeof h->err, "layer %d: store not published", l);
+                return WF_E_NOT_READY;
+            }
     if (!h->host_model) {
-        const hipError_t e =
-            wf::launch_page_table(h->table, h->L.T, A, h->L.ppc, h->ring + 1, (hipStream_t)stream);
+        const hipError_t e = wf::launch_page_table(h->table, h->L.T, A, h->L.ppc, h->ring + 1, store,
+                                                   h->store_anchor_at_round(k + 1), (hipStream_t)stream);
         if (e != hipSuccess) return h->fail_hip(e, "wf_round_advance launch");
     }
     h->ring += 1;
@@ -513,6 +581,12 @@ int wf_round_advance(wf_handle* h, void* stream) {
         uint64_t nw = old & h->prefix_bits(A);                       // anchor stays
         for (int p = A; p < A + H; ++p)                              // history <- one cleaner
             nw |= ((old >> (p + 1)) & 1ull) << p;
+        if (store_anchor >= 0) {                                     // a stored anchor chunk
+            nw |= ((old >> store) & 1ull) << store_anchor;
+            if (H > 0) nw &= ~(1ull << (A + H - 1));
+        }
+        for (int p = 0; p < h->L.T; ++p)                             // empty positions stay unready
+            if (!h->present(p)) nw &= ~(1ull << p);
         h->ready[l] = nw;                                            // live slots cleared
     }
     return WF_OK;
@@ -526,7 +600,7 @@ int wf_round_index(const wf_handle* h, int64_t* k) {
 
 int wf_schedule_chunk_ids(const wf_handle* h, int64_t* ids) {
     if (!h || !ids) return WF_E_INVALID_ARG;
-    for (int p = 0; p < h->L.T; ++p) ids[p] = h->chunk_at(p);
+    for (int p = 0; p < h->L.T; ++p) ids[p] = h->present(p) ? h->chunk_at(p) : -1;
     return WF_OK;
 }
 

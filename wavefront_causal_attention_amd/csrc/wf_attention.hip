@@ -242,8 +242,12 @@ __global__ __launch_bounds__(NTH, NW == 4 ? 2 : 1) void attn_kernel(AttnArgs a) 
     const int head = work_head(unit);
     const int qt = work_qtile(unit);
     const int N = a.N, pt = a.pt, ppc = a.ppc;
-    const int nctx = a.all_live ? a.T : a.T - s;   // context chunks slot s reads
-    const int nkeys = nctx * N;                    // legal prefix of slot s
+    // context chunks slot s reads: the occupied positions [0, anc) and [p2,
+    // end) (every position of the prefix in steady rounds), visited through a
+    // virtual position v -> v < anc ? v : v + gap
+    const int gap = a.p2 - a.anc;
+    const int nctx = a.anc + (a.all_live ? a.end_all : a.T - s) - a.p2;
+    const int nkeys = nctx * N;                    // legal keys of slot s
     // bf16: tiles cover the flat prefix; fp8: tpc tiles per chunk
     const int tpc = FP8 ? (N + BN - 1) / BN : 1;
     const int ntiles = FP8 ? nctx * tpc : (nkeys + BN - 1) / BN;
@@ -306,11 +310,11 @@ __global__ __launch_bounds__(NTH, NW == 4 ? 2 : 1) void attn_kernel(AttnArgs a) 
             const int c = (int)fast_div((uint32_t)t, tdiv);
             const int o64 = (t - c * tpc) * BN + o;
             ok = c < nctx && o64 < N;
-            return c * N + o64;
+            return (c < a.anc ? c : c + gap) * N + o64;
         } else {
             const int g = t * BN + o;
             ok = g < nkeys;
-            return g;
+            return g < a.anc * N ? g : g + gap * N;
         }
     };
 
@@ -332,7 +336,8 @@ __global__ __launch_bounds__(NTH, NW == 4 ? 2 : 1) void attn_kernel(AttnArgs a) 
             const int c = (int)fast_div((uint32_t)i, tdiv);
             const int n = (i - c * tpc) * BN;
             const int pg = n / pt, tok = n - pg * pt;
-            g_stab[i] = a.kscale[((int64_t)ptab[c * ppc + pg] * a.heads + head) * pt + tok];
+            const int pos = c < a.anc ? c : c + gap;
+            g_stab[i] = a.kscale[((int64_t)ptab[pos * ppc + pg] * a.heads + head) * pt + tok];
         }
     }
     // Offsets of the next tile's DMA are computed one tile ahead (page-table
@@ -433,8 +438,9 @@ __global__ __launch_bounds__(NTH, NW == 4 ? 2 : 1) void attn_kernel(AttnArgs a) 
     // dequantised next; recomputed only when tiles enter a new chunk.
     int bchunk = 0;
     float bcur = 0.f;
-    auto chunk_bias = [&](int pos) -> float {
-        if (pos >= nctx) return 0.f;
+    auto chunk_bias = [&](int vpos) -> float {
+        if (vpos >= nctx) return 0.f;
+        const int pos = vpos < a.anc ? vpos : vpos + gap;
         const int g = ptab[pos * ppc] / ppc;
         const float* mu = a.kmean + ((int64_t)g * a.heads + head) * D + 32 * hf;
         float acc = 0.f;

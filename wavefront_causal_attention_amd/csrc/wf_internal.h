@@ -88,11 +88,14 @@ struct AttnArgs {
     int out_fp32;
     int nblk;
     int all_live;             // 1: every slot reads the whole context (no mask)
+    // occupied context positions: [0, anc) and [p2, T - s) (all-live: [p2,
+    // end_all)); virtual position v maps to v < anc ? v : v + p2 - anc
+    int anc, p2, end_all;
     float scale_log2;         // log2(e) / sqrt(D)
 };
 
-hipError_t launch_page_table(int32_t* table, int T, int A, int ppc, int64_t ring,
-                             hipStream_t st);
+hipError_t launch_page_table(int32_t* table, int T, int A, int ppc, int64_t ring, int store_pos,
+                             int store_anchor, hipStream_t st);
 hipError_t launch_publish(const PublishArgs& a, bool fp8, hipStream_t st);
 hipError_t launch_attention(const AttnArgs& a, bool fp8, hipStream_t st);
 

@@ -490,21 +490,27 @@ __global__ __launch_bounds__(256) void publish_fp8_kernel(PublishArgs a) {
 }
 
 // table[p][i] = group(p) * ppc + i; group(p) = p for the anchor, otherwise
-// A + ((p - A + ring) mod (T - A)).
-__global__ void page_table_kernel(int32_t* table, int T, int A, int ppc, int64_t ring) {
+// A + ((p - A + ring) mod (T - A)); while the store holds an anchor chunk
+// (store_anchor >= 0, pipeline fill) the store position writes that anchor's
+// group.
+__global__ void page_table_kernel(int32_t* table, int T, int A, int ppc, int64_t ring, int store_pos,
+                                  int store_anchor) {
     const int i = blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= T * ppc) return;
     const int p = i / ppc, pg = i - p * ppc;
     const int R = T - A;
-    const int g = p < A ? p : A + (int)(((int64_t)(p - A) + ring) % R);
+    int g = p < A ? p : A + (int)(((int64_t)(p - A) + ring) % R);
+    if (p == store_pos && store_anchor >= 0) g = store_anchor;
     table[i] = g * ppc + pg;
 }
 
 }  // namespace
 
-hipError_t launch_page_table(int32_t* table, int T, int A, int ppc, int64_t ring, hipStream_t st) {
+hipError_t launch_page_table(int32_t* table, int T, int A, int ppc, int64_t ring, int store_pos,
+                             int store_anchor, hipStream_t st) {
     const int n = T * ppc;
-    hipLaunchKernelGGL(page_table_kernel, dim3((n + 255) / 256), dim3(256), 0, st, table, T, A, ppc, ring);
+    hipLaunchKernelGGL(page_table_kernel, dim3((n + 255) / 256), dim3(256), 0, st, table, T, A, ppc, ring,
+                       store_pos, store_anchor);
     return hipGetLastError();
 }
 
