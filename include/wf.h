@@ -65,7 +65,9 @@ typedef struct wf_config {
     int32_t chunk_frames;    /* latent frames per chunk                             */
     int32_t frame_h;         /* patch rows per latent frame                         */
     int32_t frame_w;         /* patch columns per latent frame                      */
-    int32_t page_tokens;     /* tokens per page; divides the chunk, multiple of 8   */
+    int32_t page_tokens;     /* tokens per page; divides the chunk, multiple of 8.
+                                Limits: T = A+H+S+1 <= 64, T * pages per chunk
+                                <= 1024, T * chunk tokens < 2^22 - 1              */
     int32_t in_dtype;        /* projected Q/K/V input: WF_DTYPE_BF16 | WF_DTYPE_FP32 */
     int32_t qk_dtype;        /* published Q/K: WF_DTYPE_BF16 | WF_DTYPE_FP8_E4M3
                                 (fp8: T * ceil(chunk tokens / 64) <= 4096)         */

@@ -175,6 +175,9 @@ int validate(const wf_config* c, Layout* L) {
     if (c->chunk_frames < 1 || c->frame_h < 1 || c->frame_w < 1) return WF_E_SHAPE;
     const int64_t N = (int64_t)c->chunk_frames * c->frame_h * c->frame_w;
     if (N > (1 << 20)) return WF_E_SHAPE;
+    // attention splits flat context keys into page and token in fp32, exact
+    // below 2^22 - 1 keys
+    if ((int64_t)T * N >= (1 << 22) - 1) return WF_E_SHAPE;
     if (c->page_tokens < 8 || c->page_tokens % 8 != 0 || N % c->page_tokens != 0) return WF_E_SHAPE;
     // fp8 attention tiles each chunk into its 64-token quantisation blocks and
     // stages one key scale per tile of the context in LDS

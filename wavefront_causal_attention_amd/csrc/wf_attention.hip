@@ -60,7 +60,10 @@ constexpr int NSTG = WF_ATTN_STAGES;   // K and V tile buffers each
 static_assert(NSTG >= 2 && NSTG <= 4, "2 to 4 tile stages");
 static_assert(NW >= 4 && NW <= 8 && BM % 32 == 0, "4 to 8 waves of 32 query rows");
 constexpr int kRescaleLog2 = 8; // running max may lag the true max by up to 2^8
-constexpr uint32_t kOOB = 0x80000000u;   // buffer offset past every region: loads zeros
+// Buffer offset past every region (each is under 2^31 bytes): loads zeros.
+// The in-tile addends of a DMA are below 2^31 as well, so kOOB plus any of
+// them stays out of range without wrapping.
+constexpr uint32_t kOOB = 0x80000000u;
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     bf16x2 r = {(__bf16)lo, (__bf16)hi};
@@ -119,6 +122,8 @@ __shared__ __align__(16) uint16_t g_vt1[kTileElems];
 __shared__ __align__(16) uint16_t g_vt2[kTileElems];
 __shared__ __align__(16) uint16_t g_vt3[kTileElems];
 __shared__ int g_ptab[kMaxTablePages];
+// element offset of (page, head) for each virtual page of the slot's context
+__shared__ uint32_t g_pbase[kMaxTablePages];
 __shared__ float g_stab[kMaxFp8Tiles];   // fp8: key scale of every tile of the prefix
 
 template <int I>
@@ -254,6 +259,14 @@ __global__ __launch_bounds__(NTH, NW == 4 ? 2 : 1) void attn_kernel(AttnArgs a) 
     const FastDiv tdiv = make_fastdiv((uint32_t)tpc);
 
     for (int i = tid; i < a.T * ppc; i += NTH) ptab[i] = a.table[i];
+    // Page base of every virtual page: the context's occupied positions
+    // renumbered without the gap, each page's (page, head) block in elements
+    // (the same for K and V; K bytes = KB x elements, V bytes = 2 x elements).
+    // Below 2^30 because every page region is under 2 GiB.
+    for (int i = tid; i < nctx * ppc; i += NTH) {
+        const int pp = i < a.anc * ppc ? i : i + gap * ppc;
+        g_pbase[i] = (uint32_t)(((int64_t)a.table[pp] * a.heads + head) * pt * D);
+    }
 
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
@@ -266,7 +279,6 @@ __global__ __launch_bounds__(NTH, NW == 4 ? 2 : 1) void attn_kernel(AttnArgs a) 
         __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(a.kpage), (short)0, a.kbytes, 0x00020000);
     const __amdgpu_buffer_rsrc_t vrs =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.vpage), (short)0, a.vbytes, 0x00020000);
-    const int64_t head_blk = (int64_t)pt * D;      // elements of one (page, head) block
     const bf16x2 kOnes = {(__bf16)1.0f, (__bf16)1.0f};
     const float c = a.scale_log2;
     float cl = c;                                  // exp2 constant of this lane's row
@@ -303,19 +315,29 @@ __global__ __launch_bounds__(NTH, NW == 4 ? 2 : 1) void attn_kernel(AttnArgs a) 
     // whole pages of pt tokens, so flat key g is token g % pt of context page
     // g / pt.
     int ktile = 0, vtile = 0;
-    const FastDiv pdiv = make_fastdiv((uint32_t)pt);
-    // flat key index of offset o (< 64) in tile t, and whether it is legal
+    // flat virtual key index of offset o (< 64) in tile t, and whether it is legal
     auto tile_key = [&](int t, int o, bool& ok) -> int {
         if constexpr (FP8) {
             const int c = (int)fast_div((uint32_t)t, tdiv);
             const int o64 = (t - c * tpc) * BN + o;
             ok = c < nctx && o64 < N;
-            return (c < a.anc ? c : c + gap) * N + o64;
+            return c * N + o64;
         } else {
             const int g = t * BN + o;
             ok = g < nkeys;
-            return g < a.anc * N ? g : g + gap * N;
+            return g;
         }
+    };
+    // Virtual page and token of a legal flat key g (< 2^22, checked on the
+    // host): floor((g + 1/2) / pt) in fp32 is exact there, since the relative
+    // error of the two roundings stays below the 1/(2 pt) margin to the next
+    // integer; this keeps the 32-bit multiplies off the per-tile VALU budget.
+    const float rpt = 1.0f / (float)pt;
+    const float rpt_half = 0.5f * rpt;
+    auto page_tok = [&](uint32_t g, uint32_t& tok) -> uint32_t {
+        const uint32_t pidx = (uint32_t)__builtin_fmaf((float)g, rpt, rpt_half);
+        tok = g - __umul24(pidx, (uint32_t)pt);
+        return pidx;
     };
 
     // K instructions of this wave: vectors wave*KPW .. (wave+1)*KPW-1 below KV
@@ -349,22 +371,21 @@ __global__ __launch_bounds__(NTH, NW == 4 ? 2 : 1) void attn_kernel(AttnArgs a) 
     auto k_addr = [&]() {
         bool ok;
         const int g = tile_key(ktile, lane, ok);
-        const uint32_t gi = ok ? (uint32_t)g : 0u;              // the lookup stays in the table
-        const uint32_t pidx = fast_div(gi, pdiv);
-        const uint32_t tok = gi - pidx * (uint32_t)pt;
-        const int64_t ph = (int64_t)ptab[pidx] * a.heads + head;
-        const uint32_t off = FP8 ? (uint32_t)(ph * head_blk + (int64_t)tok * 16)
-                                 : (uint32_t)((ph * head_blk + (int64_t)tok * 8) * 2);
+        uint32_t tok;
+        const uint32_t pidx = page_tok(ok ? (uint32_t)g : 0u, tok);   // the lookup stays in the table
+        const uint32_t off = g_pbase[pidx] * (FP8 ? 1u : 2u) + tok * 16u;
         koff = ok ? off : kOOB;
     };
+    // a V key chunk is wave-uniform: its page split runs on the scalar unit
+    const FastDiv pdiv = make_fastdiv((uint32_t)pt);
     auto v_addr = [&](int i) {
         bool ok;
         const int g = tile_key(vtile, 8 * (wave * VCW + i), ok);
         const uint32_t gi = ok ? (uint32_t)g : 0u;
         const uint32_t pidx = fast_div(gi, pdiv);
         const uint32_t tok = gi - pidx * (uint32_t)pt;
-        const uint32_t off =
-            (uint32_t)((((int64_t)ptab[pidx] * a.heads + head) * head_blk + (int64_t)tok * D) * 2);
+        const uint32_t base = __builtin_amdgcn_readfirstlane(g_pbase[pidx]);
+        const uint32_t off = base * 2u + tok * (uint32_t)(2 * D);
         voff[i] = ok ? off : kOOB;
     };
     k_addr();
@@ -379,7 +400,7 @@ __global__ __launch_bounds__(NTH, NW == 4 ? 2 : 1) void attn_kernel(AttnArgs a) 
         for (int i = 0; i < KPW; ++i) {
             const int vec = wave * KPW + i;
             if (KV % NW == 0 || i < kmine)
-                dma16(krs, kb8 + vec * BN * 16, koff == kOOB ? kOOB : koff + (uint32_t)(vec * pt * 16));
+                dma16(krs, kb8 + vec * BN * 16, koff + (uint32_t)(vec * pt * 16));
         }
         ++ktile;
         k_addr();
@@ -390,8 +411,7 @@ __global__ __launch_bounds__(NTH, NW == 4 ? 2 : 1) void attn_kernel(AttnArgs a) 
             const int kc = wave * VCW + i;
 #pragma unroll
             for (int h = 0; h < VDH; ++h)
-                dma16(vrs, vl + (kc * D + 64 * h) * 8,
-                      voff[i] == kOOB ? kOOB : voff[i] + (uint32_t)((64 * h + lane) * 16));
+                dma16(vrs, vl + (kc * D + 64 * h) * 8, voff[i] + (uint32_t)((64 * h + lane) * 16));
         }
         ++vtile;
 #pragma unroll
