@@ -67,7 +67,7 @@ def parse():
                     help="all: every live slot reads every live slot (no tile skipped), for "
                          "measuring what the wavefront mask saves")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=1024, help="query rows per (slot, head) in the CPU sample")
+    ap.add_argument("--cpu-rows", type=int, default=1536, help="query rows per (slot, head) in the CPU sample")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="also run one device copy of this many MiB (counter calibration)")
     return ap.parse_args()
