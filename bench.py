@@ -7,7 +7,9 @@ rotation). Inputs are resident in HBM before timing starts.
 
 Prints one JSON line. `value` is mask-aware attention TFLOP/s over the whole
 step (publish + attention + advance); rounds/s, per-kernel times, the
-attention roofline and an fp64-oracle CPU baseline ride along.
+attention roofline and an fp64-oracle CPU baseline ride along. With
+--layers L a step is one model round: every layer publishes and attends over
+its own pages (one pool, one page table), then one advance.
 """
 from __future__ import annotations
 
@@ -66,6 +68,9 @@ def parse():
     ap.add_argument("--live-mask", default="wavefront", choices=["wavefront", "all"],
                     help="all: every live slot reads every live slot (no tile skipped), for "
                          "measuring what the wavefront mask saves")
+    ap.add_argument("--layers", type=int, default=1,
+                    help="layers sharing one pool and page table; a step is then one model round "
+                         "(publish + attention of every layer, one advance)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=1536, help="query rows per (slot, head) in the CPU sample")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -99,8 +104,9 @@ def main():
                          head_dim=w.head_dim, chunk_frames=w.chunk_frames, frame_h=w.frame_h,
                          frame_w=w.frame_w, page_tokens=w.page_tokens, in_dtype=w.in_dtype,
                          qk_dtype=w.qk_dtype, rope_split=w.rope_split, rope_theta=w.rope_theta,
-                         first_round=k0, live_mask=w.live_mask)
+                         first_round=k0, live_mask=w.live_mask, num_layers=args.layers)
     pool = wf.Pool(cfg, device=dev)
+    L = args.layers
     tdt = torch.bfloat16 if w.in_dtype == "bf16" else torch.float32
 
     def to_dev(arrs):
@@ -110,7 +116,8 @@ def main():
     ids = pool.chunk_ids()
     cl = [W.stored_draw(w, ids[w.T - 1 - slot]) for slot in range(w.S + 1, w.T)]
     kc, vc = to_dev([x[1] for x in cl]), to_dev([x[2] for x in cl])
-    pool.publish(0, w.S + 1, w.T - w.S - 1, None, kc, vc, w.hd)
+    for layer in range(L):
+        pool.publish(layer, w.S + 1, w.T - w.S - 1, None, kc, vc, w.hd)
     del cl
     # live slots: one seeded round of projected Q/K/V, resident for every step
     live = W.draw_slots(w, k0, range(w.S + 1))
@@ -128,25 +135,30 @@ def main():
 
     stream = torch.cuda.current_stream()
 
+    # every layer publishes the same resident projection output into its own
+    # pages and attends over them: the work per layer is the real one
     def step(ev=None):
-        if ev is not None:
-            ev[0].record(stream)
-        pool.publish(0, 0, w.S + 1, qd, kd, vd, stride, q_out=q, q_scales=qs, stream=stream)
-        if ev is not None:
-            ev[1].record(stream)
-        pool.attention(0, 0, w.S + 1, q, out, q_scales=qs, stream=stream)
-        if ev is not None:
-            ev[2].record(stream)
-        pool.advance(stream=stream)
+        for layer in range(L):
+            if ev is not None and layer == 0:
+                ev[0].record(stream)
+            pool.publish(layer, 0, w.S + 1, qd, kd, vd, stride, q_out=q, q_scales=qs, stream=stream)
+            if ev is not None and layer == 0:
+                ev[1].record(stream)
+            pool.attention(layer, 0, w.S + 1, q, out, q_scales=qs, stream=stream)
+            if ev is not None and layer == 0:
+                ev[2].record(stream)
         if ev is not None:
             ev[3].record(stream)
+        pool.advance(stream=stream)
+        if ev is not None:
+            ev[4].record(stream)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
     K = args.steps
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(K)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
@@ -154,18 +166,19 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    pub_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    pub_ms = [e[0].elapsed_time(e[1]) for e in evs]          # layer 0's kernels
     att_ms = [e[1].elapsed_time(e[2]) for e in evs]
-    adv_ms = [e[2].elapsed_time(e[3]) for e in evs]
+    adv_ms = [e[3].elapsed_time(e[4]) for e in evs]
+    gpu_ms = [e[0].elapsed_time(e[4]) for e in evs]           # whole step on the stream
     ms_step = wall * 1e3 / K
-    F = w.attention_flops()
+    F = w.attention_flops() * L
     att_avg = float(np.mean(att_ms))
     pub_avg = float(np.mean(pub_ms))
     n_el = (w.S + 1) * w.N * w.hd
     in_bytes = 3 * n_el * (2 if w.in_dtype == "bf16" else 4)
     qk_bytes = 1 if w.qk_dtype == "fp8" else 2
     pub_bytes = in_bytes + 2 * n_el * qk_bytes + 2 * n_el            # read QKV; write Q, K, V
-    attn_tflops = F / (att_avg * 1e-3) / 1e12
+    attn_tflops = w.attention_flops() / (att_avg * 1e-3) / 1e12
     traffic = measured_traffic()
 
     if args.calibrate_copy_mib > 0:
@@ -193,10 +206,15 @@ def main():
                    "chunk_tokens": w.N, "chunk_shape": [w.chunk_frames, w.frame_h, w.frame_w],
                    "heads": w.heads, "head_dim": w.head_dim, "page_tokens": w.page_tokens,
                    "mask_aware_flops_per_round": F, "out_dtype": args.out_dtype,
-                   "live_mask": w.live_mask},
+                   "live_mask": w.live_mask, "layers": L},
         "rounds_per_sec": round(1e3 / ms_step, 3),
         "attention_ms": round(att_avg, 4),
         "attention_ms_minmax": [round(min(att_ms), 4), round(max(att_ms), 4)],
+        "attention_ms_median": round(float(np.median(att_ms)), 4),
+        "stream_ms_per_step": round(float(np.mean(gpu_ms)), 4),
+        # stream time not spent in the step's kernels (launch gaps), one layer only
+        "launch_gap_ms": (round(float(np.mean(gpu_ms)) - att_avg - pub_avg - float(np.mean(adv_ms)), 4)
+                          if L == 1 else None),
         "publish_ms": round(pub_avg, 4),
         "advance_ms": round(float(np.mean(adv_ms)), 4),
         "attention_tflops": round(attn_tflops, 2),
