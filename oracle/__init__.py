@@ -16,6 +16,8 @@ Sources (the Wave Forcing pages, arXiv 2611.00859):
     rank S is Store) and Figure 1 (S=4 wavefront, one chunk per round).
   * hyper.ai summary, section "Method" (WaveRT paragraph): K/V are published
     after QKV projection and RoPE.
+  * thelatestinai.com listing, Table 11: model widths (hidden = heads x 128),
+    the shape of the QKV projection that precedes RoPE.
 
 Where the pages are silent the oracle takes these readings: softmax scale
 1/sqrt(d); adjacent-pair 3D RoPE on contiguous t|h|w channel ranges with
@@ -38,6 +40,7 @@ from .numerics import (bf16_round, fp8_e4m3_encode, fp8_e4m3_decode,
 from .attention import (masked_softmax_attention, slot_attention, round_attention,
                         dense_round_attention)
 from .round import oracle_round, rotate_chunk, rotated_context
+from .projection import project_qkv, split_qkv
 
 __all__ = [
     "RoundSchedule", "live_mask", "legal_positions", "GroupRing", "slot_position",
@@ -47,4 +50,5 @@ __all__ = [
     "masked_softmax_attention", "slot_attention", "round_attention",
     "dense_round_attention",
     "oracle_round", "rotate_chunk", "rotated_context",
+    "project_qkv", "split_qkv",
 ]

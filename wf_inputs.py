@@ -184,6 +184,26 @@ def draw(w: Workload, round_index: int, slot: int):
     return q, k, v
 
 
+def draw_hidden(w: Workload, round_index: int, slot: int) -> np.ndarray:
+    """Hidden states entering the QKV projection for one chunk: float32
+    [N, hidden] (hidden = heads * head_dim, the Wan2.1 widths), N(0, 1),
+    bf16-exact. Own stream per (seed, round, slot), apart from draw()'s."""
+    ss = np.random.SeedSequence([w.seed, 0x68696464, int(round_index), int(slot)])
+    rng = np.random.Generator(np.random.PCG64(ss))
+    return round_to_bf16(rng.standard_normal((w.N, w.hd), dtype=np.float32))
+
+
+def projection_weights(w: Workload, layer: int = 0):
+    """Random-init QKV projection of one layer: weight float32 [3*h*d, hidden]
+    ([out, in]) ~ N(0, 1/hidden), bias float32 [3*h*d] ~ N(0, 0.1^2), both
+    bf16-exact, so the projected Q/K/V are about N(0, 1)."""
+    ss = np.random.SeedSequence([w.seed, 0x77716b76, int(layer)])
+    rng = np.random.Generator(np.random.PCG64(ss))
+    wt = rng.standard_normal((3 * w.hd, w.hd), dtype=np.float32) * np.float32(1.0 / np.sqrt(w.hd))
+    b = rng.standard_normal(3 * w.hd, dtype=np.float32) * np.float32(0.1)
+    return round_to_bf16(wt), round_to_bf16(b)
+
+
 def stored_draw(w: Workload, chunk_id: int):
     """K/V of a clean chunk as published by the store slot (round chunk_id + S)."""
     return draw(w, chunk_id + w.S, w.S)
