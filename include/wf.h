@@ -156,6 +156,33 @@ int wf_kv_publish(wf_handle* h, int32_t layer, int32_t slot_first, int32_t nslot
                   const int32_t* chunk_t0_host, void* q_out, float* q_scales, void* stream);
 
 /*
+ * QKV projection with RoPE + publish as its epilogue (hyper.ai summary,
+ * "Method": WaveRT publishes K/V right after the QKV projection and RoPE;
+ * thelatestinai.com listing, Table 11: the projection maps the hidden state,
+ * heads x 128 wide, to Q, K and V). One launch computes, for the live slots
+ * [slot_first, slot_first + nslots) of one layer,
+ *     qkv[n][o] = sum_c x[n][c] * w[o][c] + bias[o]
+ * and publishes it as wf_kv_publish would publish that projection output
+ * (RoPE on Q and K in fp32, bf16 pages and Q), without writing qkv to memory.
+ *
+ * x:      device bf16, row (i*N + n) = token n of slot slot_first + i, hidden
+ *         contiguous elements at x + row * x_row_stride_elems (16-byte aligned
+ *         rows).
+ * hidden: input width, a multiple of 64.
+ * w:      device bf16 [3*heads*head_dim][hidden], output channel o's weights
+ *         contiguous (the [out][in] layout of a linear layer); outputs
+ *         [0, h*d) are Q, [h*d, 2h*d) K, [2h*d, 3h*d) V, head-major.
+ * bias:   device bf16 [3*heads*head_dim], or NULL.
+ * chunk_t0_host, q_out: as for wf_kv_publish (q_out required, bf16).
+ * Only live slots (slot_first + nslots <= S+1). WF_E_SHAPE for fp8 pools,
+ * heads*head_dim not a multiple of 128, a frame smaller than 1/32 of a
+ * 256-token tile, or x or w of 2 GiB or more. Marks the slots published.
+ */
+int wf_qkv_project_publish(wf_handle* h, int32_t layer, int32_t slot_first, int32_t nslots,
+                           const void* x, int64_t x_row_stride_elems, int32_t hidden, const void* w,
+                           const void* bias, const int32_t* chunk_t0_host, void* q_out, void* stream);
+
+/*
  * Wavefront attention over the paged context (hyper.ai summary, "Method":
  * M_WF(s, j) = 1[j >= s], full attention inside a chunk). One launch computes
  * O = softmax(Q K^T / sqrt(d)) V for query slots [slot_first, slot_first+nslots)

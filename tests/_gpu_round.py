@@ -175,3 +175,27 @@ def gpu_rows(out: torch.Tensor, w: W.Workload, rows, heads=None, slots=None):
 def err_stats(gpu: np.ndarray, ref: np.ndarray):
     diff = gpu - ref
     return float(np.max(np.abs(diff))), float(np.linalg.norm(diff) / np.linalg.norm(ref))
+
+
+def bf16_dev_bits_to_f32(t: torch.Tensor) -> np.ndarray:
+    """bf16 device tensor (any int16 view) -> float32 numpy of the same values."""
+    return (t.view(torch.int16).cpu().numpy().astype(np.int32).astype(np.uint32) << 16).view(np.float32)
+
+
+def read_pages(pool, w: W.Workload, layer=0):
+    """K and V pages of one layer as float32 [page, head, token, d]."""
+    g = pool.geometry
+    npages = w.T * pool.ppc
+    D, pt = w.head_dim, w.page_tokens
+    n = npages * w.heads * pt * D * 2
+    ko = g["k_off"] + layer * g["k_layer_bytes"]
+    vo = g["v_off"] + layer * g["v_layer_bytes"]
+    kp = pool.pool[ko:ko + n].view(torch.int16).view(npages, w.heads, D // 8, pt, 8).permute(0, 1, 3, 2, 4)
+    vp = pool.pool[vo:vo + n].view(torch.int16).view(npages, w.heads, pt // 8, D, 8).permute(0, 1, 2, 4, 3)
+    return (bf16_dev_bits_to_f32(kp.reshape(npages, w.heads, pt, D).contiguous()),
+            bf16_dev_bits_to_f32(vp.reshape(npages, w.heads, pt, D).contiguous()))
+
+
+def position_rows(pages: np.ndarray, table, p: int, ppc: int) -> np.ndarray:
+    """[heads, N, d] of context position p from pages [page, head, token, d]."""
+    return np.concatenate([pages[table[p * ppc + i]] for i in range(ppc)], axis=1)

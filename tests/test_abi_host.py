@@ -338,3 +338,61 @@ def test_fill_and_drain_whole_video(lib, S, A, H, C):
         assert e.value.status == wf.WF_E_INVALID_ARG
     finally:
         wf.wf_pool_destroy(h)
+
+
+def _proj(h, w, **kw):
+    args = dict(layer=0, slot_first=0, nslots=w.S + 1, x=FAKE, stride=w.hd, hidden=w.hd, wt=FAKE, bias=None,
+                q_out=FAKE)
+    args.update(kw)
+    wf.wf_qkv_project_publish(h, args["layer"], args["slot_first"], args["nslots"], args["x"], args["stride"],
+                              args["hidden"], args["wt"], args["bias"], None, args["q_out"], None)
+
+
+def test_project_publish_marks_live_slots_and_validates(lib):
+    w = W.WORKLOADS["ragged128"]
+    h = wf.wf_pool_create_host_model(cfg_of(w))
+    try:
+        bad = [dict(slot_first=1, nslots=w.S + 1), dict(nslots=0), dict(x=None), dict(wt=None), dict(q_out=None),
+               dict(hidden=w.hd + 32), dict(stride=w.hd - 64), dict(stride=w.hd + 4), dict(x=FAKE + 8),
+               dict(layer=1)]
+        for kw in bad:
+            with pytest.raises(wf.WfError) as e:
+                _proj(h, w, **kw)
+            assert e.value.status == wf.WF_E_INVALID_ARG, kw
+            assert wf.wf_ready_mask(h, 0) == 0
+        _proj(h, w, slot_first=1, nslots=w.S)            # slots 1..S
+        live = sum(1 << (w.T - 1 - s) for s in range(1, w.S + 1))
+        assert wf.wf_ready_mask(h, 0) == live
+        _proj(h, w, slot_first=0, nslots=1, hidden=2 * w.hd, stride=2 * w.hd, bias=FAKE)
+        assert wf.wf_ready_mask(h, 0) == live | 1 << (w.T - 1)
+    finally:
+        wf.wf_pool_destroy(h)
+
+
+@pytest.mark.parametrize("change", [dict(qk_dtype="fp8"), dict(heads=3, head_dim=64),
+                                    dict(frame_h=1, frame_w=8, chunk_frames=8, page_tokens=64)])
+def test_project_publish_rejects_unsupported_shapes(lib, change):
+    import dataclasses
+    w = dataclasses.replace(W.WORKLOADS["tiny"], **change)
+    if change.get("heads") == 3:
+        w = dataclasses.replace(w, rope_split=(24, 20, 20))
+    h = wf.wf_pool_create_host_model(cfg_of(w))
+    try:
+        with pytest.raises(wf.WfError) as e:
+            _proj(h, w)
+        assert e.value.status == wf.WF_E_SHAPE
+    finally:
+        wf.wf_pool_destroy(h)
+
+
+def test_project_publish_rejects_empty_slots_in_fill_rounds(lib):
+    w = W.WORKLOADS["tiny"]
+    h = wf.wf_pool_create_host_model(cfg_of(w, first_round=0))
+    try:
+        with pytest.raises(wf.WfError) as e:
+            _proj(h, w)                                    # round 0: only slot 0 holds a chunk
+        assert e.value.status == wf.WF_E_INVALID_ARG
+        _proj(h, w, nslots=1)
+        assert wf.wf_ready_mask(h, 0) == 1 << (w.T - 1)
+    finally:
+        wf.wf_pool_destroy(h)

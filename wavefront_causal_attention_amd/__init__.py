@@ -11,6 +11,7 @@ from ._lib import (WF_DTYPE_BF16, WF_DTYPE_FP32, WF_DTYPE_FP8_E4M3, WF_E_HIP, WF
                    WF_E_NOT_READY, WF_E_SHAPE, WF_MASK_ALL_LIVE, WF_MASK_WAVEFRONT, WF_OK, WfError,
                    load, wf_attention_round, wf_config,
                    wf_geometry, wf_kv_publish, wf_page_table_host, wf_pool_bytes, wf_pool_create,
+                   wf_qkv_project_publish,
                    wf_pool_create_host_model, wf_pool_destroy, wf_ready_mask, wf_round_advance,
                    wf_round_index, wf_schedule_chunk_ids)
 
@@ -89,6 +90,11 @@ class Pool:
                 chunk_t0=None, stream=None):
         wf_kv_publish(self.handle, layer, slot_first, nslots, q, k, v, row_stride, chunk_t0,
                       q_out, q_scales, stream)
+
+    def project_publish(self, layer, slot_first, nslots, x, x_row_stride, hidden, w, bias=None, q_out=None,
+                        chunk_t0=None, stream=None):
+        wf_qkv_project_publish(self.handle, layer, slot_first, nslots, x, x_row_stride, hidden, w, bias,
+                               chunk_t0, q_out, stream)
 
     def attention(self, layer, slot_first, nslots, q, out, q_scales=None, stream=None):
         import torch

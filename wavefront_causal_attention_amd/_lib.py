@@ -80,6 +80,7 @@ def load() -> ctypes.CDLL:
         "wf_pool_create_host_model": (ctypes.c_int, [ctypes.POINTER(wf_config), ctypes.POINTER(P)]),
         "wf_pool_destroy": (None, [P]),
         "wf_kv_publish": (ctypes.c_int, [P, I32, I32, I32, P, P, P, I64, P, P, P, P]),
+        "wf_qkv_project_publish": (ctypes.c_int, [P, I32, I32, I32, P, I64, I32, P, P, P, P, P]),
         "wf_attention_round": (ctypes.c_int, [P, I32, I32, I32, P, P, P, I32, P]),
         "wf_round_advance": (ctypes.c_int, [P, P]),
         "wf_round_index": (ctypes.c_int, [P, ctypes.POINTER(I64)]),
@@ -163,6 +164,17 @@ def wf_kv_publish(h, layer, slot_first, nslots, q, k, v, row_stride_elems,
                                 _stream(stream)), "wf_kv_publish", h)
 
 
+def wf_qkv_project_publish(h, layer, slot_first, nslots, x, x_row_stride_elems, hidden, w, bias=None,
+                           chunk_t0=None, q_out=None, stream=None) -> None:
+    t0 = None
+    if chunk_t0 is not None:
+        arr = (ctypes.c_int32 * len(chunk_t0))(*[int(v) for v in chunk_t0])
+        t0 = ctypes.cast(arr, ctypes.c_void_p)
+    _check(load().wf_qkv_project_publish(h, layer, slot_first, nslots, _ptr(x), int(x_row_stride_elems),
+                                         int(hidden), _ptr(w), _ptr(bias), t0, _ptr(q_out), _stream(stream)),
+           "wf_qkv_project_publish", h)
+
+
 def wf_attention_round(h, layer, slot_first, nslots, q, q_scales, out, out_dtype, stream=None) -> None:
     _check(load().wf_attention_round(h, layer, slot_first, nslots, _ptr(q), _ptr(q_scales),
                                      _ptr(out), int(out_dtype), _stream(stream)),
@@ -207,7 +219,7 @@ def wf_geometry(h):
 
 EXPORTED = [
     "wf_pool_bytes", "wf_pool_create", "wf_pool_create_host_model", "wf_pool_destroy",
-    "wf_kv_publish", "wf_attention_round", "wf_round_advance", "wf_round_index",
+    "wf_kv_publish", "wf_qkv_project_publish", "wf_attention_round", "wf_round_advance", "wf_round_index",
     "wf_schedule_chunk_ids", "wf_page_table_host", "wf_ready_mask", "wf_geometry",
     "wf_status_string", "wf_last_error",
 ]

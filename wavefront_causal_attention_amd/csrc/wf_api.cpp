@@ -479,6 +479,79 @@ int wf_kv_publish(wf_handle* h, int32_t layer, int32_t slot_first, int32_t nslot
     return WF_OK;
 }
 
+int wf_qkv_project_publish(wf_handle* h, int32_t layer, int32_t slot_first, int32_t nslots,
+                           const void* x, int64_t x_row_stride_elems, int32_t hidden, const void* w,
+                           const void* bias, const int32_t* chunk_t0_host, void* q_out, void* stream) {
+    if (!h) return WF_E_INVALID_ARG;
+    const wf_config& c = h->cfg;
+    const Layout& L = h->L;
+    if (layer < 0 || layer >= c.num_layers) return WF_E_INVALID_ARG;
+    if (nslots < 1 || slot_first < 0 || slot_first + nslots > c.S + 1) return WF_E_INVALID_ARG;
+    if (!x || !w || !q_out) return WF_E_INVALID_ARG;
+    if (hidden < 64 || hidden % 64 != 0 || x_row_stride_elems < hidden) return WF_E_INVALID_ARG;
+    if (((uintptr_t)x | (uintptr_t)w | (uintptr_t)q_out) % 16 || (x_row_stride_elems * 2) % 16 ||
+        ((uintptr_t)bias % 2))
+        return WF_E_INVALID_ARG;
+    const int hd = c.heads * c.head_dim;
+    if (c.qk_dtype != WF_DTYPE_BF16 || hd % 128 != 0) return WF_E_SHAPE;
+    if (wf::proj_frames_per_tile(c.frame_h * c.frame_w) > wf::kProjMaxFrames) return WF_E_SHAPE;
+    const int64_t xbytes = (((int64_t)nslots * L.N - 1) * x_row_stride_elems + hidden) * 2;
+    const int64_t wbytes = (int64_t)3 * hd * hidden * 2;
+    if (xbytes >= ((int64_t)1 << 31) || wbytes >= ((int64_t)1 << 31)) return WF_E_SHAPE;
+    for (int i = 0; i < nslots; ++i)
+        if (!h->present(h->position_of_slot(slot_first + i))) {
+            snprintf(h->err, sizeof h->err, "slot %d holds no chunk in round %lld", slot_first + i,
+                     (long long)h->round());
+            return WF_E_INVALID_ARG;
+        }
+    wf::ProjArgs a{};
+    for (int i = 0; i < nslots; ++i) {
+        const int64_t t0 = chunk_t0_host
+                               ? (int64_t)chunk_t0_host[i]
+                               : (int64_t)c.chunk_frames * h->chunk_at(h->position_of_slot(slot_first + i));
+        if (t0 < 0 || t0 > INT32_MAX / 2) return WF_E_INVALID_ARG;
+        a.t0[i] = (int)t0;
+    }
+    if (!h->host_model) {
+        a.x = (const uint16_t*)x;
+        a.x_stride = x_row_stride_elems;
+        a.xbytes = (int32_t)xbytes;
+        a.w = (const uint16_t*)w;
+        a.wbytes = (int32_t)wbytes;
+        a.bias = (const uint16_t*)bias;
+        a.q_out = q_out;
+        a.kpage = h->pool + L.k_off + L.k_layer * layer;
+        a.vpage = (uint16_t*)(h->pool + L.v_off + L.v_layer * layer);
+        a.table = h->table;
+        a.htab = (const float2*)(h->pool + L.htab_off);
+        a.wtab = (const float2*)(h->pool + L.wtab_off);
+        a.omega_t = (const double*)(h->pool + L.omega_off);
+        a.N = L.N; a.heads = c.heads; a.D = c.head_dim; a.pt = c.page_tokens; a.ppc = L.ppc;
+        a.T = L.T; a.hidden = hidden;
+        a.frame_h = c.frame_h; a.frame_w = c.frame_w;
+        a.dt = c.rope_split[0]; a.dh = c.rope_split[1]; a.dw = c.rope_split[2];
+        a.slot_first = slot_first; a.nslots = nslots;
+        a.mtiles = (L.N + wf::kProjTokens - 1) / wf::kProjTokens;
+        a.ctiles = 3 * hd / 128;
+        a.mrows = nslots * a.mtiles;
+        // each XCD takes one block of (channel-tile group x token-row group), so
+        // its L2 holds a slice of w and the x rows it is working on
+        a.g_ct = a.ctiles >= 4 ? 4 : (a.ctiles >= 2 ? 2 : 1);
+        a.g_mt = wf::kXcds / a.g_ct;
+        int per = 0;
+        for (int xc = 0; xc < wf::kXcds; ++xc) {
+            const int cg = xc % a.g_ct, mg = xc / a.g_ct;
+            const int nc = (cg + 1) * a.ctiles / a.g_ct - cg * a.ctiles / a.g_ct;
+            const int nr = (mg + 1) * a.mrows / a.g_mt - mg * a.mrows / a.g_mt;
+            per = std::max(per, nc * nr);
+        }
+        const hipError_t e = wf::launch_project(a, per * wf::kXcds, (hipStream_t)stream);
+        if (e != hipSuccess) return h->fail_hip(e, "wf_qkv_project_publish launch");
+    }
+    for (int i = 0; i < nslots; ++i) h->ready[layer] |= 1ull << h->position_of_slot(slot_first + i);
+    return WF_OK;
+}
+
 int wf_attention_round(wf_handle* h, int32_t layer, int32_t slot_first, int32_t nslots,
                        const void* q, const float* q_scales, void* out, int32_t out_dtype,
                        void* stream) {

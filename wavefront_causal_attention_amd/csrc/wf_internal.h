@@ -94,6 +94,37 @@ struct AttnArgs {
     float scale_log2;         // log2(e) / sqrt(D)
 };
 
+// QKV projection with RoPE + publish as its epilogue (bf16 pools), for
+// `nslots` consecutive live slots of one layer.
+constexpr int kProjTokens = 256;     // tokens per projection workgroup tile
+constexpr int kProjMaxFrames = 32;   // latent frames one tile may touch (time table in LDS)
+struct ProjArgs {
+    const uint16_t* x;        // hidden states [nslots * N][x_stride] bf16
+    int64_t x_stride;         // elements between token rows
+    int32_t xbytes;           // bytes readable from x (< 2^31)
+    const uint16_t* w;        // weight [3 * heads * D][hidden] bf16 ([out][in])
+    int32_t wbytes;           // bytes of w (< 2^31)
+    const uint16_t* bias;     // [3 * heads * D] bf16, or NULL
+    void* q_out;              // [S+1][heads][N][D] bf16
+    void* kpage;              // this layer's K pages
+    uint16_t* vpage;          // this layer's V pages
+    const int32_t* table;     // page table [T][ppc]
+    const float2* htab;       // RoPE row-axis (cos, sin) [frame_h][dh/2]
+    const float2* wtab;       // RoPE column-axis (cos, sin) [frame_w][dw/2]
+    const double* omega_t;    // RoPE time-axis frequencies [dt/2]
+    int N, heads, D, pt, ppc, T, hidden;
+    int frame_h, frame_w;
+    int dt, dh, dw;
+    int slot_first, nslots;
+    int mtiles;               // token tiles per chunk
+    int ctiles;               // 128-channel tiles of the 3 * heads * D outputs
+    int mrows;                // nslots * mtiles
+    int g_ct, g_mt;           // XCD blocking: channel-tile groups x token-row groups = 8
+    int t0[kMaxSlots];        // RoPE time offset per slot
+};
+int proj_frames_per_tile(int hw);
+hipError_t launch_project(const ProjArgs& a, int nblocks, hipStream_t st);
+
 hipError_t launch_page_table(int32_t* table, int T, int A, int ppc, int64_t ring, int store_pos,
                              int store_anchor, hipStream_t st);
 hipError_t launch_publish(const PublishArgs& a, bool fp8, hipStream_t st);

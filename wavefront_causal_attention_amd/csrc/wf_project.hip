@@ -1,0 +1,334 @@
+// QKV projection with RoPE and publish as its epilogue, gfx950: bf16 MFMA.
+//
+// The pages publish K/V right after the QKV projection and RoPE (Wave
+// Forcing, hyper.ai summary, section "Method", WaveRT paragraph; e-cogni.com.br,
+// "Como funciona"); the projection maps the hidden state (heads x 128 wide,
+// thelatestinai.com listing, Table 11) to [Q | K | V]. Here the projection
+// output never goes to memory: each workgroup's accumulators are rotated and
+// written straight into the Q buffer and the K/V pages of the slot's context
+// position, in the same formats the publish kernel writes.
+//
+//   qkv[n][o] = sum_c x[n][c] * w[o][c] + b[o]      (w in [out][in] layout)
+//
+// Workgroup tile: 256 tokens of one slot's chunk x 128 output channels, which
+// lie wholly inside Q, K or V (h*d is a multiple of 128). 8 waves, each 64
+// tokens x 64 channels as 2 x 2 blocks of v_mfma_f32_32x32x16_bf16.
+//   Q and K tiles compute the transposed block C^T[channel][token], so a lane
+//   holds one token and runs of 4 consecutive channels: the RoPE pairs
+//   (2m, 2m+1) are in-lane, and a lane pair (l, l+32) holds 8 consecutive
+//   channels, i.e. one 16-byte K page vector.
+//   V tiles compute C[token][channel], so a lane holds one channel and runs of
+//   4 consecutive tokens: a lane pair holds 8 consecutive tokens of one
+//   channel, i.e. one 16-byte V page vector.
+// Both orientations read the same LDS fragments (16 bytes = 8 consecutive
+// hidden channels of one row of x or w) and only swap the MFMA operands.
+//
+// Operands arrive by LDS DMA in 64-channel stages through a 3-stage ring. A
+// stage holds rows of 128 bytes; 16-byte vector kv of row r sits in slot
+// kv ^ ((r >> 1) & 7), so that each DMA instruction reads eight whole rows
+// (eight 128-byte lines of x or w) and the fragment reads of 16 lanes (16
+// consecutive rows, one kv) fall on 16 distinct 16-byte bank groups.
+#include <hip/hip_runtime.h>
+
+#include <type_traits>
+
+#include "wf_internal.h"
+
+namespace wf {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+constexpr int PM = kProjTokens;   // tokens per workgroup tile
+constexpr int PC = 128;           // output channels per workgroup tile
+constexpr int BK = 64;            // hidden channels per stage
+constexpr int PNT = 512;          // threads per workgroup (8 waves)
+constexpr int XI = PM / 8 / 8;    // x DMA instructions per wave per stage (8 rows each)
+constexpr int WI = PC / 8 / 8;    // w DMA instructions per wave per stage
+// Buffer offset past every region (each is under 2^31 bytes): loads zeros.
+// The per-stage addend is below 2^31 too, so kOOB plus it stays out of range.
+constexpr uint32_t kOOB = 0x80000000u;
+
+__shared__ __align__(16) uint16_t g_px0[PM * BK];
+__shared__ __align__(16) uint16_t g_px1[PM * BK];
+__shared__ __align__(16) uint16_t g_px2[PM * BK];
+__shared__ __align__(16) uint16_t g_pw0[PC * BK];
+__shared__ __align__(16) uint16_t g_pw1[PC * BK];
+__shared__ __align__(16) uint16_t g_pw2[PC * BK];
+// time-axis (cos, sin) of every frame the tile touches: [frame][32]
+extern __shared__ float2 g_pttab[];
+
+template <int I>
+__device__ __forceinline__ uint16_t* xbuf() {
+    if constexpr (I == 0) return g_px0;
+    else if constexpr (I == 1) return g_px1;
+    else return g_px2;
+}
+template <int I>
+__device__ __forceinline__ uint16_t* wbuf() {
+    if constexpr (I == 0) return g_pw0;
+    else if constexpr (I == 1) return g_pw1;
+    else return g_pw2;
+}
+
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        static_for<I + 1, N>(f);
+    }
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmem_n() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
+// All LDS DMA of the stage about to be read has landed in every wave (each
+// wave waited for its own before): a bare barrier orders the buffers.
+__device__ __forceinline__ void stage_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, const void* lds, uint32_t voff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds, 16, voff, 0, 0, 0);
+}
+
+// byte offset of 16-byte vector kv of row r inside a stage
+__device__ __forceinline__ int swz(int r, int kv) { return r * 128 + ((kv ^ ((r >> 1) & 7)) << 4); }
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+    bf2 r = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, r);
+}
+__device__ __forceinline__ float bf_to_f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+template <int D>
+__global__ __launch_bounds__(PNT, 1) void proj_publish_kernel(ProjArgs a) {
+    // ---- which tile: XCD x takes a block of (token-tile rows x channel tiles)
+    const int xcd = blockIdx.x % kXcds, j = blockIdx.x / kXcds;
+    const int cg = xcd % a.g_ct, mg = xcd / a.g_ct;
+    const int c_lo = cg * a.ctiles / a.g_ct, c_hi = (cg + 1) * a.ctiles / a.g_ct;
+    const int r_lo = mg * a.mrows / a.g_mt, r_hi = (mg + 1) * a.mrows / a.g_mt;
+    const int nc = c_hi - c_lo;
+    if (nc <= 0) return;
+    const int row = r_lo + j / nc;
+    if (row >= r_hi) return;                       // padding of the per-XCD ranges
+    const int ct = c_lo + j % nc;
+    const int sr = row / a.mtiles, mt = row - sr * a.mtiles;
+    const int s = a.slot_first + sr;
+    const int N = a.N, hd = a.heads * D;
+    const int kind = ct * PC / hd;                 // 0 Q, 1 K, 2 V (uniform)
+    const int n0 = mt * PM;
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
+    const int wm = wave & 3, wc = wave >> 2;       // 64-token and 64-channel block of this wave
+
+    const __amdgpu_buffer_rsrc_t xrs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.x), (short)0, a.xbytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t wrs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.w), (short)0, a.wbytes, 0x00020000);
+
+    // ---- time-axis table (Q and K tiles): frequencies loaded and waited for
+    // before any DMA, so the DMA wait counts below stay exact; the fp64 sincos
+    // then runs while the first stages are in flight
+    const int HW = a.frame_h * a.frame_w;
+    const int f_lo = n0 / HW;
+    const int nf = (min(n0 + PM, N) - 1) / HW - f_lo + 1;
+    const int hp = a.dt >> 1;
+    const bool rope = kind < 2;
+    // entries tid and tid + PNT of the [frame][pair] table (at most
+    // kProjMaxFrames x 32 = 2 x PNT entries, checked on the host)
+    double om[2] = {0.0, 0.0};
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+        const int idx = tid + e * PNT;
+        if (rope && idx < nf * hp) om[e] = a.omega_t[idx % hp];
+    }
+    wait_vmem_n<0>();
+
+    // ---- DMA offsets: lane covers vector (lane % 8) of row (lane / 8) of each
+    // 8-row instruction; the vector it fetches is the one that slot holds
+    uint32_t xoff[XI], woff[WI];
+#pragma unroll
+    for (int i = 0; i < XI; ++i) {
+        const int r = (wave * XI + i) * 8 + (lane >> 3);
+        const int kv = (lane & 7) ^ ((r >> 1) & 7);
+        const int n = n0 + r;
+        xoff[i] = n < N ? (uint32_t)((((int64_t)sr * N + n) * a.x_stride + kv * 8) * 2) : kOOB;
+    }
+#pragma unroll
+    for (int i = 0; i < WI; ++i) {
+        const int r = (wave * WI + i) * 8 + (lane >> 3);
+        const int kv = (lane & 7) ^ ((r >> 1) & 7);
+        woff[i] = (uint32_t)((((int64_t)ct * PC + r) * a.hidden + kv * 8) * 2);
+    }
+    auto dma_stage = [&](auto I, int kt) {
+        constexpr int B = decltype(I)::value;
+        const uint32_t kb = (uint32_t)kt * BK * 2;
+        uint8_t* xl = reinterpret_cast<uint8_t*>(xbuf<B>());
+        uint8_t* wl = reinterpret_cast<uint8_t*>(wbuf<B>());
+#pragma unroll
+        for (int i = 0; i < XI; ++i) dma16(xrs, xl + (wave * XI + i) * 1024, xoff[i] + kb);
+#pragma unroll
+        for (int i = 0; i < WI; ++i) dma16(wrs, wl + (wave * WI + i) * 1024, woff[i] + kb);
+    };
+    const int nk = a.hidden / BK;
+    dma_stage(std::integral_constant<int, 0>{}, 0);
+    if (nk > 1) dma_stage(std::integral_constant<int, 1>{}, 1);
+
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+        const int idx = tid + e * PNT;
+        if (rope && idx < nf * hp) {
+            const int fi = idx / hp, m = idx - fi * hp;
+            double sn, cs;
+            sincos((double)(a.t0[sr] + f_lo + fi) * om[e], &sn, &cs);
+            g_pttab[fi * 32 + m] = make_float2((float)cs, (float)sn);
+        }
+    }
+
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][jj][e] = 0.f;
+
+    // TR: the transposed block C^T[channel][token] (Q and K tiles)
+    auto compute_stage = [&](auto I, auto TR) {
+        constexpr int B = decltype(I)::value;
+        const uint8_t* xl = reinterpret_cast<const uint8_t*>(xbuf<B>());
+        const uint8_t* wl = reinterpret_cast<const uint8_t*>(wbuf<B>());
+#pragma unroll
+        for (int ks = 0; ks < BK / 16; ++ks) {
+            const int kv = ks * 2 + hf;
+            bf16x8 xf[2], wf_[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+                xf[i] = *reinterpret_cast<const bf16x8*>(xl + swz(wm * 64 + i * 32 + l32, kv));
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj)
+                wf_[jj] = *reinterpret_cast<const bf16x8*>(wl + swz(wc * 64 + jj * 32 + l32, kv));
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int jj = 0; jj < 2; ++jj)
+                    if constexpr (decltype(TR)::value)
+                        acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf_[jj], xf[i], acc[i][jj], 0, 0, 0);
+                    else
+                        acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xf[i], wf_[jj], acc[i][jj], 0, 0, 0);
+        }
+    };
+
+    auto kloop = [&](auto TR) {
+        for (int kt0 = 0; kt0 < nk; kt0 += 3) {
+            static_for<0, 3>([&](auto I) {
+                constexpr int B = decltype(I)::value;
+                const int kt = kt0 + B;
+                if (kt < nk) {
+                    if (kt + 1 < nk) wait_vmem_n<XI + WI>();   // the next stage may still be in flight
+                    else wait_vmem_n<0>();
+                    stage_barrier();
+                    if (kt + 2 < nk) dma_stage(std::integral_constant<int, (B + 2) % 3>{}, kt + 2);
+                    compute_stage(I, TR);
+                }
+            });
+        }
+    };
+    if (rope) kloop(std::true_type{});
+    else kloop(std::false_type{});
+    __syncthreads();                               // time-axis table visible (nk may be 1)
+
+    // ---- epilogue: bias, RoPE (Q, K), bf16, straight into Q buffer / pages
+    const int p = a.T - 1 - s;                     // context position of slot s
+    const int pt = a.pt;
+    const int ob = ct * PC;                        // first output channel of the tile
+    if (rope) {
+        const int cb = ob - kind * hd;             // first channel of the tile inside Q or K
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int n = n0 + wm * 64 + i * 32 + l32;
+            if (n >= N) continue;
+            const int f = n / HW;
+            const int yy = (n / a.frame_w) % a.frame_h;
+            const int xw = n % a.frame_w;
+            const int pg = n / pt, tok = n - pg * pt;
+            const int64_t phys = kind == 1 ? (int64_t)a.table[p * a.ppc + pg] : 0;
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int cl = wc * 64 + jj * 32 + 8 * g + 4 * hf;     // 4 consecutive channels
+                    const int cq = cb + cl;
+                    const int head = cq / D, d0 = cq - head * D;
+                    float v[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        v[e] = acc[i][jj][4 * g + e] + (a.bias ? bf_to_f(a.bias[ob + cl + e]) : 0.f);
+#pragma unroll
+                    for (int pr = 0; pr < 2; ++pr) {
+                        const int dc = d0 + 2 * pr;
+                        float2 c2;
+                        if (dc < a.dt) c2 = g_pttab[(f - f_lo) * 32 + (dc >> 1)];
+                        else if (dc < a.dt + a.dh) c2 = a.htab[yy * (a.dh >> 1) + ((dc - a.dt) >> 1)];
+                        else c2 = a.wtab[xw * (a.dw >> 1) + ((dc - a.dt - a.dh) >> 1)];
+                        const float x0 = v[2 * pr], x1 = v[2 * pr + 1];
+                        v[2 * pr] = fmaf(x0, c2.x, -x1 * c2.y);
+                        v[2 * pr + 1] = fmaf(x0, c2.y, x1 * c2.x);
+                    }
+                    const uint2 o2 = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+                    if (kind == 0) {
+                        uint16_t* qp = static_cast<uint16_t*>(a.q_out) +
+                                       (((int64_t)s * a.heads + head) * N + n) * D + d0;
+                        *reinterpret_cast<uint2*>(qp) = o2;
+                    } else {
+                        const int64_t base = (phys * a.heads + head) * pt * D;
+                        uint16_t* kp = static_cast<uint16_t*>(a.kpage) + base + ((int64_t)(d0 >> 3) * pt + tok) * 8 + (d0 & 7);
+                        *reinterpret_cast<uint2*>(kp) = o2;
+                    }
+                }
+        }
+    } else {
+        const int cb = ob - 2 * hd;
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+            const int cl = wc * 64 + jj * 32 + l32;                        // one channel
+            const int cv = cb + cl;
+            const int head = cv / D, d = cv - head * D;
+            const float bb = a.bias ? bf_to_f(a.bias[ob + cl]) : 0.f;
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int n = n0 + wm * 64 + i * 32 + 8 * g + 4 * hf;   // 4 consecutive tokens
+                    if (n >= N) continue;              // N is a multiple of 8: all 4 or none
+                    const int pg = n / pt, tok = n - pg * pt;
+                    const int64_t phys = a.table[p * a.ppc + pg];
+                    const int64_t base = (phys * a.heads + head) * pt * D;
+                    const uint2 o2 = make_uint2(pack_bf16x2(acc[i][jj][4 * g] + bb, acc[i][jj][4 * g + 1] + bb),
+                                                pack_bf16x2(acc[i][jj][4 * g + 2] + bb, acc[i][jj][4 * g + 3] + bb));
+                    uint16_t* vp = a.vpage + base + ((int64_t)(tok >> 3) * D + d) * 8 + (tok & 7);
+                    *reinterpret_cast<uint2*>(vp) = o2;
+                }
+        }
+    }
+}
+
+}  // namespace
+
+int proj_frames_per_tile(int hw) { return (PM - 1) / hw + 2; }
+
+hipError_t launch_project(const ProjArgs& a, int nblocks, hipStream_t st) {
+    const size_t tbytes = (size_t)proj_frames_per_tile(a.frame_h * a.frame_w) * 32 * sizeof(float2);
+    if (a.D == 128)
+        hipLaunchKernelGGL((proj_publish_kernel<128>), dim3(nblocks), dim3(PNT), tbytes, st, a);
+    else if (a.D == 64)
+        hipLaunchKernelGGL((proj_publish_kernel<64>), dim3(nblocks), dim3(PNT), tbytes, st, a);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+}  // namespace wf
