@@ -71,6 +71,9 @@ def parse():
     ap.add_argument("--layers", type=int, default=1,
                     help="layers sharing one pool and page table; a step is then one model round "
                          "(publish + attention of every layer, one advance)")
+    ap.add_argument("--project", action="store_true",
+                    help="publish through the fused QKV projection (hidden states -> RoPE'd Q/K/V pages) "
+                         "instead of from a projection output; also times hipBLASLt addmm + publish")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=1536, help="query rows per (slot, head) in the CPU sample")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -131,6 +134,12 @@ def main():
     q = pool.q_buffer()
     qs = pool.q_scale_buffer()
     out = pool.out_buffer(args.out_dtype)
+    if args.project:
+        assert w.qk_dtype == "bf16", "the fused projection publishes bf16 pages"
+        xh = to_dev([W.draw_hidden(w, k0, s) for s in range(w.S + 1)]).to(torch.bfloat16)
+        wt_np, b_np = W.projection_weights(w)
+        wproj = torch.from_numpy(wt_np).to(torch.bfloat16).to(dev)            # [3hd, hidden]
+        bproj = torch.from_numpy(b_np).to(torch.bfloat16).to(dev)
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()
@@ -141,7 +150,10 @@ def main():
         for layer in range(L):
             if ev is not None and layer == 0:
                 ev[0].record(stream)
-            pool.publish(layer, 0, w.S + 1, qd, kd, vd, stride, q_out=q, q_scales=qs, stream=stream)
+            if args.project:
+                pool.project_publish(layer, 0, w.S + 1, xh, w.hd, w.hd, wproj, bproj, q_out=q, stream=stream)
+            else:
+                pool.publish(layer, 0, w.S + 1, qd, kd, vd, stride, q_out=q, q_scales=qs, stream=stream)
             if ev is not None and layer == 0:
                 ev[1].record(stream)
             pool.attention(layer, 0, w.S + 1, q, out, q_scales=qs, stream=stream)
@@ -180,6 +192,36 @@ def main():
     pub_bytes = in_bytes + 2 * n_el * qk_bytes + 2 * n_el            # read QKV; write Q, K, V
     attn_tflops = w.attention_flops() / (att_avg * 1e-3) / 1e12
     traffic = measured_traffic()
+
+    proj = None
+    if args.project:
+        # the same projection unfused: hipBLASLt addmm to a [tokens, 3hd] bf16
+        # output, then the publish kernel reads it back
+        wT = wproj.t().contiguous()                                   # [hidden, 3hd]
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        mm, pb = [], []
+        for i in range(K + 2):
+            ev[0].record(stream)
+            y = torch.addmm(bproj, xh, wT)
+            ev[1].record(stream)
+            pool.publish(0, 0, w.S + 1, y[:, :w.hd], y[:, w.hd:2 * w.hd], y[:, 2 * w.hd:], 3 * w.hd,
+                         q_out=q, stream=stream)
+            ev[2].record(stream)
+            torch.cuda.synchronize()
+            if i >= 2:
+                mm.append(ev[0].elapsed_time(ev[1]))
+                pb.append(ev[1].elapsed_time(ev[2]))
+        pf = 2.0 * (w.S + 1) * w.N * 3 * w.hd * w.hd
+        fused_ms = float(np.mean(pub_ms))
+        proj = {"fused_ms": round(fused_ms, 4),
+                "fused_tflops": round(pf / (fused_ms * 1e-3) / 1e12, 1),
+                "roofline": {"bound": "mfma", "achieved": round(pf / (fused_ms * 1e-3) / 1e12, 1),
+                             "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                             "frac": round(pf / (fused_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)},
+                "flops": pf,
+                "unfused_addmm_ms": round(float(np.mean(mm)), 4),
+                "unfused_publish_ms": round(float(np.mean(pb)), 4),
+                "unfused_ms": round(float(np.mean(mm)) + float(np.mean(pb)), 4)}
 
     if args.calibrate_copy_mib > 0:
         nb = args.calibrate_copy_mib * (1 << 20)
@@ -227,6 +269,11 @@ def main():
                              "frac": round(pub_bytes / (pub_avg * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
                              "algorithmic_bytes": pub_bytes},
     }
+    if proj is not None:
+        res["projection"] = proj
+        res["config"]["publish"] = "fused QKV projection + RoPE + publish"
+        del res["publish_roofline"]
+        del res["publish_gbps"]
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_rows)
     print(json.dumps(res), flush=True)

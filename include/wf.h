@@ -172,7 +172,7 @@ int wf_kv_publish(wf_handle* h, int32_t layer, int32_t slot_first, int32_t nslot
  * w:      device bf16 [3*heads*head_dim][hidden], output channel o's weights
  *         contiguous (the [out][in] layout of a linear layer); outputs
  *         [0, h*d) are Q, [h*d, 2h*d) K, [2h*d, 3h*d) V, head-major.
- * bias:   device bf16 [3*heads*head_dim], or NULL.
+ * bias:   device bf16 [3*heads*head_dim], 16-byte aligned, or NULL.
  * chunk_t0_host, q_out: as for wf_kv_publish (q_out required, bf16).
  * Only live slots (slot_first + nslots <= S+1). WF_E_SHAPE for fp8 pools,
  * heads*head_dim not a multiple of 128, a frame smaller than 1/32 of a

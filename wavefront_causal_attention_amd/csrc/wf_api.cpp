@@ -490,11 +490,13 @@ int wf_qkv_project_publish(wf_handle* h, int32_t layer, int32_t slot_first, int3
     if (!x || !w || !q_out) return WF_E_INVALID_ARG;
     if (hidden < 64 || hidden % 64 != 0 || x_row_stride_elems < hidden) return WF_E_INVALID_ARG;
     if (((uintptr_t)x | (uintptr_t)w | (uintptr_t)q_out) % 16 || (x_row_stride_elems * 2) % 16 ||
-        ((uintptr_t)bias % 2))
+        ((uintptr_t)bias % 16))
         return WF_E_INVALID_ARG;
     const int hd = c.heads * c.head_dim;
     if (c.qk_dtype != WF_DTYPE_BF16 || hd % 128 != 0) return WF_E_SHAPE;
     if (wf::proj_frames_per_tile(c.frame_h * c.frame_w) > wf::kProjMaxFrames) return WF_E_SHAPE;
+    if (c.frame_h * (c.rope_split[1] / 2) + c.frame_w * (c.rope_split[2] / 2) > wf::kProjMaxRopeEntries)
+        return WF_E_SHAPE;
     const int64_t xbytes = (((int64_t)nslots * L.N - 1) * x_row_stride_elems + hidden) * 2;
     const int64_t wbytes = (int64_t)3 * hd * hidden * 2;
     if (xbytes >= ((int64_t)1 << 31) || wbytes >= ((int64_t)1 << 31)) return WF_E_SHAPE;

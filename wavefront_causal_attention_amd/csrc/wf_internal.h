@@ -98,6 +98,7 @@ struct AttnArgs {
 // `nslots` consecutive live slots of one layer.
 constexpr int kProjTokens = 256;     // tokens per projection workgroup tile
 constexpr int kProjMaxFrames = 32;   // latent frames one tile may touch (time table in LDS)
+constexpr int kProjMaxRopeEntries = 4096;  // frame_h*dh/2 + frame_w*dw/2 (row/column tables in LDS)
 struct ProjArgs {
     const uint16_t* x;        // hidden states [nslots * N][x_stride] bf16
     int64_t x_stride;         // elements between token rows

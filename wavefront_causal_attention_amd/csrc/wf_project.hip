@@ -57,8 +57,11 @@ __shared__ __align__(16) uint16_t g_px2[PM * BK];
 __shared__ __align__(16) uint16_t g_pw0[PC * BK];
 __shared__ __align__(16) uint16_t g_pw1[PC * BK];
 __shared__ __align__(16) uint16_t g_pw2[PC * BK];
-// time-axis (cos, sin) of every frame the tile touches: [frame][32]
-extern __shared__ float2 g_pttab[];
+// time-axis (cos, sin) of every frame the tile touches: [frame][32]. Static,
+// like the stage buffers: with only static LDS the compiler can tell each
+// DMA target from the stage being read and does not drain the DMA queue
+// before the fragment reads.
+__shared__ float2 g_pttab[kProjMaxFrames * 32];
 
 template <int I>
 __device__ __forceinline__ uint16_t* xbuf() {
@@ -145,6 +148,16 @@ __global__ __launch_bounds__(PNT, 1) void proj_publish_kernel(ProjArgs a) {
         const int idx = tid + e * PNT;
         if (rope && idx < nf * hp) om[e] = a.omega_t[idx % hp];
     }
+    // row- and column-axis (cos, sin) tables, copied to LDS after the main
+    // loop (kProjMaxRopeEntries entries at most, checked on the host): loaded
+    // here, coalesced, so their latency hides behind the first stage
+    const int nh = a.frame_h * (a.dh >> 1), nrope = nh + a.frame_w * (a.dw >> 1);
+    float2 rt[kProjMaxRopeEntries / PNT];
+#pragma unroll
+    for (int e = 0; e < kProjMaxRopeEntries / PNT; ++e) {
+        const int idx = tid + e * PNT;
+        rt[e] = (rope && idx < nrope) ? (idx < nh ? a.htab[idx] : a.wtab[idx - nh]) : make_float2(0.f, 0.f);
+    }
     wait_vmem_n<0>();
 
     // ---- DMA offsets: lane covers vector (lane % 8) of row (lane / 8) of each
@@ -196,30 +209,41 @@ __global__ __launch_bounds__(PNT, 1) void proj_publish_kernel(ProjArgs a) {
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][jj][e] = 0.f;
 
-    // TR: the transposed block C^T[channel][token] (Q and K tiles)
-    auto compute_stage = [&](auto I, auto TR) {
+    // One stage: every fragment read of the stage is issued first, then the
+    // DMA of stage kt+2 (a different buffer), then the 16 MFMAs. With the
+    // reads ahead of the DMA in program order the compiler has no DMA write
+    // to wait for before them, and their latency overlaps the DMA issue and
+    // the other wave's MFMAs.
+    // TR: the transposed block C^T[channel][token] (Q and K tiles).
+    auto stage = [&](auto I, auto TR, int kt) {
         constexpr int B = decltype(I)::value;
         const uint8_t* xl = reinterpret_cast<const uint8_t*>(xbuf<B>());
         const uint8_t* wl = reinterpret_cast<const uint8_t*>(wbuf<B>());
+        bf16x8 xf[BK / 16][2], wf_[BK / 16][2];
 #pragma unroll
         for (int ks = 0; ks < BK / 16; ++ks) {
             const int kv = ks * 2 + hf;
-            bf16x8 xf[2], wf_[2];
 #pragma unroll
             for (int i = 0; i < 2; ++i)
-                xf[i] = *reinterpret_cast<const bf16x8*>(xl + swz(wm * 64 + i * 32 + l32, kv));
+                xf[ks][i] = *reinterpret_cast<const bf16x8*>(xl + swz(wm * 64 + i * 32 + l32, kv));
 #pragma unroll
             for (int jj = 0; jj < 2; ++jj)
-                wf_[jj] = *reinterpret_cast<const bf16x8*>(wl + swz(wc * 64 + jj * 32 + l32, kv));
+                wf_[ks][jj] = *reinterpret_cast<const bf16x8*>(wl + swz(wc * 64 + jj * 32 + l32, kv));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (kt + 2 < nk) dma_stage(std::integral_constant<int, (B + 2) % 3>{}, kt + 2);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int ks = 0; ks < BK / 16; ++ks)
 #pragma unroll
             for (int i = 0; i < 2; ++i)
 #pragma unroll
-                for (int jj = 0; jj < 2; ++jj)
+                for (int jj = 0; jj < 2; ++jj) {
                     if constexpr (decltype(TR)::value)
-                        acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf_[jj], xf[i], acc[i][jj], 0, 0, 0);
+                        acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf_[ks][jj], xf[ks][i], acc[i][jj], 0, 0, 0);
                     else
-                        acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xf[i], wf_[jj], acc[i][jj], 0, 0, 0);
-        }
+                        acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xf[ks][i], wf_[ks][jj], acc[i][jj], 0, 0, 0);
+                }
     };
 
     auto kloop = [&](auto TR) {
@@ -231,8 +255,7 @@ __global__ __launch_bounds__(PNT, 1) void proj_publish_kernel(ProjArgs a) {
                     if (kt + 1 < nk) wait_vmem_n<XI + WI>();   // the next stage may still be in flight
                     else wait_vmem_n<0>();
                     stage_barrier();
-                    if (kt + 2 < nk) dma_stage(std::integral_constant<int, (B + 2) % 3>{}, kt + 2);
-                    compute_stage(I, TR);
+                    stage(I, TR, kt);
                 }
             });
         }
@@ -241,77 +264,121 @@ __global__ __launch_bounds__(PNT, 1) void proj_publish_kernel(ProjArgs a) {
     else kloop(std::false_type{});
     __syncthreads();                               // time-axis table visible (nk may be 1)
 
-    // ---- epilogue: bias, RoPE (Q, K), bf16, straight into Q buffer / pages
+    // ---- epilogue: bias, RoPE (Q, K), bf16, then out to the Q buffer / pages.
+    // The stage buffers are free now. The RoPE row/column tables go to LDS
+    // (the column entry differs for every lane's token, a scattered read in
+    // global memory); each wave stages its 64 x 64 bf16 block in LDS in the
+    // destination's order and writes it out with 16-byte stores: 1 KB
+    // contiguous per K or V instruction, whole 128-byte row pieces for Q.
+    float2* rtab = reinterpret_cast<float2*>(g_px2);            // [frame_h][dh/2] then [frame_w][dw/2]
+    if (rope) {
+#pragma unroll
+        for (int e = 0; e < kProjMaxRopeEntries / PNT; ++e) {
+            const int idx = tid + e * PNT;
+            if (idx < nrope) rtab[idx] = rt[e];
+        }
+    }
+    __syncthreads();
     const int p = a.T - 1 - s;                     // context position of slot s
     const int pt = a.pt;
     const int ob = ct * PC;                        // first output channel of the tile
+    uint8_t* st = reinterpret_cast<uint8_t*>(wave < 4 ? g_px0 : g_px1) + (wave & 3) * 8192;
+    const int tb = n0 + wm * 64;                   // first token of this wave
     if (rope) {
-        const int cb = ob - kind * hd;             // first channel of the tile inside Q or K
+        const int cb = ob - kind * hd + wc * 64;   // first channel of this wave inside Q or K
+        // [token 64][8 x 16-byte chunks of 8 channels], chunk slot c ^ (t & 7)
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-            const int n = n0 + wm * 64 + i * 32 + l32;
-            if (n >= N) continue;
-            const int f = n / HW;
+            const int t = i * 32 + l32;
+            const int n = min(tb + t, N - 1);
+            const int f = n / HW - f_lo;
             const int yy = (n / a.frame_w) % a.frame_h;
             const int xw = n % a.frame_w;
-            const int pg = n / pt, tok = n - pg * pt;
-            const int64_t phys = kind == 1 ? (int64_t)a.table[p * a.ppc + pg] : 0;
 #pragma unroll
             for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
-                    const int cl = wc * 64 + jj * 32 + 8 * g + 4 * hf;     // 4 consecutive channels
-                    const int cq = cb + cl;
-                    const int head = cq / D, d0 = cq - head * D;
+                    const int cl = jj * 32 + 8 * g + 4 * hf;                // 4 consecutive channels
+                    const int d0 = (cb + cl) % D;
+                    const uint2 bq = a.bias ? *reinterpret_cast<const uint2*>(a.bias + ob + wc * 64 + cl)
+                                            : make_uint2(0, 0);
                     float v[4];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        v[e] = acc[i][jj][4 * g + e] + (a.bias ? bf_to_f(a.bias[ob + cl + e]) : 0.f);
+                    v[0] = acc[i][jj][4 * g + 0] + __uint_as_float(bq.x << 16);
+                    v[1] = acc[i][jj][4 * g + 1] + __uint_as_float(bq.x & 0xFFFF0000u);
+                    v[2] = acc[i][jj][4 * g + 2] + __uint_as_float(bq.y << 16);
+                    v[3] = acc[i][jj][4 * g + 3] + __uint_as_float(bq.y & 0xFFFF0000u);
 #pragma unroll
                     for (int pr = 0; pr < 2; ++pr) {
                         const int dc = d0 + 2 * pr;
                         float2 c2;
-                        if (dc < a.dt) c2 = g_pttab[(f - f_lo) * 32 + (dc >> 1)];
-                        else if (dc < a.dt + a.dh) c2 = a.htab[yy * (a.dh >> 1) + ((dc - a.dt) >> 1)];
-                        else c2 = a.wtab[xw * (a.dw >> 1) + ((dc - a.dt - a.dh) >> 1)];
+                        if (dc < a.dt) c2 = g_pttab[f * 32 + (dc >> 1)];
+                        else if (dc < a.dt + a.dh) c2 = rtab[yy * (a.dh >> 1) + ((dc - a.dt) >> 1)];
+                        else c2 = rtab[nh + xw * (a.dw >> 1) + ((dc - a.dt - a.dh) >> 1)];
                         const float x0 = v[2 * pr], x1 = v[2 * pr + 1];
                         v[2 * pr] = fmaf(x0, c2.x, -x1 * c2.y);
                         v[2 * pr + 1] = fmaf(x0, c2.y, x1 * c2.x);
                     }
-                    const uint2 o2 = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
-                    if (kind == 0) {
-                        uint16_t* qp = static_cast<uint16_t*>(a.q_out) +
-                                       (((int64_t)s * a.heads + head) * N + n) * D + d0;
-                        *reinterpret_cast<uint2*>(qp) = o2;
-                    } else {
-                        const int64_t base = (phys * a.heads + head) * pt * D;
-                        uint16_t* kp = static_cast<uint16_t*>(a.kpage) + base + ((int64_t)(d0 >> 3) * pt + tok) * 8 + (d0 & 7);
-                        *reinterpret_cast<uint2*>(kp) = o2;
-                    }
+                    const int chunk = jj * 4 + g;
+                    *reinterpret_cast<uint2*>(st + t * 128 + ((chunk ^ (t & 7)) << 4) + hf * 8) =
+                        make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
                 }
         }
+        if (kind == 0) {
+            // Q [s][head][n][D]: 8 lanes per token write its 64 channels (128 bytes)
+#pragma unroll
+            for (int it = 0; it < 8; ++it) {
+                const int t = it * 8 + (lane >> 3), chunk = lane & 7;
+                const uint4 val = *reinterpret_cast<const uint4*>(st + t * 128 + ((chunk ^ (t & 7)) << 4));
+                const int n = tb + t;
+                if (n >= N) continue;
+                const int c = cb + chunk * 8;
+                const int head = c / D, d = c - head * D;
+                *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.q_out) +
+                                          (((int64_t)s * a.heads + head) * N + n) * D + d) = val;
+            }
+        } else {
+            // K pages [phys][head][D/8][pt][8]: one lane per token, one 8-channel vector per store
+            const int n = tb + lane;
+            const int tok = n % pt;
+            const int64_t phys = a.table[p * a.ppc + min(n, N - 1) / pt];
+#pragma unroll
+            for (int v8 = 0; v8 < 8; ++v8) {
+                const uint4 val = *reinterpret_cast<const uint4*>(st + lane * 128 + ((v8 ^ (lane & 7)) << 4));
+                if (n >= N) continue;
+                const int c = cb + v8 * 8;
+                const int head = c / D, d = c - head * D;
+                *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.kpage) + (phys * a.heads + head) * pt * D +
+                                          ((int64_t)(d >> 3) * pt + tok) * 8) = val;
+            }
+        }
     } else {
-        const int cb = ob - 2 * hd;
+        const int cb = ob - 2 * hd + wc * 64;      // first channel of this wave inside V
+        // [channel 64][8 x 16-byte chunks of 8 tokens], chunk slot tg ^ (c & 7)
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj) {
-            const int cl = wc * 64 + jj * 32 + l32;                        // one channel
-            const int cv = cb + cl;
-            const int head = cv / D, d = cv - head * D;
-            const float bb = a.bias ? bf_to_f(a.bias[ob + cl]) : 0.f;
+            const int c = jj * 32 + l32;
+            const float bb = a.bias ? bf_to_f(a.bias[ob + wc * 64 + c]) : 0.f;
 #pragma unroll
             for (int i = 0; i < 2; ++i)
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
-                    const int n = n0 + wm * 64 + i * 32 + 8 * g + 4 * hf;   // 4 consecutive tokens
-                    if (n >= N) continue;              // N is a multiple of 8: all 4 or none
-                    const int pg = n / pt, tok = n - pg * pt;
-                    const int64_t phys = a.table[p * a.ppc + pg];
-                    const int64_t base = (phys * a.heads + head) * pt * D;
-                    const uint2 o2 = make_uint2(pack_bf16x2(acc[i][jj][4 * g] + bb, acc[i][jj][4 * g + 1] + bb),
-                                                pack_bf16x2(acc[i][jj][4 * g + 2] + bb, acc[i][jj][4 * g + 3] + bb));
-                    uint16_t* vp = a.vpage + base + ((int64_t)(tok >> 3) * D + d) * 8 + (tok & 7);
-                    *reinterpret_cast<uint2*>(vp) = o2;
+                    const int chunk = i * 4 + g;                            // tokens 8*chunk + 4*hf .. +3
+                    *reinterpret_cast<uint2*>(st + c * 128 + ((chunk ^ (c & 7)) << 4) + hf * 8) =
+                        make_uint2(pack_bf16x2(acc[i][jj][4 * g] + bb, acc[i][jj][4 * g + 1] + bb),
+                                   pack_bf16x2(acc[i][jj][4 * g + 2] + bb, acc[i][jj][4 * g + 3] + bb));
                 }
+        }
+        // V pages [phys][head][pt/8][D][8]: one lane per channel, one 8-token group per store
+        const int c = cb + lane;
+        const int head = c / D, d = c - head * D;
+#pragma unroll
+        for (int tg = 0; tg < 8; ++tg) {
+            const uint4 val = *reinterpret_cast<const uint4*>(st + lane * 128 + ((tg ^ (lane & 7)) << 4));
+            const int n = tb + tg * 8;
+            if (n >= N) continue;                  // N is a multiple of 8: all 8 tokens or none
+            const int tok = n % pt;
+            const int64_t phys = a.table[p * a.ppc + n / pt];
+            *reinterpret_cast<uint4*>(a.vpage + (phys * a.heads + head) * pt * D + ((int64_t)(tok >> 3) * D + d) * 8) = val;
         }
     }
 }
@@ -321,11 +388,10 @@ __global__ __launch_bounds__(PNT, 1) void proj_publish_kernel(ProjArgs a) {
 int proj_frames_per_tile(int hw) { return (PM - 1) / hw + 2; }
 
 hipError_t launch_project(const ProjArgs& a, int nblocks, hipStream_t st) {
-    const size_t tbytes = (size_t)proj_frames_per_tile(a.frame_h * a.frame_w) * 32 * sizeof(float2);
     if (a.D == 128)
-        hipLaunchKernelGGL((proj_publish_kernel<128>), dim3(nblocks), dim3(PNT), tbytes, st, a);
+        hipLaunchKernelGGL((proj_publish_kernel<128>), dim3(nblocks), dim3(PNT), 0, st, a);
     else if (a.D == 64)
-        hipLaunchKernelGGL((proj_publish_kernel<64>), dim3(nblocks), dim3(PNT), tbytes, st, a);
+        hipLaunchKernelGGL((proj_publish_kernel<64>), dim3(nblocks), dim3(PNT), 0, st, a);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();
