@@ -421,3 +421,27 @@ def test_fill_rounds_of_an_open_ended_video_reach_the_steady_state():
         if w.S in present:
             clean[sch.slot_chunk(w.S)] = tuple(live[w.S][1:])
         pool.advance()
+
+
+def test_maximum_positions_and_table_pages():
+    """T = 64 context positions and 1024 table pages (the library's limits):
+    every output of two consecutive rounds against the oracle, across an
+    advance, with all 64 readiness bits in use."""
+    w = W.WORKLOADS["max64"]
+    assert w.T == 64 and w.T * (w.N // w.page_tokens) == 1024
+    say("case max64: T = 64, 1024 pages")
+    r = RoundRunner(w)
+    r.seed_clean()
+    for i in range(2):
+        r.publish_live(live=W.draw_slots(w, r.k, range(w.S + 1)))
+        assert r.pool.ready_mask(0) == (1 << 64) - 1
+        out = r.attention("fp32")
+        ref = oracle_round(w, r.k, r.live, r.clean_for_round(), storage="bf16")
+        g = gpu_rows(out, w, np.arange(w.N))
+        assert not np.isnan(g).any()
+        mx, rel = err_stats(g, ref)
+        say("max64 round", r.k, "max_abs %.3e rel_l2 %.3e" % (mx, rel))
+        assert mx <= BF16_MAX_ABS and rel <= BF16_REL_L2
+        dev = r.pool.table.cpu().numpy().tolist()
+        assert dev == r.pool.page_table_host()
+        r.advance()

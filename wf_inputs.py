@@ -124,6 +124,13 @@ WORKLOADS = {
                            frame_h=8, frame_w=9, page_tokens=24, in_dtype="bf16", qk_dtype="bf16",
                            rope_split=_split(64), rope_theta=1e4, seed=14,
                            description="S=1, A=2, H=0, chunk 72 (1x8x9), page 24, 2x64, bf16"),
+    # Largest schedule the library takes: T = A+H+S+1 = 64 context positions
+    # (every bit of the readiness mask) and T x pages-per-chunk = 1024 pages
+    # (the attention kernel's LDS page table, full), 8192-key contexts.
+    "max64": Workload("max64", S=30, A=1, H=32, heads=2, head_dim=64, chunk_frames=2,
+                      frame_h=8, frame_w=8, page_tokens=8, in_dtype="bf16", qk_dtype="bf16",
+                      rope_split=_split(64), rope_theta=1e4, seed=17,
+                      description="S=30, A=1, H=32: T=64, chunk 128 (2x8x8), page 8 (1024 pages), 2x64"),
     # fp8 QK with chunks shorter than one 64-key tile.
     "tiny_fp8": Workload("tiny_fp8", S=2, A=1, H=1, heads=2, head_dim=64, chunk_frames=1,
                          frame_h=6, frame_w=8, page_tokens=24, in_dtype="bf16", qk_dtype="fp8",
