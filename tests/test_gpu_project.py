@@ -180,3 +180,45 @@ def test_project_publish_full_size_sampled():
     say("attention rows", len(rows), "heads", heads, "max_abs %.3e rel_l2 %.3e" % (mx, rel))
     assert mx <= BF16_MAX_ABS and rel <= BF16_REL_L2
     assert torch.isfinite(out).all().item()
+
+
+@pytest.mark.parametrize("name,C,with_bias", [("tiny", 5, True), ("edge_s1_h0", 5, False)])
+def test_project_publish_whole_video(name, C, with_bias):
+    """Every round of a short video published through the fused projection:
+    the store's projected K/V becomes anchor or history (an anchor chunk is
+    written straight into the anchor's pages), and each occupied slot matches
+    the oracle's fill schedule over the positions that hold a chunk."""
+    from _gpu_round import config_of
+    import wavefront_causal_attention_amd as wf
+    w = W.WORKLOADS[name]
+    say("case", name, "fused projection, whole video of", C, "chunks, bias", with_bias)
+    pool = wf.Pool(config_of(w, first_round=0, total_chunks=C))
+    q = pool.q_buffer()
+    wt, b = W.projection_weights(w)
+    b = b if with_bias else None
+    wd = to_dev(wt, "bf16")
+    bd = to_dev(b, "bf16") if with_bias else None
+    clean = {}
+    for k in range(C + w.S):
+        sch = RoundSchedule(w.S, w.A, w.H, k, fill=True, total_chunks=C)
+        present = [s for s in range(w.S + 1) if sch.slot_present(s)]
+        lo, hi = present[0], present[-1]
+        xs = {s: W.draw_hidden(w, k, s) for s in present}
+        xd = to_dev(np.concatenate([xs[s] for s in present], 0), "bf16")
+        pool.project_publish(0, lo, hi - lo + 1, xd, w.hd, w.hd, wd, bd, q_out=q)
+        out = pool.out_buffer("fp32")
+        out.fill_(float("nan"))
+        pool.attention(0, lo, hi - lo + 1, q, out)
+        torch.cuda.synchronize()
+        live = [tuple(split_qkv(project_qkv(xs[s], wt, b), w.hd)) if s in xs else None for s in range(w.S + 1)]
+        cl = {c: clean[c] for c in sch.present_chunk_ids()[:w.A + w.H] if c is not None}
+        ref = oracle_round(w, k, live, cl, storage="bf16", fill=True, total_chunks=C, slots=range(lo, hi + 1))
+        o = out.cpu().numpy().reshape(w.S + 1, w.N, w.heads, w.head_dim).astype(np.float64)
+        assert np.isnan(np.delete(o, list(range(lo, hi + 1)), axis=0)).all()
+        mx, rel = err_stats(o[lo:hi + 1], ref)
+        say(name, "round", k, "slots", lo, "..", hi, "max_abs %.3e rel_l2 %.3e" % (mx, rel))
+        assert mx <= BF16_MAX_ABS and rel <= BF16_REL_L2, (k, mx, rel)
+        if w.S in present:
+            clean[sch.slot_chunk(w.S)] = tuple(live[w.S][1:])
+        if k < C - 1 + w.S:
+            pool.advance()
