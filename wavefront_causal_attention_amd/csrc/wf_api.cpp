@@ -534,7 +534,7 @@ int wf_qkv_project_publish(wf_handle* h, int32_t layer, int32_t slot_first, int3
         a.dt = c.rope_split[0]; a.dh = c.rope_split[1]; a.dw = c.rope_split[2];
         a.slot_first = slot_first; a.nslots = nslots;
         a.mtiles = (L.N + wf::kProjTokens - 1) / wf::kProjTokens;
-        a.ctiles = 3 * hd / 128;
+        a.ctiles = (3 * hd + wf::kProjChannels - 1) / wf::kProjChannels;
         a.mrows = nslots * a.mtiles;
         // each XCD takes one block of (channel-tile group x token-row group), so
         // its L2 holds a slice of w and the x rows it is working on

@@ -97,8 +97,9 @@ struct AttnArgs {
 // QKV projection with RoPE + publish as its epilogue (bf16 pools), for
 // `nslots` consecutive live slots of one layer.
 constexpr int kProjTokens = 256;     // tokens per projection workgroup tile
-constexpr int kProjMaxFrames = 32;   // latent frames one tile may touch (time table in LDS)
-constexpr int kProjMaxRopeEntries = 4096;  // frame_h*dh/2 + frame_w*dw/2 (row/column tables in LDS)
+constexpr int kProjChannels = 256;   // output channels per projection workgroup tile
+constexpr int kProjMaxFrames = 8;    // latent frames one tile may touch (time table in LDS)
+constexpr int kProjMaxRopeEntries = 2048;  // frame_h*dh/2 + frame_w*dw/2 (row/column tables in LDS)
 struct ProjArgs {
     const uint16_t* x;        // hidden states [nslots * N][x_stride] bf16
     int64_t x_stride;         // elements between token rows
@@ -118,7 +119,7 @@ struct ProjArgs {
     int dt, dh, dw;
     int slot_first, nslots;
     int mtiles;               // token tiles per chunk
-    int ctiles;               // 128-channel tiles of the 3 * heads * D outputs
+    int ctiles;               // 256-channel tiles of the 3 * heads * D outputs (the last may be half)
     int mrows;                // nslots * mtiles
     int g_ct, g_mt;           // XCD blocking: channel-tile groups x token-row groups = 8
     int t0[kMaxSlots];        // RoPE time offset per slot

@@ -10,9 +10,11 @@
 //
 //   qkv[n][o] = sum_c x[n][c] * w[o][c] + b[o]      (w in [out][in] layout)
 //
-// Workgroup tile: 256 tokens of one slot's chunk x 128 output channels, which
-// lie wholly inside Q, K or V (h*d is a multiple of 128). 8 waves, each 64
-// tokens x 64 channels as 2 x 2 blocks of v_mfma_f32_32x32x16_bf16.
+// Workgroup tile: 256 tokens of one slot's chunk x 256 output channels. 8
+// waves (two per SIMD), each 64 tokens x 128 channels as 2 x 4 blocks of
+// v_mfma_f32_32x32x16_bf16, so every X fragment read from LDS feeds four
+// MFMAs and every W fragment two. A wave's 128 channels lie wholly inside Q,
+// K or V (h*d is a multiple of 128), so the orientation below is per wave.
 //   Q and K tiles compute the transposed block C^T[channel][token], so a lane
 //   holds one token and runs of 4 consecutive channels: the RoPE pairs
 //   (2m, 2m+1) are in-lane, and a lane pair (l, l+32) holds 8 consecutive
@@ -23,7 +25,7 @@
 // Both orientations read the same LDS fragments (16 bytes = 8 consecutive
 // hidden channels of one row of x or w) and only swap the MFMA operands.
 //
-// Operands arrive by LDS DMA in 64-channel stages through a 3-stage ring. A
+// Operands arrive by LDS DMA in 64-channel stages, double-buffered. A
 // stage holds rows of 128 bytes; 16-byte vector kv of row r sits in slot
 // kv ^ ((r >> 1) & 7), so that each DMA instruction reads eight whole rows
 // (eight 128-byte lines of x or w) and the fragment reads of 16 lanes (16
@@ -42,7 +44,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 
 constexpr int PM = kProjTokens;   // tokens per workgroup tile
-constexpr int PC = 128;           // output channels per workgroup tile
+constexpr int PC = kProjChannels; // output channels per workgroup tile
 constexpr int BK = 64;            // hidden channels per stage
 constexpr int PNT = 512;          // threads per workgroup (8 waves)
 constexpr int XI = PM / 8 / 8;    // x DMA instructions per wave per stage (8 rows each)
@@ -53,35 +55,22 @@ constexpr uint32_t kOOB = 0x80000000u;
 
 __shared__ __align__(16) uint16_t g_px0[PM * BK];
 __shared__ __align__(16) uint16_t g_px1[PM * BK];
-__shared__ __align__(16) uint16_t g_px2[PM * BK];
 __shared__ __align__(16) uint16_t g_pw0[PC * BK];
 __shared__ __align__(16) uint16_t g_pw1[PC * BK];
-__shared__ __align__(16) uint16_t g_pw2[PC * BK];
-// time-axis (cos, sin) of every frame the tile touches: [frame][32]. Static,
-// like the stage buffers: with only static LDS the compiler can tell each
-// DMA target from the stage being read and does not drain the DMA queue
-// before the fragment reads.
+// row- and column-axis (cos, sin) tables: [frame_h][dh/2] then [frame_w][dw/2]
+__shared__ float2 g_prtab[kProjMaxRopeEntries];
+// time-axis (cos, sin) of every frame the tile touches: [frame][32]
 __shared__ float2 g_pttab[kProjMaxFrames * 32];
 
 template <int I>
 __device__ __forceinline__ uint16_t* xbuf() {
     if constexpr (I == 0) return g_px0;
-    else if constexpr (I == 1) return g_px1;
-    else return g_px2;
+    else return g_px1;
 }
 template <int I>
 __device__ __forceinline__ uint16_t* wbuf() {
     if constexpr (I == 0) return g_pw0;
-    else if constexpr (I == 1) return g_pw1;
-    else return g_pw2;
-}
-
-template <int I, int N, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-    if constexpr (I < N) {
-        f(std::integral_constant<int, I>{});
-        static_for<I + 1, N>(f);
-    }
+    else return g_pw1;
 }
 
 template <int N>
@@ -90,8 +79,26 @@ __device__ __forceinline__ void wait_vmem_n() { asm volatile("s_waitcnt vmcnt(%0
 // wave waited for its own before): a bare barrier orders the buffers.
 __device__ __forceinline__ void stage_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, const void* lds, uint32_t voff) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds, 16, voff, 0, 0, 0);
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+// Buffer resource for raw loads from [base, base + bytes).
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, int32_t bytes) {
+    const uint64_t b = (uint64_t)base;
+    i32x4 r;
+    r.x = (int)(uint32_t)b;
+    r.y = (int)(uint32_t)(b >> 32) & 0xFFFF;    // stride 0
+    r.z = bytes;
+    r.w = 0x00020000;
+    return r;
+}
+// LDS DMA of 16 bytes per lane to LDS address lds + 16 * lane. Written as
+// inline asm: it writes LDS, not registers, and the kernel orders every read
+// of a stage after that stage's DMA with an explicit vmcnt wait and a barrier,
+// so the compiler must not add waits of its own before the fragment reads
+// that follow the next stage's DMA (it cannot tell the two buffers apart).
+__device__ __forceinline__ void dma16(i32x4 r, const void* lds, uint32_t voff) {
+    const uint32_t m = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_t*)lds);
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :: "s"(m), "v"(voff), "s"(r) : "memory", "m0");
 }
 
 // byte offset of 16-byte vector kv of row r inside a stage
@@ -119,46 +126,46 @@ __global__ __launch_bounds__(PNT, 1) void proj_publish_kernel(ProjArgs a) {
     const int sr = row / a.mtiles, mt = row - sr * a.mtiles;
     const int s = a.slot_first + sr;
     const int N = a.N, hd = a.heads * D;
-    const int kind = ct * PC / hd;                 // 0 Q, 1 K, 2 V (uniform)
     const int n0 = mt * PM;
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
-    const int wm = wave & 3, wc = wave >> 2;       // 64-token and 64-channel block of this wave
+    const int wm = wave & 3, wc = wave >> 2;       // 64-token and 128-channel block of this wave
+    const int ob = ct * PC + wc * 128;             // first output channel of this wave
+    const bool live = ob < 3 * hd;                 // the last tile may reach past 3*h*d
+    const int kind = live ? ob / hd : 0;           // 0 Q, 1 K, 2 V (uniform: h*d % 128 == 0)
+    const bool rope = live && kind < 2;
+    const bool tile_rope = ct * PC < 2 * hd;       // some wave of the tile rotates
 
-    const __amdgpu_buffer_rsrc_t xrs =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.x), (short)0, a.xbytes, 0x00020000);
-    const __amdgpu_buffer_rsrc_t wrs =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.w), (short)0, a.wbytes, 0x00020000);
+    const i32x4 xrs = make_rsrc(a.x, a.xbytes);
+    const i32x4 wrs = make_rsrc(a.w, a.wbytes);
 
-    // ---- time-axis table (Q and K tiles): frequencies loaded and waited for
-    // before any DMA, so the DMA wait counts below stay exact; the fp64 sincos
-    // then runs while the first stages are in flight
+    // ---- RoPE tables: the time-axis frequency of this thread's table entry
+    // and the row/column (cos, sin) tables, loaded and waited for before any
+    // DMA, so the DMA wait counts stay exact; the fp64 sincos runs while the
+    // first stage is in flight
     const int HW = a.frame_h * a.frame_w;
     const int f_lo = n0 / HW;
     const int nf = (min(n0 + PM, N) - 1) / HW - f_lo + 1;
     const int hp = a.dt >> 1;
-    const bool rope = kind < 2;
-    // entries tid and tid + PNT of the [frame][pair] table (at most
-    // kProjMaxFrames x 32 = 2 x PNT entries, checked on the host)
-    double om[2] = {0.0, 0.0};
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-        const int idx = tid + e * PNT;
-        if (rope && idx < nf * hp) om[e] = a.omega_t[idx % hp];
-    }
-    // row- and column-axis (cos, sin) tables, copied to LDS after the main
-    // loop (kProjMaxRopeEntries entries at most, checked on the host): loaded
-    // here, coalesced, so their latency hides behind the first stage
+    static_assert(kProjMaxFrames * 32 <= PNT, "one time-table entry per thread");
+    const bool tt = tile_rope && tid < nf * hp;
+    const double om = tt ? a.omega_t[tid % hp] : 0.0;
     const int nh = a.frame_h * (a.dh >> 1), nrope = nh + a.frame_w * (a.dw >> 1);
-    float2 rt[kProjMaxRopeEntries / PNT];
+    constexpr int RE = kProjMaxRopeEntries / PNT;
+    float2 rt[RE];
 #pragma unroll
-    for (int e = 0; e < kProjMaxRopeEntries / PNT; ++e) {
+    for (int e = 0; e < RE; ++e) {
         const int idx = tid + e * PNT;
-        rt[e] = (rope && idx < nrope) ? (idx < nh ? a.htab[idx] : a.wtab[idx - nh]) : make_float2(0.f, 0.f);
+        rt[e] = (tile_rope && idx < nrope) ? (idx < nh ? a.htab[idx] : a.wtab[idx - nh]) : make_float2(0.f, 0.f);
     }
     wait_vmem_n<0>();
+#pragma unroll
+    for (int e = 0; e < RE; ++e) {
+        const int idx = tid + e * PNT;
+        if (tile_rope && idx < nrope) g_prtab[idx] = rt[e];
+    }
 
     // ---- DMA offsets: lane covers vector (lane % 8) of row (lane / 8) of each
     // 8-row instruction; the vector it fetches is the one that slot holds
@@ -174,7 +181,8 @@ __global__ __launch_bounds__(PNT, 1) void proj_publish_kernel(ProjArgs a) {
     for (int i = 0; i < WI; ++i) {
         const int r = (wave * WI + i) * 8 + (lane >> 3);
         const int kv = (lane & 7) ^ ((r >> 1) & 7);
-        woff[i] = (uint32_t)((((int64_t)ct * PC + r) * a.hidden + kv * 8) * 2);
+        const int o = ct * PC + r;
+        woff[i] = o < 3 * hd ? (uint32_t)((((int64_t)o) * a.hidden + kv * 8) * 2) : kOOB;
     }
     auto dma_stage = [&](auto I, int kt) {
         constexpr int B = decltype(I)::value;
@@ -188,197 +196,182 @@ __global__ __launch_bounds__(PNT, 1) void proj_publish_kernel(ProjArgs a) {
     };
     const int nk = a.hidden / BK;
     dma_stage(std::integral_constant<int, 0>{}, 0);
-    if (nk > 1) dma_stage(std::integral_constant<int, 1>{}, 1);
 
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-        const int idx = tid + e * PNT;
-        if (rope && idx < nf * hp) {
-            const int fi = idx / hp, m = idx - fi * hp;
-            double sn, cs;
-            sincos((double)(a.t0[sr] + f_lo + fi) * om[e], &sn, &cs);
-            g_pttab[fi * 32 + m] = make_float2((float)cs, (float)sn);
-        }
+    if (tt) {
+        const int fi = tid / hp, m = tid - fi * hp;
+        double sn, cs;
+        sincos((double)(a.t0[sr] + f_lo + fi) * om, &sn, &cs);
+        g_pttab[fi * 32 + m] = make_float2((float)cs, (float)sn);
     }
 
-    f32x16 acc[2][2];
+    f32x16 acc[2][4];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int jj = 0; jj < 2; ++jj)
+        for (int jj = 0; jj < 4; ++jj)
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][jj][e] = 0.f;
 
-    // One stage: every fragment read of the stage is issued first, then the
-    // DMA of stage kt+2 (a different buffer), then the 16 MFMAs. With the
-    // reads ahead of the DMA in program order the compiler has no DMA write
-    // to wait for before them, and their latency overlaps the DMA issue and
-    // the other wave's MFMAs.
-    // TR: the transposed block C^T[channel][token] (Q and K tiles).
+    // One stage: wait for its DMA and the barrier, read every fragment of the
+    // stage (the reads of the second half after the next stage's DMA into the
+    // other buffer, which every wave finished reading before this barrier),
+    // then 32 MFMAs, which the next stage's DMA lands behind.
+    // TR: the transposed block C^T[channel][token] (Q and K waves).
     auto stage = [&](auto I, auto TR, int kt) {
         constexpr int B = decltype(I)::value;
+        wait_vmem_n<0>();
+        stage_barrier();
         const uint8_t* xl = reinterpret_cast<const uint8_t*>(xbuf<B>());
         const uint8_t* wl = reinterpret_cast<const uint8_t*>(wbuf<B>());
-        bf16x8 xf[BK / 16][2], wf_[BK / 16][2];
-#pragma unroll
-        for (int ks = 0; ks < BK / 16; ++ks) {
+        bf16x8 xf[BK / 16][2], wf_[BK / 16][4];
+        auto rd = [&](int ks) {
             const int kv = ks * 2 + hf;
 #pragma unroll
             for (int i = 0; i < 2; ++i)
                 xf[ks][i] = *reinterpret_cast<const bf16x8*>(xl + swz(wm * 64 + i * 32 + l32, kv));
 #pragma unroll
-            for (int jj = 0; jj < 2; ++jj)
-                wf_[ks][jj] = *reinterpret_cast<const bf16x8*>(wl + swz(wc * 64 + jj * 32 + l32, kv));
-        }
+            for (int jj = 0; jj < 4; ++jj)
+                wf_[ks][jj] = *reinterpret_cast<const bf16x8*>(wl + swz(wc * 128 + jj * 32 + l32, kv));
+        };
+        rd(0);
+        rd(1);
         __builtin_amdgcn_sched_barrier(0);
-        if (kt + 2 < nk) dma_stage(std::integral_constant<int, (B + 2) % 3>{}, kt + 2);
+        if (kt + 1 < nk) dma_stage(std::integral_constant<int, B ^ 1>{}, kt + 1);
         __builtin_amdgcn_sched_barrier(0);
+        rd(2);
+        rd(3);
 #pragma unroll
         for (int ks = 0; ks < BK / 16; ++ks)
 #pragma unroll
             for (int i = 0; i < 2; ++i)
 #pragma unroll
-                for (int jj = 0; jj < 2; ++jj) {
+                for (int jj = 0; jj < 4; ++jj) {
                     if constexpr (decltype(TR)::value)
                         acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf_[ks][jj], xf[ks][i], acc[i][jj], 0, 0, 0);
                     else
                         acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xf[ks][i], wf_[ks][jj], acc[i][jj], 0, 0, 0);
                 }
     };
-
+    // every wave runs the same stages (and barriers) whichever orientation it takes
     auto kloop = [&](auto TR) {
-        for (int kt0 = 0; kt0 < nk; kt0 += 3) {
-            static_for<0, 3>([&](auto I) {
-                constexpr int B = decltype(I)::value;
-                const int kt = kt0 + B;
-                if (kt < nk) {
-                    if (kt + 1 < nk) wait_vmem_n<XI + WI>();   // the next stage may still be in flight
-                    else wait_vmem_n<0>();
-                    stage_barrier();
-                    stage(I, TR, kt);
-                }
-            });
+        for (int kt = 0; kt < nk; kt += 2) {
+            stage(std::integral_constant<int, 0>{}, TR, kt);
+            if (kt + 1 < nk) stage(std::integral_constant<int, 1>{}, TR, kt + 1);
         }
     };
-    if (rope) kloop(std::true_type{});
+    if (rope || !live) kloop(std::true_type{});
     else kloop(std::false_type{});
-    __syncthreads();                               // time-axis table visible (nk may be 1)
+    __syncthreads();                               // stage buffers free, time table visible
+    if (!live) return;
 
-    // ---- epilogue: bias, RoPE (Q, K), bf16, then out to the Q buffer / pages.
-    // The stage buffers are free now. The RoPE row/column tables go to LDS
-    // (the column entry differs for every lane's token, a scattered read in
-    // global memory); each wave stages its 64 x 64 bf16 block in LDS in the
-    // destination's order and writes it out with 16-byte stores: 1 KB
-    // contiguous per K or V instruction, whole 128-byte row pieces for Q.
-    float2* rtab = reinterpret_cast<float2*>(g_px2);            // [frame_h][dh/2] then [frame_w][dw/2]
-    if (rope) {
-#pragma unroll
-        for (int e = 0; e < kProjMaxRopeEntries / PNT; ++e) {
-            const int idx = tid + e * PNT;
-            if (idx < nrope) rtab[idx] = rt[e];
-        }
-    }
-    __syncthreads();
+    // ---- epilogue: bias, RoPE (Q, K), bf16, then out to the Q buffer / pages,
+    // in two passes of 64 channels. Each wave stages a 64 x 64 bf16 block in
+    // LDS in the destination's order and writes it out with 16-byte stores:
+    // 1 KB contiguous per K or V instruction, 128-byte row pieces for Q.
     const int p = a.T - 1 - s;                     // context position of slot s
     const int pt = a.pt;
-    const int ob = ct * PC;                        // first output channel of the tile
     uint8_t* st = reinterpret_cast<uint8_t*>(wave < 4 ? g_px0 : g_px1) + (wave & 3) * 8192;
     const int tb = n0 + wm * 64;                   // first token of this wave
-    if (rope) {
-        const int cb = ob - kind * hd + wc * 64;   // first channel of this wave inside Q or K
-        // [token 64][8 x 16-byte chunks of 8 channels], chunk slot c ^ (t & 7)
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int t = i * 32 + l32;
-            const int n = min(tb + t, N - 1);
-            const int f = n / HW - f_lo;
-            const int yy = (n / a.frame_w) % a.frame_h;
-            const int xw = n % a.frame_w;
+    for (int h2 = 0; h2 < 2; ++h2) {
+        const int oc = ob + 64 * h2;               // first output channel of this pass
+        if (rope) {
+            const int cb = oc - kind * hd;         // its channel inside Q or K
+            // [token 64][8 x 16-byte chunks of 8 channels], chunk slot c ^ (t & 7)
 #pragma unroll
-            for (int jj = 0; jj < 2; ++jj)
+            for (int i = 0; i < 2; ++i) {
+                const int t = i * 32 + l32;
+                const int n = min(tb + t, N - 1);
+                const int f = n / HW - f_lo;
+                const int yy = (n / a.frame_w) % a.frame_h;
+                const int xw = n % a.frame_w;
 #pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int cl = jj * 32 + 8 * g + 4 * hf;                // 4 consecutive channels
-                    const int d0 = (cb + cl) % D;
-                    const uint2 bq = a.bias ? *reinterpret_cast<const uint2*>(a.bias + ob + wc * 64 + cl)
-                                            : make_uint2(0, 0);
-                    float v[4];
-                    v[0] = acc[i][jj][4 * g + 0] + __uint_as_float(bq.x << 16);
-                    v[1] = acc[i][jj][4 * g + 1] + __uint_as_float(bq.x & 0xFFFF0000u);
-                    v[2] = acc[i][jj][4 * g + 2] + __uint_as_float(bq.y << 16);
-                    v[3] = acc[i][jj][4 * g + 3] + __uint_as_float(bq.y & 0xFFFF0000u);
+                for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
-                    for (int pr = 0; pr < 2; ++pr) {
-                        const int dc = d0 + 2 * pr;
-                        float2 c2;
-                        if (dc < a.dt) c2 = g_pttab[f * 32 + (dc >> 1)];
-                        else if (dc < a.dt + a.dh) c2 = rtab[yy * (a.dh >> 1) + ((dc - a.dt) >> 1)];
-                        else c2 = rtab[nh + xw * (a.dw >> 1) + ((dc - a.dt - a.dh) >> 1)];
-                        const float x0 = v[2 * pr], x1 = v[2 * pr + 1];
-                        v[2 * pr] = fmaf(x0, c2.x, -x1 * c2.y);
-                        v[2 * pr + 1] = fmaf(x0, c2.y, x1 * c2.x);
+                    for (int g = 0; g < 4; ++g) {
+                        const int cl = jj * 32 + 8 * g + 4 * hf;            // 4 consecutive channels
+                        const int d0 = (cb + cl) % D;
+                        const uint2 bq = a.bias ? *reinterpret_cast<const uint2*>(a.bias + oc + cl) : make_uint2(0, 0);
+                        const f32x16& A = acc[i][2 * h2 + jj];
+                        float v[4];
+                        v[0] = A[4 * g + 0] + __uint_as_float(bq.x << 16);
+                        v[1] = A[4 * g + 1] + __uint_as_float(bq.x & 0xFFFF0000u);
+                        v[2] = A[4 * g + 2] + __uint_as_float(bq.y << 16);
+                        v[3] = A[4 * g + 3] + __uint_as_float(bq.y & 0xFFFF0000u);
+#pragma unroll
+                        for (int pr = 0; pr < 2; ++pr) {
+                            const int dc = d0 + 2 * pr;
+                            float2 c2;
+                            if (dc < a.dt) c2 = g_pttab[f * 32 + (dc >> 1)];
+                            else if (dc < a.dt + a.dh) c2 = g_prtab[yy * (a.dh >> 1) + ((dc - a.dt) >> 1)];
+                            else c2 = g_prtab[nh + xw * (a.dw >> 1) + ((dc - a.dt - a.dh) >> 1)];
+                            const float x0 = v[2 * pr], x1 = v[2 * pr + 1];
+                            v[2 * pr] = fmaf(x0, c2.x, -x1 * c2.y);
+                            v[2 * pr + 1] = fmaf(x0, c2.y, x1 * c2.x);
+                        }
+                        const int chunk = jj * 4 + g;
+                        *reinterpret_cast<uint2*>(st + t * 128 + ((chunk ^ (t & 7)) << 4) + hf * 8) =
+                            make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
                     }
-                    const int chunk = jj * 4 + g;
-                    *reinterpret_cast<uint2*>(st + t * 128 + ((chunk ^ (t & 7)) << 4) + hf * 8) =
-                        make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
-                }
-        }
-        if (kind == 0) {
-            // Q [s][head][n][D]: 8 lanes per token write its 64 channels (128 bytes)
+            }
+            if (kind == 0) {
+                // Q [s][head][n][D]: 8 lanes per token write its 64 channels (128 bytes)
 #pragma unroll
-            for (int it = 0; it < 8; ++it) {
-                const int t = it * 8 + (lane >> 3), chunk = lane & 7;
-                const uint4 val = *reinterpret_cast<const uint4*>(st + t * 128 + ((chunk ^ (t & 7)) << 4));
-                const int n = tb + t;
-                if (n >= N) continue;
-                const int c = cb + chunk * 8;
-                const int head = c / D, d = c - head * D;
-                *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.q_out) +
-                                          (((int64_t)s * a.heads + head) * N + n) * D + d) = val;
+                for (int it = 0; it < 8; ++it) {
+                    const int t = it * 8 + (lane >> 3), chunk = lane & 7;
+                    const uint4 val = *reinterpret_cast<const uint4*>(st + t * 128 + ((chunk ^ (t & 7)) << 4));
+                    const int n = tb + t;
+                    if (n >= N) continue;
+                    const int c = cb + chunk * 8;
+                    const int head = c / D, d = c - head * D;
+                    *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.q_out) +
+                                              (((int64_t)s * a.heads + head) * N + n) * D + d) = val;
+                }
+            } else {
+                // K pages [phys][head][D/8][pt][8]: one lane per token, one 8-channel vector per store
+                const int n = tb + lane;
+                const int tok = n % pt;
+                const int64_t phys = a.table[p * a.ppc + min(n, N - 1) / pt];
+#pragma unroll
+                for (int v8 = 0; v8 < 8; ++v8) {
+                    const uint4 val = *reinterpret_cast<const uint4*>(st + lane * 128 + ((v8 ^ (lane & 7)) << 4));
+                    if (n >= N) continue;
+                    const int c = cb + v8 * 8;
+                    const int head = c / D, d = c - head * D;
+                    *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.kpage) + (phys * a.heads + head) * pt * D +
+                                              ((int64_t)(d >> 3) * pt + tok) * 8) = val;
+                }
             }
         } else {
-            // K pages [phys][head][D/8][pt][8]: one lane per token, one 8-channel vector per store
-            const int n = tb + lane;
-            const int tok = n % pt;
-            const int64_t phys = a.table[p * a.ppc + min(n, N - 1) / pt];
+            const int cb = oc - 2 * hd;            // first channel of this pass inside V
+            // [channel 64][8 x 16-byte chunks of 8 tokens], chunk slot tg ^ (c & 7)
 #pragma unroll
-            for (int v8 = 0; v8 < 8; ++v8) {
-                const uint4 val = *reinterpret_cast<const uint4*>(st + lane * 128 + ((v8 ^ (lane & 7)) << 4));
-                if (n >= N) continue;
-                const int c = cb + v8 * 8;
-                const int head = c / D, d = c - head * D;
-                *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.kpage) + (phys * a.heads + head) * pt * D +
-                                          ((int64_t)(d >> 3) * pt + tok) * 8) = val;
+            for (int jj = 0; jj < 2; ++jj) {
+                const int c = jj * 32 + l32;
+                const float bb = a.bias ? bf_to_f(a.bias[oc + c]) : 0.f;
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const f32x16& Ai = acc[i][2 * h2 + jj];
+                        const int chunk = i * 4 + g;                        // tokens 8*chunk + 4*hf .. +3
+                        *reinterpret_cast<uint2*>(st + c * 128 + ((chunk ^ (c & 7)) << 4) + hf * 8) =
+                            make_uint2(pack_bf16x2(Ai[4 * g] + bb, Ai[4 * g + 1] + bb),
+                                       pack_bf16x2(Ai[4 * g + 2] + bb, Ai[4 * g + 3] + bb));
+                    }
             }
-        }
-    } else {
-        const int cb = ob - 2 * hd + wc * 64;      // first channel of this wave inside V
-        // [channel 64][8 x 16-byte chunks of 8 tokens], chunk slot tg ^ (c & 7)
+            // V pages [phys][head][pt/8][D][8]: one lane per channel, one 8-token group per store
+            const int c = cb + lane;
+            const int head = c / D, d = c - head * D;
 #pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
-            const int c = jj * 32 + l32;
-            const float bb = a.bias ? bf_to_f(a.bias[ob + wc * 64 + c]) : 0.f;
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int chunk = i * 4 + g;                            // tokens 8*chunk + 4*hf .. +3
-                    *reinterpret_cast<uint2*>(st + c * 128 + ((chunk ^ (c & 7)) << 4) + hf * 8) =
-                        make_uint2(pack_bf16x2(acc[i][jj][4 * g] + bb, acc[i][jj][4 * g + 1] + bb),
-                                   pack_bf16x2(acc[i][jj][4 * g + 2] + bb, acc[i][jj][4 * g + 3] + bb));
-                }
-        }
-        // V pages [phys][head][pt/8][D][8]: one lane per channel, one 8-token group per store
-        const int c = cb + lane;
-        const int head = c / D, d = c - head * D;
-#pragma unroll
-        for (int tg = 0; tg < 8; ++tg) {
-            const uint4 val = *reinterpret_cast<const uint4*>(st + lane * 128 + ((tg ^ (lane & 7)) << 4));
-            const int n = tb + tg * 8;
-            if (n >= N) continue;                  // N is a multiple of 8: all 8 tokens or none
-            const int tok = n % pt;
-            const int64_t phys = a.table[p * a.ppc + n / pt];
-            *reinterpret_cast<uint4*>(a.vpage + (phys * a.heads + head) * pt * D + ((int64_t)(tok >> 3) * D + d) * 8) = val;
+            for (int tg = 0; tg < 8; ++tg) {
+                const uint4 val = *reinterpret_cast<const uint4*>(st + lane * 128 + ((tg ^ (lane & 7)) << 4));
+                const int n = tb + tg * 8;
+                if (n >= N) continue;              // N is a multiple of 8: all 8 tokens or none
+                const int tok = n % pt;
+                const int64_t phys = a.table[p * a.ppc + n / pt];
+                *reinterpret_cast<uint4*>(a.vpage + (phys * a.heads + head) * pt * D + ((int64_t)(tok >> 3) * D + d) * 8) = val;
+            }
         }
     }
 }
