@@ -217,6 +217,19 @@ int wf_attention_round(wf_handle* h, int32_t layer, int32_t slot_first, int32_t 
  */
 int wf_round_advance(wf_handle* h, void* stream);
 
+/*
+ * Attention launch order (host only, no handle or device needed): the list
+ * the pool uploads for query slots [slot_first, slot_first + nslots), i.e.
+ * what workgroup b of an attention launch computes. Entry b is
+ * (slot << 26) | (head << 16) | query_tile, or -1 for an idle workgroup;
+ * workgroup b runs on XCD b % 8. The (slot, head, query tile) units are cut
+ * into 8 pieces of equal key-chunk cost, one per XCD, and each piece is packed
+ * onto cus_per_xcd CUs and listed by planned start time. *count receives the
+ * length (a multiple of 8); units (capacity entries) may be NULL to query it.
+ */
+int wf_attention_work_list(const wf_config* cfg, int32_t slot_first, int32_t nslots, int32_t cus_per_xcd,
+                           int32_t* units, int64_t capacity, int64_t* count);
+
 /* Host queries (no device access). */
 int wf_round_index(const wf_handle* h, int64_t* k);
 int wf_schedule_chunk_ids(const wf_handle* h, int64_t* ids /* [T], -1 = no chunk */);

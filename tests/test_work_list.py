@@ -1,0 +1,77 @@
+"""CPU tests of the attention launch order (wf_attention_work_list): the host
+logic that cuts (slot, head, query tile) units into one piece per XCD and
+packs each piece onto that XCD's CUs. No device is involved."""
+import dataclasses
+import heapq
+import math
+
+import pytest
+
+import wf_inputs as W
+import wavefront_causal_attention_amd as wf
+from _gpu_round import config_of
+
+XCDS = 8
+
+
+def _units(w, first, n):
+    qt = math.ceil(w.N / 256)
+    return {(s, h, q) for s in range(first, first + n) for h in range(w.heads) for q in range(qt)}
+
+
+def _cost(w, s):
+    return w.T if w.live_mask == "all" else w.T - s
+
+
+def _ranges(S):
+    return [(f, n) for f in range(S + 1) for n in range(1, S + 2 - f)]
+
+
+@pytest.mark.parametrize("name", ["tiny", "ragged128", "edge_s1_h0", "wan1.3b_s4", "wan14b_s4", "max64"])
+def test_every_unit_listed_exactly_once(name):
+    w = W.WORKLOADS[name]
+    ranges = _ranges(w.S) if w.S < 8 else [(0, w.S + 1), (0, 1), (w.S, 1), (3, 11), (17, 14)]
+    for first, n in ranges:
+        lst = wf.wf_attention_work_list(config_of(w), first, n, 32)
+        assert len(lst) % XCDS == 0
+        got = [u for u in lst if u is not None]
+        assert len(got) == len(set(got)) and set(got) == _units(w, first, n), (first, n)
+
+
+@pytest.mark.parametrize("name,mask", [("wan1.3b_s4", "wavefront"), ("wan14b_s4", "wavefront"),
+                                       ("wan1.3b_s5_30", "wavefront"), ("wan1.3b_s4", "all")])
+def test_xcd_pieces_balanced_and_packed_order_fills_the_cus(name, mask):
+    """Each XCD's share of the key-chunk cost is within one unit of an
+    eighth. Handing the XCD's entries in list order to whichever of its 32
+    CUs frees first (the hardware dispatcher) ends within one unit of the
+    average CU load, and for the wavefront mask's mixed unit costs keeps the
+    CUs >= 97% busy (all-live units all cost T, so 142.5 units on 32 CUs
+    cannot do better than 4.45 / 5)."""
+    w = dataclasses.replace(W.WORKLOADS[name], live_mask=mask)
+    lst = wf.wf_attention_work_list(config_of(w), 0, w.S + 1, 32)
+    per = [[u for b, u in enumerate(lst) if b % XCDS == x and u is not None] for x in range(XCDS)]
+    loads = [sum(_cost(w, s) for s, _, _ in p) for p in per]
+    total = sum(loads)
+    umax = max(_cost(w, s) for s in range(w.S + 1))
+    assert max(loads) - total / XCDS <= umax and total / XCDS - min(loads) <= umax
+    for p in per:
+        free = [0] * 32
+        heapq.heapify(free)
+        for s, _, _ in p:
+            heapq.heappush(free, heapq.heappop(free) + _cost(w, s))
+        span = max(free)
+        work = sum(_cost(w, s) for s, _, _ in p)
+        assert span <= work / 32 + umax
+        if mask == "wavefront":
+            assert work / (32 * span) >= 0.97, (name, work / (32 * span))
+
+
+def test_work_list_validation():
+    w = W.WORKLOADS["ragged128"]
+    for args in [(-1, 1), (0, 0), (0, w.S + 2), (w.S, 2)]:
+        with pytest.raises(wf.WfError) as e:
+            wf.wf_attention_work_list(config_of(w), args[0], args[1], 32)
+        assert e.value.status == wf.WF_E_INVALID_ARG
+    with pytest.raises(wf.WfError) as e:
+        wf.wf_attention_work_list(config_of(w), 0, 1, 0)
+    assert e.value.status == wf.WF_E_INVALID_ARG

@@ -9,7 +9,7 @@ from __future__ import annotations
 
 from ._lib import (WF_DTYPE_BF16, WF_DTYPE_FP32, WF_DTYPE_FP8_E4M3, WF_E_HIP, WF_E_INVALID_ARG,
                    WF_E_NOT_READY, WF_E_SHAPE, WF_MASK_ALL_LIVE, WF_MASK_WAVEFRONT, WF_OK, WfError,
-                   load, wf_attention_round, wf_config,
+                   load, wf_attention_round, wf_attention_work_list, wf_config,
                    wf_geometry, wf_kv_publish, wf_page_table_host, wf_pool_bytes, wf_pool_create,
                    wf_qkv_project_publish,
                    wf_pool_create_host_model, wf_pool_destroy, wf_ready_mask, wf_round_advance,

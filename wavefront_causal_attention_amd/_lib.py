@@ -83,6 +83,8 @@ def load() -> ctypes.CDLL:
         "wf_qkv_project_publish": (ctypes.c_int, [P, I32, I32, I32, P, I64, I32, P, P, P, P, P]),
         "wf_attention_round": (ctypes.c_int, [P, I32, I32, I32, P, P, P, I32, P]),
         "wf_round_advance": (ctypes.c_int, [P, P]),
+        "wf_attention_work_list": (ctypes.c_int, [ctypes.POINTER(wf_config), I32, I32, I32, P, I64,
+                                                  ctypes.POINTER(I64)]),
         "wf_round_index": (ctypes.c_int, [P, ctypes.POINTER(I64)]),
         "wf_schedule_chunk_ids": (ctypes.c_int, [P, P]),
         "wf_page_table_host": (ctypes.c_int, [P, P]),
@@ -209,6 +211,18 @@ def wf_ready_mask(h, layer: int) -> int:
     return m.value
 
 
+def wf_attention_work_list(cfg, slot_first, nslots, cus_per_xcd):
+    """The attention launch order for a slot range: list of (slot, head, qtile) or None (idle)."""
+    n = ctypes.c_int64(0)
+    _check(load().wf_attention_work_list(ctypes.byref(cfg), slot_first, nslots, cus_per_xcd, None, 0,
+                                         ctypes.byref(n)), "wf_attention_work_list")
+    arr = (ctypes.c_int32 * n.value)()
+    _check(load().wf_attention_work_list(ctypes.byref(cfg), slot_first, nslots, cus_per_xcd,
+                                         ctypes.cast(arr, ctypes.c_void_p), n.value, ctypes.byref(n)),
+           "wf_attention_work_list")
+    return [None if x < 0 else ((x >> 26) & 63, (x >> 16) & 1023, x & 0xFFFF) for x in arr]
+
+
 def wf_geometry(h):
     arr = (ctypes.c_int64 * 12)()
     _check(load().wf_geometry(h, ctypes.cast(arr, ctypes.c_void_p)), "wf_geometry")
@@ -220,6 +234,7 @@ def wf_geometry(h):
 EXPORTED = [
     "wf_pool_bytes", "wf_pool_create", "wf_pool_create_host_model", "wf_pool_destroy",
     "wf_kv_publish", "wf_qkv_project_publish", "wf_attention_round", "wf_round_advance", "wf_round_index",
+    "wf_attention_work_list",
     "wf_schedule_chunk_ids", "wf_page_table_host", "wf_ready_mask", "wf_geometry",
     "wf_status_string", "wf_last_error",
 ]

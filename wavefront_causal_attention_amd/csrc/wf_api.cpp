@@ -676,6 +676,24 @@ int wf_round_index(const wf_handle* h, int64_t* k) {
     return WF_OK;
 }
 
+int wf_attention_work_list(const wf_config* cfg, int32_t slot_first, int32_t nslots, int32_t cus_per_xcd,
+                           int32_t* units, int64_t capacity, int64_t* count) {
+    Layout L{};
+    const int st = validate(cfg, &L);
+    if (st != WF_OK) return st;
+    if (!count || nslots < 1 || slot_first < 0 || slot_first + nslots > cfg->S + 1 || cus_per_xcd < 1)
+        return WF_E_INVALID_ARG;
+    const int qtiles = (L.N + wf::kAttnBM - 1) / wf::kAttnBM;
+    const std::vector<int32_t> wl = build_work_list(slot_first, nslots, cfg->heads, qtiles, L.T,
+                                                    cfg->live_mask == WF_MASK_ALL_LIVE, cus_per_xcd);
+    *count = (int64_t)wl.size();
+    if (units) {
+        if (capacity < (int64_t)wl.size()) return WF_E_INVALID_ARG;
+        std::copy(wl.begin(), wl.end(), units);
+    }
+    return WF_OK;
+}
+
 int wf_schedule_chunk_ids(const wf_handle* h, int64_t* ids) {
     if (!h || !ids) return WF_E_INVALID_ARG;
     for (int p = 0; p < h->L.T; ++p) ids[p] = h->present(p) ? h->chunk_at(p) : -1;
