@@ -18,6 +18,8 @@ Sources (the Wave Forcing pages, arXiv 2611.00859):
     after QKV projection and RoPE.
   * thelatestinai.com listing, Table 11: model widths (hidden = heads x 128),
     the shape of the QKV projection that precedes RoPE.
+  * e-cogni.com.br article, section "Como funciona", and thelatestinai.com
+    listing, Table 6: W8A8 (8-bit weights and activations) in the projections.
 
 Where the pages are silent the oracle takes these readings: softmax scale
 1/sqrt(d); adjacent-pair 3D RoPE on contiguous t|h|w channel ranges with
@@ -30,7 +32,10 @@ closed forms, invariants, brute force or a library routine, except the choice
 of the fp8 scale/mean scheme, which the pages do not describe (they only name
 an fp8 payload with scales); its encoder is pinned to torch's float8_e4m3fn
 cast, but the blocking and mean smoothing follow the workload description and
-are "parity unpinned" beyond that.
+are "parity unpinned" beyond that. Likewise the W8A8 format (e4m3, one scale
+per token and per output channel) is a reading: its quantiser is pinned to
+brute-force nearest rounding and its projection to exact rational arithmetic,
+but the choice of format and granularity is not fixed by the pages.
 """
 from .schedule import (RoundSchedule, live_mask, legal_positions, GroupRing,
                        slot_position)
@@ -40,7 +45,7 @@ from .numerics import (bf16_round, fp8_e4m3_encode, fp8_e4m3_decode,
 from .attention import (masked_softmax_attention, slot_attention, round_attention,
                         dense_round_attention)
 from .round import oracle_round, rotate_chunk, rotated_context
-from .projection import project_qkv, split_qkv
+from .projection import project_qkv, project_qkv_w8a8, quantize_rows_fp8, split_qkv
 
 __all__ = [
     "RoundSchedule", "live_mask", "legal_positions", "GroupRing", "slot_position",
@@ -50,5 +55,5 @@ __all__ = [
     "masked_softmax_attention", "slot_attention", "round_attention",
     "dense_round_attention",
     "oracle_round", "rotate_chunk", "rotated_context",
-    "project_qkv", "split_qkv",
+    "project_qkv", "split_qkv", "quantize_rows_fp8", "project_qkv_w8a8",
 ]
