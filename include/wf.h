@@ -183,6 +183,49 @@ int wf_qkv_project_publish(wf_handle* h, int32_t layer, int32_t slot_first, int3
                            const void* bias, const int32_t* chunk_t0_host, void* q_out, void* stream);
 
 /*
+ * Per-row fp8 e4m3 quantisation of W8A8 operands (e-cogni.com.br, "Como
+ * funciona": W8A8 quantisation of weights and activations; thelatestinai.com
+ * listing, Table 6, the Sage+W8A8 backend). Row r of x (cols bf16 values at
+ * x + r * x_row_stride_elems) gets the fp32 scale absmax / 448 (1 for an
+ * all-zero row) and codes e4m3(x / scale), the quotient taken in IEEE fp32,
+ * rounded to nearest even and saturated at +-448. Used on the hidden states
+ * (one scale per token) and, once, on a weight [out][in] (one scale per
+ * output channel). Inputs must be finite.
+ *
+ * x:      device bf16, 16-byte aligned, x_row_stride_elems a multiple of 8.
+ * cols:   a multiple of 8, at most 8192.
+ * codes:  device uint8 [rows][code_row_stride], 8-byte aligned,
+ *         code_row_stride >= cols and a multiple of 8 (16 for a projection
+ *         operand, whose rows must be 16-byte aligned).
+ * scales: device float [rows].
+ * rows = 0 launches nothing. Caller-owned memory; the work is enqueued on
+ * stream. WF_E_INVALID_ARG for bad pointers or strides, WF_E_SHAPE for cols
+ * out of range.
+ */
+int wf_quantize_rows_fp8(const void* x, int64_t rows, int32_t cols, int64_t x_row_stride_elems,
+                         uint8_t* codes, int64_t code_row_stride, float* scales, void* stream);
+
+/*
+ * W8A8 form of wf_qkv_project_publish: the same launch and publish, with the
+ * projection taken over e4m3 operands (v_mfma_f32_32x32x64_f8f6f4) and their
+ * per-row scales,
+ *     qkv[n][o] = x_scales[n] * w_scales[o] * sum_c x8[n][c] * w8[o][c] + bias[o]
+ *
+ * x8:       device e4m3 codes, row (i*N + n) = token n of slot slot_first + i,
+ *           at x8 + row * x_row_stride (bytes, a multiple of 16), as written
+ *           by wf_quantize_rows_fp8.
+ * x_scales: device float [nslots*N], the scale of each x8 row, 16-byte aligned.
+ * hidden:   a multiple of 128.
+ * w8:       device e4m3 codes [3*heads*head_dim][hidden], 16-byte aligned.
+ * w_scales: device float [3*heads*head_dim], 16-byte aligned.
+ * bias, chunk_t0_host, q_out and the errors: as wf_qkv_project_publish.
+ */
+int wf_qkv_project_publish_w8a8(wf_handle* h, int32_t layer, int32_t slot_first, int32_t nslots,
+                                const void* x8, int64_t x_row_stride, const float* x_scales, int32_t hidden,
+                                const void* w8, const float* w_scales, const void* bias,
+                                const int32_t* chunk_t0_host, void* q_out, void* stream);
+
+/*
  * Wavefront attention over the paged context (hyper.ai summary, "Method":
  * M_WF(s, j) = 1[j >= s], full attention inside a chunk). One launch computes
  * O = softmax(Q K^T / sqrt(d)) V for query slots [slot_first, slot_first+nslots)

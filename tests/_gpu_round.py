@@ -199,3 +199,26 @@ def read_pages(pool, w: W.Workload, layer=0):
 def position_rows(pages: np.ndarray, table, p: int, ppc: int) -> np.ndarray:
     """[heads, N, d] of context position p from pages [page, head, token, d]."""
     return np.concatenate([pages[table[p * ppc + i]] for i in range(ppc)], axis=1)
+
+
+# fp32 accumulation of `hidden` bf16 products of size ~1/sqrt(hidden) leaves
+# an absolute error near 2^-24 * sqrt(hidden); where the exact value is that
+# small (cancellation), one bf16 ulp of it is finer than the fp32 result, so
+# elements are compared in ulps above this floor and absolutely below it.
+ABS_FLOOR = 2.0 ** -14
+
+
+def bf16_ulps(a, b):
+    """bf16 ulps between got and ref, 0 where they differ by less than ABS_FLOOR."""
+    a = np.asarray(a, dtype=np.float32)
+    b = np.asarray(b, dtype=np.float32)
+    ia = (a.view(np.uint32) >> 16).astype(np.int64)
+    ib = (b.view(np.uint32) >> 16).astype(np.int64)
+    u = np.abs(ia - ib)
+    return np.where(np.abs(a.astype(np.float64) - b.astype(np.float64)) < ABS_FLOOR, 0, u)
+
+
+def worst_ulp(got, ref):
+    u = bf16_ulps(got, ref)
+    i = np.unravel_index(int(np.argmax(u)), u.shape)
+    return "worst %d ulp at %s: got %r ref %r" % (int(u[i]), i, float(got[i]), float(ref[i]))

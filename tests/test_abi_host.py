@@ -30,7 +30,7 @@ def cfg_of(w, **kw):
 
 def test_every_declared_symbol_is_exported(lib):
     header = open(os.path.join(ROOT, "include", "wf.h")).read()
-    declared = set(re.findall(r"\b(wf_[a-z_]+)\s*\(", header))
+    declared = set(re.findall(r"\b(wf_[a-z0-9_]+)\s*\(", header))
     assert {"wf_kv_publish", "wf_attention_round", "wf_round_advance"} <= declared
     for name in declared:
         assert hasattr(lib, name), name
@@ -396,3 +396,69 @@ def test_project_publish_rejects_empty_slots_in_fill_rounds(lib):
         assert wf.wf_ready_mask(h, 0) == 1 << (w.T - 1)
     finally:
         wf.wf_pool_destroy(h)
+
+
+def _proj8(h, w, **kw):
+    args = dict(layer=0, slot_first=0, nslots=w.S + 1, x=FAKE, stride=w.hd, xs=FAKE, hidden=w.hd, wt=FAKE,
+                ws=FAKE, bias=None, q_out=FAKE)
+    args.update(kw)
+    wf.wf_qkv_project_publish_w8a8(h, args["layer"], args["slot_first"], args["nslots"], args["x"], args["stride"],
+                                   args["xs"], args["hidden"], args["wt"], args["ws"], args["bias"], None,
+                                   args["q_out"], None)
+
+
+def test_w8a8_project_publish_marks_live_slots_and_validates(lib):
+    w = W.WORKLOADS["ragged128"]                      # h*d = 384: three 128-code stages
+    h = wf.wf_pool_create_host_model(cfg_of(w))
+    try:
+        bad = [dict(slot_first=1, nslots=w.S + 1), dict(nslots=0), dict(x=None), dict(wt=None), dict(q_out=None),
+               dict(xs=None), dict(ws=None), dict(xs=FAKE + 4), dict(ws=FAKE + 8),
+               dict(hidden=w.hd + 64),                # not a multiple of 128 codes
+               dict(stride=w.hd - 128), dict(stride=w.hd + 8), dict(x=FAKE + 8), dict(layer=1)]
+        for kw in bad:
+            with pytest.raises(wf.WfError) as e:
+                _proj8(h, w, **kw)
+            assert e.value.status == wf.WF_E_INVALID_ARG, kw
+            assert wf.wf_ready_mask(h, 0) == 0
+        _proj8(h, w, slot_first=1, nslots=w.S)
+        live = sum(1 << (w.T - 1 - s) for s in range(1, w.S + 1))
+        assert wf.wf_ready_mask(h, 0) == live
+        _proj8(h, w, slot_first=0, nslots=1, hidden=2 * w.hd, stride=2 * w.hd + 16, bias=FAKE)
+        assert wf.wf_ready_mask(h, 0) == live | 1 << (w.T - 1)
+    finally:
+        wf.wf_pool_destroy(h)
+
+
+@pytest.mark.parametrize("change", [dict(qk_dtype="fp8"), dict(heads=3, head_dim=64)])
+def test_w8a8_project_publish_rejects_unsupported_shapes(lib, change):
+    import dataclasses
+    w = dataclasses.replace(W.WORKLOADS["tiny"], **change)
+    if change.get("heads") == 3:
+        w = dataclasses.replace(w, rope_split=(24, 20, 20))
+    h = wf.wf_pool_create_host_model(cfg_of(w))
+    try:
+        with pytest.raises(wf.WfError) as e:
+            _proj8(h, w, hidden=128, stride=128)
+        assert e.value.status == wf.WF_E_SHAPE
+    finally:
+        wf.wf_pool_destroy(h)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), "INVALID_ARG"), (dict(codes=None), "INVALID_ARG"), (dict(scales=None), "INVALID_ARG"),
+    (dict(rows=-1), "INVALID_ARG"), (dict(cols=0), "SHAPE"), (dict(cols=12), "SHAPE"), (dict(cols=8200), "SHAPE"),
+    (dict(x_stride=8), "INVALID_ARG"), (dict(x_stride=36), "INVALID_ARG"), (dict(code_stride=12), "INVALID_ARG"),
+    (dict(code_stride=36), "INVALID_ARG"), (dict(x=FAKE + 8), "INVALID_ARG"), (dict(codes=FAKE + 4), "INVALID_ARG"),
+    (dict(scales=FAKE + 2), "INVALID_ARG"), (dict(rows=1 << 31), "SHAPE"),
+])
+def test_quantize_rows_validates_before_any_launch(lib, kw, status):
+    args = dict(x=FAKE, rows=10, cols=32, x_stride=32, codes=FAKE, code_stride=32, scales=FAKE)
+    args.update(kw)
+    with pytest.raises(wf.WfError) as e:
+        wf.wf_quantize_rows_fp8(args["x"], args["rows"], args["cols"], args["x_stride"], args["codes"],
+                                args["code_stride"], args["scales"], 0)
+    assert e.value.status == getattr(wf, "WF_E_" + status)
+
+
+def test_quantize_rows_zero_rows_launches_nothing(lib):
+    wf.wf_quantize_rows_fp8(FAKE, 0, 64, 64, FAKE, 64, FAKE, 0)

@@ -19,6 +19,7 @@ from oracle import RoundSchedule, bf16_round, oracle_round, project_qkv, rope_3d
 
 from _gpu_round import (RoundRunner, bf16_dev_bits_to_f32, err_stats, gpu_rows, oracle_rows, position_rows,
                         read_pages, to_dev)
+from _gpu_round import bf16_ulps as _bf16_ulps, worst_ulp as _worst
 
 pytestmark = pytest.mark.gpu
 
@@ -37,29 +38,6 @@ def _device():
     import wavefront_causal_attention_amd as wf
     wf.load()
     yield
-
-
-# fp32 accumulation of `hidden` bf16 products of size ~1/sqrt(hidden) leaves
-# an absolute error near 2^-24 * sqrt(hidden); where the exact value is that
-# small (cancellation), one bf16 ulp of it is finer than the fp32 result, so
-# elements are compared in ulps above this floor and absolutely below it.
-ABS_FLOOR = 2.0 ** -14
-
-
-def _bf16_ulps(a, b):
-    """bf16 ulps between got and ref, 0 where they differ by less than ABS_FLOOR."""
-    a = np.asarray(a, dtype=np.float32)
-    b = np.asarray(b, dtype=np.float32)
-    ia = (a.view(np.uint32) >> 16).astype(np.int64)
-    ib = (b.view(np.uint32) >> 16).astype(np.int64)
-    u = np.abs(ia - ib)
-    return np.where(np.abs(a.astype(np.float64) - b.astype(np.float64)) < ABS_FLOOR, 0, u)
-
-
-def _worst(got, ref):
-    u = _bf16_ulps(got, ref)
-    i = np.unravel_index(int(np.argmax(u)), u.shape)
-    return "worst %d ulp at %s: got %r ref %r" % (int(u[i]), i, float(got[i]), float(ref[i]))
 
 
 def _project_round(r: RoundRunner, slot_first=0, nslots=None):

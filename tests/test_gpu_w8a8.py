@@ -1,0 +1,258 @@
+"""GPU parity of the W8A8 path against the fp64 oracle, through the C ABI:
+the per-row e4m3 quantiser (wf_quantize_rows_fp8) and the fused projection +
+RoPE + publish over e4m3 operands (wf_qkv_project_publish_w8a8).
+
+The quantiser decides integers from floating point, so both sides decide in
+the same precision (the IEEE fp32 quotient x / scale) and codes and scales
+must be bit-identical. The projection then starts from the same codes on both
+sides: the oracle sums the dequantised products in fp64; the kernel sums code
+products on the e4m3 MFMA, which does not add its 64 products exactly. Probed
+on controlled inputs, one v_mfma_f32_32x32x64_f8f6f4 returns its dot product
+within 2^-12 of the instruction's largest product (small products are dropped
+below a fixed number of bits under the largest, as if aligned to it), while
+the fp32 accumulator add is exact. So each element of the projection may
+differ from the exact one by up to ACC_REL * sum_c |x^_c w^_c| (2x the probed
+worst case), and a published element is bounded by that (after RoPE: the sum
+over its channel pair) plus one bf16 ulp. End to end, attention over the W8A8
+publish meets the bf16 bar (max-abs 1e-2, rel-L2 5e-3, fp32 output mode)
+against the oracle's attention over the oracle's W8A8 projection.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import wf_inputs as W
+from oracle import (RoundSchedule, bf16_round, fp8_e4m3_decode, oracle_round, project_qkv_w8a8,
+                    quantize_rows_fp8, rope_3d, rotate_chunk, split_qkv, token_grid)
+
+from _gpu_round import (RoundRunner, bf16_dev_bits_to_f32, err_stats, gpu_rows, oracle_rows, position_rows,
+                        read_pages, to_dev)
+
+pytestmark = pytest.mark.gpu
+
+BF16_MAX_ABS = 1e-2
+BF16_REL_L2 = 5e-3
+ACC_REL = 2.0 ** -11      # e4m3 MFMA summation error per sum of |products|
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    assert torch.cuda.is_available(), "GPU tests need a ROCm device"
+    import wavefront_causal_attention_amd as wf
+    wf.load()
+    yield
+
+
+def _rows(seed, rows, cols):
+    """bf16-exact rows over many binades, with an all-zero row, a row whose one
+    outlier sends the rest to e4m3 subnormals, and rows whose quotients sit
+    next to e4m3 midpoints (the fp32 reciprocal would round them one code up)."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((rows, cols)).astype(np.float32)
+    x *= np.exp2(rng.integers(-30, 30, (rows, 1))).astype(np.float32)
+    x[0] = 0.0
+    if rows > 1:
+        x[1] = rng.standard_normal(cols).astype(np.float32) * np.float32(1e-3)
+        x[1, cols // 2] = 9.0
+    if rows > 4:
+        for r, (amax, v) in zip((2, 3, 4), ((1.1875, 0.111328125), (2.375, 0.890625),
+                                            (0.0673828125, -0.050537109375))):
+            x[r] = rng.uniform(-0.5, 0.5, cols).astype(np.float32) * np.float32(amax)
+            x[r, 0], x[r, 1:8] = amax, v
+    return W.round_to_bf16(x)
+
+
+@pytest.mark.parametrize("rows,cols,x_stride,code_stride", [
+    (37, 1536, 1536, 1536),       # Wan2.1-1.3B width, a partial last workgroup of rows
+    (3, 8, 16, 16),               # the narrowest row, padded strides
+    (9, 8192, 8192, 8192),        # the widest row the quantiser holds
+    (130, 5120, 5128, 5136),      # Wan2.1-14B width, padded strides
+])
+def test_quantize_rows_bit_exact(rows, cols, x_stride, code_stride):
+    import wavefront_causal_attention_amd as wf
+    say("case quantize rows", rows, "cols", cols, "strides", x_stride, code_stride)
+    x = _rows(40 + rows, rows, cols)
+    xp = np.full((rows, x_stride), 3.0e38, dtype=np.float32)       # padding the kernel must not read
+    xp[:, :cols] = x
+    xd = to_dev(xp, "bf16")
+    codes = torch.full((rows, code_stride), 0xAB, dtype=torch.uint8, device="cuda")
+    scales = torch.full((rows + 1,), -7.0, dtype=torch.float32, device="cuda")
+    wf.wf_quantize_rows_fp8(xd, rows, cols, x_stride, codes, code_stride, scales, None)
+    torch.cuda.synchronize()
+    ref_c, ref_s = quantize_rows_fp8(x)
+    got_c = codes.cpu().numpy()
+    got_s = scales.cpu().numpy()
+    bad = np.argwhere(got_c[:, :cols] != ref_c)
+    assert len(bad) == 0, "%d codes differ, first at %s: got %d ref %d" % (
+        len(bad), tuple(bad[0]), got_c[tuple(bad[0])], ref_c[tuple(bad[0])])
+    assert np.array_equal(got_s[:rows].view(np.uint32), ref_s.view(np.uint32))
+    assert (got_c[:, cols:] == 0xAB).all() and got_s[rows] == -7.0
+
+
+def _w8a8_round(r: RoundRunner, slot_first=0, nslots=None, with_bias=True):
+    """W8A8 projection + publish of live slots [slot_first, +nslots): the
+    hidden states and the weight are quantised on the GPU, checked bit-exact
+    against the oracle's quantiser, and the oracle's fp64 (q, k, v) of every
+    live slot is returned."""
+    import wavefront_causal_attention_amd as wf
+    w = r.w
+    nslots = w.S + 1 - slot_first if nslots is None else nslots
+    xs = [W.draw_hidden(w, r.k, s) for s in range(w.S + 1)]
+    wt, b = W.projection_weights(w)
+    b = b if with_bias else None
+    xd = to_dev(np.concatenate(xs[slot_first:slot_first + nslots], 0), "bf16")
+    x8, sx = wf.quantize_rows_fp8(xd)
+    w8, sw = wf.quantize_rows_fp8(to_dev(wt, "bf16"))
+    bd = to_dev(b, "bf16") if with_bias else None
+    r.pool.project_publish_w8a8(0, slot_first, nslots, x8, x8.stride(0), sx, w.hd, w8, sw, bd, q_out=r.q)
+    torch.cuda.synchronize()
+    wc, ws = quantize_rows_fp8(wt)
+    assert np.array_equal(w8.cpu().numpy(), wc) and np.array_equal(sw.cpu().numpy(), ws)
+    q8 = [quantize_rows_fp8(x) for x in xs]
+    assert np.array_equal(x8.cpu().numpy(), np.concatenate([q8[s][0] for s in range(slot_first, slot_first + nslots)]))
+    assert np.array_equal(sx.cpu().numpy(), np.concatenate([q8[s][1] for s in range(slot_first, slot_first + nslots)]))
+    live = [tuple(split_qkv(project_qkv_w8a8(q8[s][0], q8[s][1], wc, ws, b), w.hd)) for s in range(w.S + 1)]
+    r.live = live
+    wabs = np.abs(fp8_e4m3_decode(wc) * ws.astype(np.float64)[:, None])
+    r.absum = lambda s, rows=slice(None): (np.abs(fp8_e4m3_decode(q8[s][0][rows]) *
+                                                  q8[s][1][rows].astype(np.float64)[:, None]) @ wabs.T)
+    return live
+
+
+def _bf16_ulp(v):
+    """Spacing of bfloat16 values at |v| (normal range)."""
+    _, e = np.frexp(np.maximum(np.abs(v), 2.0 ** -126))
+    return np.ldexp(1.0, e - 8)
+
+
+def _pair_sum(a):
+    """Per channel, the sum over its RoPE pair (2m, 2m+1) along the last axis."""
+    p = a.reshape(a.shape[:-1] + (a.shape[-1] // 2, 2)).sum(-1)
+    return np.repeat(p, 2, axis=-1)
+
+
+def _bound_check(got, ref, acc_bound, what):
+    """|got - ref| <= one bf16 ulp + the e4m3 MFMA summation bound; returns
+    (elements that differ, elements, worst share of the allowance used)."""
+    got = np.asarray(got, dtype=np.float64)
+    err = np.abs(got - ref)
+    allow = _bf16_ulp(np.maximum(np.abs(got), np.abs(ref))) + acc_bound
+    use = err / allow
+    i = np.unravel_index(int(np.argmax(use)), use.shape)
+    assert use[i] <= 1.0, "%s: %s got %r ref %r err %.3e allowed %.3e (acc %.3e)" % (
+        what, i, got[i], ref[i], err[i], allow[i], acc_bound[i])
+    return int(np.count_nonzero(err)), err.size, float(use[i])
+
+
+def _check_pages(r, live, slots):
+    w = r.w
+    sch = RoundSchedule(w.S, w.A, w.H, r.k)
+    kp, vp = read_pages(r.pool, w)
+    table = r.pool.table.cpu().numpy()
+    qf = bf16_dev_bits_to_f32(r.q)
+    total = diff = 0
+    worst = 0.0
+    for s in slots:
+        c = sch.slot_chunk(s)
+        q, k, v = live[s]
+        a = ACC_REL * r.absum(s)                           # [N, 3 h d]
+        heads = lambda m: m.reshape(w.N, w.heads, w.head_dim).transpose(1, 0, 2)
+        p = w.T - 1 - s
+        refs = [(qf[s], bf16_round(rotate_chunk(w, c, q)).transpose(1, 0, 2), _pair_sum(heads(a[:, :w.hd])), "Q"),
+                (position_rows(kp, table, p, r.pool.ppc), bf16_round(rotate_chunk(w, c, k)).transpose(1, 0, 2),
+                 _pair_sum(heads(a[:, w.hd:2 * w.hd])), "K"),
+                (position_rows(vp, table, p, r.pool.ppc), bf16_round(v.reshape(w.N, w.heads, w.head_dim)).transpose(1, 0, 2),
+                 heads(a[:, 2 * w.hd:]), "V")]
+        for got, ref, bound, what in refs:
+            d, t, u = _bound_check(got, ref, bound, "slot %d %s" % (s, what))
+            diff, total, worst = diff + d, total + t, max(worst, u)
+    return diff, total, worst
+
+
+@pytest.mark.parametrize("name,with_bias", [("tiny", True), ("ragged128", True), ("ragged64", False),
+                                            ("edge_s1_h0", True)])
+def test_w8a8_project_publish_pages_match_oracle(name, with_bias):
+    w = W.WORKLOADS[name]
+    say("case", name, "W8A8 projection: Q and pages, bias", with_bias)
+    r = RoundRunner(w)
+    live = _w8a8_round(r, with_bias=with_bias)
+    diff, total, worst = _check_pages(r, live, range(w.S + 1))
+    say(name, "elements differing from the oracle: %d of %d; worst share of the allowance %.3f" % (diff, total, worst))
+
+
+def test_w8a8_slot_subset():
+    w = W.WORKLOADS["ragged128"]
+    say("case ragged128, W8A8 projection: slots 1..S-1")
+    r = RoundRunner(w)
+    live = _w8a8_round(r, slot_first=1, nslots=w.S - 1)
+    diff, total, worst = _check_pages(r, live, range(1, w.S))
+    say("elements differing from the oracle: %d of %d; worst share of the allowance %.3f" % (diff, total, worst))
+
+
+@pytest.mark.parametrize("name", ["tiny", "ragged128", "edge_s1_h0"])
+def test_w8a8_round_parity(name):
+    w = W.WORKLOADS[name]
+    say("case", name, "W8A8 projection: full round")
+    r = RoundRunner(w)
+    r.seed_clean()
+    live = _w8a8_round(r)
+    out = r.attention("fp32")
+    ref = oracle_round(w, r.k, live, r.clean_for_round(), storage="bf16")
+    g = gpu_rows(out, w, np.arange(w.N))
+    assert not np.isnan(g).any()
+    mx, rel = err_stats(g, ref)
+    say(name, "max_abs %.3e rel_l2 %.3e" % (mx, rel))
+    assert mx <= BF16_MAX_ABS and rel <= BF16_REL_L2
+
+
+def test_w8a8_full_size_sampled():
+    """Wan2.1-1.3B S = 4: W8A8 projection of all five live slots; pages on
+    sampled tokens against the oracle's W8A8 projection, attention on sampled
+    rows and heads against the oracle over the whole projected context."""
+    w = W.WORKLOADS["wan1.3b_s4"]
+    say("case wan1.3b_s4, W8A8 projection, full size")
+    r = RoundRunner(w)
+    r.seed_clean()
+    live = _w8a8_round(r)
+    out = r.attention("fp32")
+    rng = np.random.default_rng(22)
+    toks = np.array(sorted(set([0, 1, 255, 256, 4607, 4608, w.N - 1] + list(rng.integers(0, w.N, 40)))))
+    sch = RoundSchedule(w.S, w.A, w.H, r.k)
+    kp, vp = read_pages(r.pool, w)
+    table = r.pool.table.cpu().numpy()
+    qf = bf16_dev_bits_to_f32(r.q)
+    diff = total = 0
+    worst = 0.0
+    heads = lambda m: m.reshape(len(toks), w.heads, w.head_dim).transpose(1, 0, 2)
+    for s in range(w.S + 1):
+        c = sch.slot_chunk(s)
+        t, y, x = token_grid(c, w.chunk_frames, w.frame_h, w.frame_w)
+        q, k, v = (a.reshape(w.N, w.heads, w.head_dim)[toks] for a in live[s])
+        a = ACC_REL * r.absum(s, toks)
+        qr = bf16_round(rope_3d(q, t[toks], y[toks], x[toks], w.rope_split, w.rope_theta))
+        kr = bf16_round(rope_3d(k, t[toks], y[toks], x[toks], w.rope_split, w.rope_theta))
+        p = w.T - 1 - s
+        for got, ref, bound, what in (
+                (qf[s][:, toks], qr.transpose(1, 0, 2), _pair_sum(heads(a[:, :w.hd])), "Q"),
+                (position_rows(kp, table, p, r.pool.ppc)[:, toks], kr.transpose(1, 0, 2),
+                 _pair_sum(heads(a[:, w.hd:2 * w.hd])), "K"),
+                (position_rows(vp, table, p, r.pool.ppc)[:, toks], bf16_round(v).transpose(1, 0, 2),
+                 heads(a[:, 2 * w.hd:]), "V")):
+            d, tt, u = _bound_check(got, ref, bound, "slot %d %s" % (s, what))
+            diff, total, worst = diff + d, total + tt, max(worst, u)
+    say("sampled elements differing from the oracle: %d of %d; worst share of the allowance %.3f" % (diff, total, worst))
+    rows = np.array(sorted(set([0, 255, 256, 4607, 4608, w.N - 1] + list(rng.integers(0, w.N, 10)))))
+    heads = [0, 7]
+    ref = oracle_rows(w, r.k, live, r.clean_for_round(), rows, heads=heads)
+    g = gpu_rows(out, w, rows, heads=heads)
+    mx, rel = err_stats(g, ref)
+    say("attention rows", len(rows), "heads", heads, "max_abs %.3e rel_l2 %.3e" % (mx, rel))
+    assert mx <= BF16_MAX_ABS and rel <= BF16_REL_L2
+    assert torch.isfinite(out).all().item()

@@ -11,7 +11,7 @@ from ._lib import (WF_DTYPE_BF16, WF_DTYPE_FP32, WF_DTYPE_FP8_E4M3, WF_E_HIP, WF
                    WF_E_NOT_READY, WF_E_SHAPE, WF_MASK_ALL_LIVE, WF_MASK_WAVEFRONT, WF_OK, WfError,
                    load, wf_attention_round, wf_attention_work_list, wf_config,
                    wf_geometry, wf_kv_publish, wf_page_table_host, wf_pool_bytes, wf_pool_create,
-                   wf_qkv_project_publish,
+                   wf_qkv_project_publish, wf_qkv_project_publish_w8a8, wf_quantize_rows_fp8,
                    wf_pool_create_host_model, wf_pool_destroy, wf_ready_mask, wf_round_advance,
                    wf_round_index, wf_schedule_chunk_ids)
 
@@ -96,6 +96,11 @@ class Pool:
         wf_qkv_project_publish(self.handle, layer, slot_first, nslots, x, x_row_stride, hidden, w, bias,
                                chunk_t0, q_out, stream)
 
+    def project_publish_w8a8(self, layer, slot_first, nslots, x8, x_row_stride, x_scales, hidden, w8, w_scales,
+                             bias=None, q_out=None, chunk_t0=None, stream=None):
+        wf_qkv_project_publish_w8a8(self.handle, layer, slot_first, nslots, x8, x_row_stride, x_scales, hidden,
+                                    w8, w_scales, bias, chunk_t0, q_out, stream)
+
     def attention(self, layer, slot_first, nslots, q, out, q_scales=None, stream=None):
         import torch
         od = WF_DTYPE_FP32 if out.dtype == torch.float32 else WF_DTYPE_BF16
@@ -115,3 +120,18 @@ class Pool:
 
     def ready_mask(self, layer=0):
         return wf_ready_mask(self.handle, layer)
+
+
+def quantize_rows_fp8(x, codes=None, scales=None, stream=None):
+    """Per-row e4m3 codes and fp32 scales of a 2-D bf16 device tensor (rows
+    16-byte aligned), for the W8A8 projection. Returns (codes uint8 [rows,
+    cols] with 16-byte row pitch, scales float32 [rows])."""
+    import torch
+    rows, cols = x.shape
+    if codes is None:
+        pitch = (cols + 15) // 16 * 16
+        codes = torch.empty((rows, pitch), dtype=torch.uint8, device=x.device)[:, :cols]
+    if scales is None:
+        scales = torch.empty(rows, dtype=torch.float32, device=x.device)
+    wf_quantize_rows_fp8(x, rows, cols, x.stride(0), codes, codes.stride(0), scales, stream)
+    return codes, scales

@@ -81,6 +81,8 @@ def load() -> ctypes.CDLL:
         "wf_pool_destroy": (None, [P]),
         "wf_kv_publish": (ctypes.c_int, [P, I32, I32, I32, P, P, P, I64, P, P, P, P]),
         "wf_qkv_project_publish": (ctypes.c_int, [P, I32, I32, I32, P, I64, I32, P, P, P, P, P]),
+        "wf_qkv_project_publish_w8a8": (ctypes.c_int, [P, I32, I32, I32, P, I64, P, I32, P, P, P, P, P, P]),
+        "wf_quantize_rows_fp8": (ctypes.c_int, [P, I64, I32, I64, P, I64, P, P]),
         "wf_attention_round": (ctypes.c_int, [P, I32, I32, I32, P, P, P, I32, P]),
         "wf_round_advance": (ctypes.c_int, [P, P]),
         "wf_attention_work_list": (ctypes.c_int, [ctypes.POINTER(wf_config), I32, I32, I32, P, I64,
@@ -177,6 +179,24 @@ def wf_qkv_project_publish(h, layer, slot_first, nslots, x, x_row_stride_elems, 
            "wf_qkv_project_publish", h)
 
 
+def wf_qkv_project_publish_w8a8(h, layer, slot_first, nslots, x8, x_row_stride, x_scales, hidden, w8, w_scales,
+                                bias=None, chunk_t0=None, q_out=None, stream=None) -> None:
+    t0 = None
+    if chunk_t0 is not None:
+        arr = (ctypes.c_int32 * len(chunk_t0))(*[int(v) for v in chunk_t0])
+        t0 = ctypes.cast(arr, ctypes.c_void_p)
+    _check(load().wf_qkv_project_publish_w8a8(h, layer, slot_first, nslots, _ptr(x8), int(x_row_stride),
+                                              _ptr(x_scales), int(hidden), _ptr(w8), _ptr(w_scales), _ptr(bias),
+                                              t0, _ptr(q_out), _stream(stream)),
+           "wf_qkv_project_publish_w8a8", h)
+
+
+def wf_quantize_rows_fp8(x, rows, cols, x_row_stride, codes, code_row_stride, scales, stream=None) -> None:
+    _check(load().wf_quantize_rows_fp8(_ptr(x), int(rows), int(cols), int(x_row_stride), _ptr(codes),
+                                       int(code_row_stride), _ptr(scales), _stream(stream)),
+           "wf_quantize_rows_fp8")
+
+
 def wf_attention_round(h, layer, slot_first, nslots, q, q_scales, out, out_dtype, stream=None) -> None:
     _check(load().wf_attention_round(h, layer, slot_first, nslots, _ptr(q), _ptr(q_scales),
                                      _ptr(out), int(out_dtype), _stream(stream)),
@@ -233,7 +253,8 @@ def wf_geometry(h):
 
 EXPORTED = [
     "wf_pool_bytes", "wf_pool_create", "wf_pool_create_host_model", "wf_pool_destroy",
-    "wf_kv_publish", "wf_qkv_project_publish", "wf_attention_round", "wf_round_advance", "wf_round_index",
+    "wf_kv_publish", "wf_qkv_project_publish", "wf_qkv_project_publish_w8a8", "wf_quantize_rows_fp8",
+    "wf_attention_round", "wf_round_advance", "wf_round_index",
     "wf_attention_work_list",
     "wf_schedule_chunk_ids", "wf_page_table_host", "wf_ready_mask", "wf_geometry",
     "wf_status_string", "wf_last_error",

@@ -479,26 +479,32 @@ int wf_kv_publish(wf_handle* h, int32_t layer, int32_t slot_first, int32_t nslot
     return WF_OK;
 }
 
-int wf_qkv_project_publish(wf_handle* h, int32_t layer, int32_t slot_first, int32_t nslots,
-                           const void* x, int64_t x_row_stride_elems, int32_t hidden, const void* w,
-                           const void* bias, const int32_t* chunk_t0_host, void* q_out, void* stream) {
+// The fused projection + publish, bf16 operands or (f8) e4m3 codes with
+// per-row scales xs / ws.
+static int project_publish(wf_handle* h, int32_t layer, int32_t slot_first, int32_t nslots, const void* x,
+                           int64_t x_row_stride_elems, const float* xs, int32_t hidden, const void* w,
+                           const float* ws, const void* bias, const int32_t* chunk_t0_host, void* q_out,
+                           void* stream, bool f8) {
     if (!h) return WF_E_INVALID_ARG;
     const wf_config& c = h->cfg;
     const Layout& L = h->L;
+    const int esz = f8 ? 1 : 2;                    // bytes per operand element
+    const int kstage = 128 / esz;                  // hidden channels per 128-byte stage
     if (layer < 0 || layer >= c.num_layers) return WF_E_INVALID_ARG;
     if (nslots < 1 || slot_first < 0 || slot_first + nslots > c.S + 1) return WF_E_INVALID_ARG;
     if (!x || !w || !q_out) return WF_E_INVALID_ARG;
-    if (hidden < 64 || hidden % 64 != 0 || x_row_stride_elems < hidden) return WF_E_INVALID_ARG;
-    if (((uintptr_t)x | (uintptr_t)w | (uintptr_t)q_out) % 16 || (x_row_stride_elems * 2) % 16 ||
-        ((uintptr_t)bias % 16))
+    if (f8 && (!xs || !ws)) return WF_E_INVALID_ARG;
+    if (hidden < kstage || hidden % kstage != 0 || x_row_stride_elems < hidden) return WF_E_INVALID_ARG;
+    if (((uintptr_t)x | (uintptr_t)w | (uintptr_t)q_out) % 16 || (x_row_stride_elems * esz) % 16 ||
+        ((uintptr_t)bias % 16) || ((uintptr_t)xs % 16) || ((uintptr_t)ws % 16))
         return WF_E_INVALID_ARG;
     const int hd = c.heads * c.head_dim;
     if (c.qk_dtype != WF_DTYPE_BF16 || hd % 128 != 0) return WF_E_SHAPE;
     if (wf::proj_frames_per_tile(c.frame_h * c.frame_w) > wf::kProjMaxFrames) return WF_E_SHAPE;
     if (c.frame_h * (c.rope_split[1] / 2) + c.frame_w * (c.rope_split[2] / 2) > wf::kProjMaxRopeEntries)
         return WF_E_SHAPE;
-    const int64_t xbytes = (((int64_t)nslots * L.N - 1) * x_row_stride_elems + hidden) * 2;
-    const int64_t wbytes = (int64_t)3 * hd * hidden * 2;
+    const int64_t xbytes = (((int64_t)nslots * L.N - 1) * x_row_stride_elems + hidden) * esz;
+    const int64_t wbytes = (int64_t)3 * hd * hidden * esz;
     if (xbytes >= ((int64_t)1 << 31) || wbytes >= ((int64_t)1 << 31)) return WF_E_SHAPE;
     for (int i = 0; i < nslots; ++i)
         if (!h->present(h->position_of_slot(slot_first + i))) {
@@ -515,11 +521,13 @@ int wf_qkv_project_publish(wf_handle* h, int32_t layer, int32_t slot_first, int3
         a.t0[i] = (int)t0;
     }
     if (!h->host_model) {
-        a.x = (const uint16_t*)x;
+        a.x = x;
         a.x_stride = x_row_stride_elems;
         a.xbytes = (int32_t)xbytes;
-        a.w = (const uint16_t*)w;
+        a.w = w;
         a.wbytes = (int32_t)wbytes;
+        a.xs = xs;
+        a.ws = ws;
         a.bias = (const uint16_t*)bias;
         a.q_out = q_out;
         a.kpage = h->pool + L.k_off + L.k_layer * layer;
@@ -547,11 +555,42 @@ int wf_qkv_project_publish(wf_handle* h, int32_t layer, int32_t slot_first, int3
             const int nr = (mg + 1) * a.mrows / a.g_mt - mg * a.mrows / a.g_mt;
             per = std::max(per, nc * nr);
         }
-        const hipError_t e = wf::launch_project(a, per * wf::kXcds, (hipStream_t)stream);
-        if (e != hipSuccess) return h->fail_hip(e, "wf_qkv_project_publish launch");
+        const hipError_t e = wf::launch_project(a, f8, per * wf::kXcds, (hipStream_t)stream);
+        if (e != hipSuccess)
+            return h->fail_hip(e, f8 ? "wf_qkv_project_publish_w8a8 launch" : "wf_qkv_project_publish launch");
     }
     for (int i = 0; i < nslots; ++i) h->ready[layer] |= 1ull << h->position_of_slot(slot_first + i);
     return WF_OK;
+}
+
+int wf_qkv_project_publish(wf_handle* h, int32_t layer, int32_t slot_first, int32_t nslots,
+                           const void* x, int64_t x_row_stride_elems, int32_t hidden, const void* w,
+                           const void* bias, const int32_t* chunk_t0_host, void* q_out, void* stream) {
+    return project_publish(h, layer, slot_first, nslots, x, x_row_stride_elems, nullptr, hidden, w, nullptr,
+                           bias, chunk_t0_host, q_out, stream, false);
+}
+
+int wf_qkv_project_publish_w8a8(wf_handle* h, int32_t layer, int32_t slot_first, int32_t nslots,
+                                const void* x8, int64_t x_row_stride, const float* x_scales, int32_t hidden,
+                                const void* w8, const float* w_scales, const void* bias,
+                                const int32_t* chunk_t0_host, void* q_out, void* stream) {
+    return project_publish(h, layer, slot_first, nslots, x8, x_row_stride, x_scales, hidden, w8, w_scales,
+                           bias, chunk_t0_host, q_out, stream, true);
+}
+
+int wf_quantize_rows_fp8(const void* x, int64_t rows, int32_t cols, int64_t x_row_stride_elems,
+                         uint8_t* codes, int64_t code_row_stride, float* scales, void* stream) {
+    if (rows < 0 || !x || !codes || !scales) return WF_E_INVALID_ARG;
+    if (cols < 8 || cols % 8 != 0 || cols > wf::kQuantMaxCols) return WF_E_SHAPE;
+    if (x_row_stride_elems < cols || x_row_stride_elems % 8 != 0 || code_row_stride < cols ||
+        code_row_stride % 8 != 0)
+        return WF_E_INVALID_ARG;
+    if ((uintptr_t)x % 16 || (uintptr_t)codes % 8 || (uintptr_t)scales % 4) return WF_E_INVALID_ARG;
+    if (rows > INT32_MAX) return WF_E_SHAPE;
+    if (rows == 0) return WF_OK;
+    const hipError_t e = wf::launch_quant_rows((const uint16_t*)x, rows, cols, x_row_stride_elems, codes,
+                                               code_row_stride, scales, (hipStream_t)stream);
+    return e == hipSuccess ? WF_OK : WF_E_HIP;
 }
 
 int wf_attention_round(wf_handle* h, int32_t layer, int32_t slot_first, int32_t nslots,

@@ -101,11 +101,13 @@ constexpr int kProjChannels = 256;   // output channels per projection workgroup
 constexpr int kProjMaxFrames = 8;    // latent frames one tile may touch (time table in LDS)
 constexpr int kProjMaxRopeEntries = 2048;  // frame_h*dh/2 + frame_w*dw/2 (row/column tables in LDS)
 struct ProjArgs {
-    const uint16_t* x;        // hidden states [nslots * N][x_stride] bf16
+    const void* x;            // hidden states [nslots * N][x_stride], bf16 or e4m3 codes
     int64_t x_stride;         // elements between token rows
     int32_t xbytes;           // bytes readable from x (< 2^31)
-    const uint16_t* w;        // weight [3 * heads * D][hidden] bf16 ([out][in])
+    const void* w;            // weight [3 * heads * D][hidden] ([out][in]), bf16 or e4m3 codes
     int32_t wbytes;           // bytes of w (< 2^31)
+    const float* xs;          // e4m3 operands: scale per row of x [nslots * N]
+    const float* ws;          // e4m3 operands: scale per output channel [3 * heads * D]
     const uint16_t* bias;     // [3 * heads * D] bf16, or NULL
     void* q_out;              // [S+1][heads][N][D] bf16
     void* kpage;              // this layer's K pages
@@ -125,7 +127,12 @@ struct ProjArgs {
     int t0[kMaxSlots];        // RoPE time offset per slot
 };
 int proj_frames_per_tile(int hw);
-hipError_t launch_project(const ProjArgs& a, int nblocks, hipStream_t st);
+// f8: x and w are e4m3 codes with per-row scales (xs, ws), else bf16
+hipError_t launch_project(const ProjArgs& a, bool f8, int nblocks, hipStream_t st);
+
+constexpr int kQuantMaxCols = 8192;  // row width of the per-row e4m3 quantiser (held in registers)
+hipError_t launch_quant_rows(const uint16_t* x, int64_t rows, int cols, int64_t x_stride, uint8_t* codes,
+                             int64_t code_stride, float* scales, hipStream_t st);
 
 hipError_t launch_page_table(int32_t* table, int T, int A, int ppc, int64_t ring, int store_pos,
                              int store_anchor, hipStream_t st);

@@ -1,4 +1,5 @@
-// QKV projection with RoPE and publish as its epilogue, gfx950: bf16 MFMA.
+// QKV projection with RoPE and publish as its epilogue, gfx950: bf16 MFMA, or
+// fp8 e4m3 MFMA for W8A8 operands.
 //
 // The pages publish K/V right after the QKV projection and RoPE (Wave
 // Forcing, hyper.ai summary, section "Method", WaveRT paragraph; e-cogni.com.br,
@@ -25,11 +26,20 @@
 // Both orientations read the same LDS fragments (16 bytes = 8 consecutive
 // hidden channels of one row of x or w) and only swap the MFMA operands.
 //
-// Operands arrive by LDS DMA in 64-channel stages, double-buffered. A
-// stage holds rows of 128 bytes; 16-byte vector kv of row r sits in slot
-// kv ^ ((r >> 1) & 7), so that each DMA instruction reads eight whole rows
-// (eight 128-byte lines of x or w) and the fragment reads of 16 lanes (16
+// Operands arrive by LDS DMA in stages of 128 bytes per row (64 bf16 or 128
+// e4m3 hidden channels), double-buffered. 16-byte vector kv of row r sits in
+// slot kv ^ ((r >> 1) & 7), so that each DMA instruction reads eight whole
+// rows (eight 128-byte lines of x or w) and the fragment reads of 16 lanes (16
 // consecutive rows, one kv) fall on 16 distinct 16-byte bank groups.
+//
+// W8A8 (the pages pair 8-bit weights and activations with the quantised
+// attention: e-cogni.com.br, "Como funciona"; thelatestinai.com listing,
+// Table 6): x and w hold e4m3 codes with one fp32 scale per row of each
+// (per token, per output channel). The stage layout and DMA are the same
+// bytes; each lane feeds v_mfma_f32_32x32x64_f8f6f4 with 32 consecutive codes
+// (two 16-byte vectors), and the epilogue multiplies every accumulator by its
+// token's and channel's scales before the bias, so the products of codes are
+// summed exactly as the bf16 path sums products of values.
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
@@ -41,11 +51,12 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 
 constexpr int PM = kProjTokens;   // tokens per workgroup tile
 constexpr int PC = kProjChannels; // output channels per workgroup tile
-constexpr int BK = 64;            // hidden channels per stage
+constexpr int BK = 64;            // bf16 hidden channels per stage (128 bytes per row)
 constexpr int PNT = 512;          // threads per workgroup (8 waves)
 constexpr int XI = PM / 8 / 8;    // x DMA instructions per wave per stage (8 rows each)
 constexpr int WI = PC / 8 / 8;    // w DMA instructions per wave per stage
@@ -110,9 +121,14 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, r);
 }
 __device__ __forceinline__ float bf_to_f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+__device__ __forceinline__ i32x8 as_i32x8(uint4 a, uint4 b) {
+    return i32x8{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
+}
 
-template <int D>
+template <int D, bool F8>
 __global__ __launch_bounds__(PNT, 1) void proj_publish_kernel(ProjArgs a) {
+    constexpr int ESZ = F8 ? 1 : 2;               // bytes per operand element
+    constexpr int BKE = 128 / ESZ;                // hidden channels per stage
     // ---- which tile: XCD x takes a block of (token-tile rows x channel tiles)
     const int xcd = blockIdx.x % kXcds, j = blockIdx.x / kXcds;
     const int cg = xcd % a.g_ct, mg = xcd / a.g_ct;
@@ -175,18 +191,18 @@ __global__ __launch_bounds__(PNT, 1) void proj_publish_kernel(ProjArgs a) {
         const int r = (wave * XI + i) * 8 + (lane >> 3);
         const int kv = (lane & 7) ^ ((r >> 1) & 7);
         const int n = n0 + r;
-        xoff[i] = n < N ? (uint32_t)((((int64_t)sr * N + n) * a.x_stride + kv * 8) * 2) : kOOB;
+        xoff[i] = n < N ? (uint32_t)(((int64_t)sr * N + n) * a.x_stride * ESZ + kv * 16) : kOOB;
     }
 #pragma unroll
     for (int i = 0; i < WI; ++i) {
         const int r = (wave * WI + i) * 8 + (lane >> 3);
         const int kv = (lane & 7) ^ ((r >> 1) & 7);
         const int o = ct * PC + r;
-        woff[i] = o < 3 * hd ? (uint32_t)((((int64_t)o) * a.hidden + kv * 8) * 2) : kOOB;
+        woff[i] = o < 3 * hd ? (uint32_t)((int64_t)o * a.hidden * ESZ + kv * 16) : kOOB;
     }
     auto dma_stage = [&](auto I, int kt) {
         constexpr int B = decltype(I)::value;
-        const uint32_t kb = (uint32_t)kt * BK * 2;
+        const uint32_t kb = (uint32_t)kt * 128;
         uint8_t* xl = reinterpret_cast<uint8_t*>(xbuf<B>());
         uint8_t* wl = reinterpret_cast<uint8_t*>(wbuf<B>());
 #pragma unroll
@@ -194,7 +210,7 @@ __global__ __launch_bounds__(PNT, 1) void proj_publish_kernel(ProjArgs a) {
 #pragma unroll
         for (int i = 0; i < WI; ++i) dma16(wrs, wl + (wave * WI + i) * 1024, woff[i] + kb);
     };
-    const int nk = a.hidden / BK;
+    const int nk = a.hidden / BKE;
     dma_stage(std::integral_constant<int, 0>{}, 0);
 
     if (tt) {
@@ -223,6 +239,45 @@ __global__ __launch_bounds__(PNT, 1) void proj_publish_kernel(ProjArgs a) {
         stage_barrier();
         const uint8_t* xl = reinterpret_cast<const uint8_t*>(xbuf<B>());
         const uint8_t* wl = reinterpret_cast<const uint8_t*>(wbuf<B>());
+        if constexpr (F8) {
+            // two 64-code K steps; lane half hf supplies codes 32 hf .. 32 hf + 31
+            // of each, i.e. vectors 4 ks + 2 hf and 4 ks + 2 hf + 1 of its row
+            uint4 xf8[2][2][2], wf8[2][4][2];
+            auto rd8 = [&](int ks) {
+                const int kv = 4 * ks + 2 * hf;
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+#pragma unroll
+                    for (int u = 0; u < 2; ++u)
+                        xf8[ks][i][u] = *reinterpret_cast<const uint4*>(xl + swz(wm * 64 + i * 32 + l32, kv + u));
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+                    for (int u = 0; u < 2; ++u)
+                        wf8[ks][jj][u] = *reinterpret_cast<const uint4*>(wl + swz(wc * 128 + jj * 32 + l32, kv + u));
+            };
+            rd8(0);
+            __builtin_amdgcn_sched_barrier(0);
+            if (kt + 1 < nk) dma_stage(std::integral_constant<int, B ^ 1>{}, kt + 1);
+            __builtin_amdgcn_sched_barrier(0);
+            rd8(1);
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) {
+                        const i32x8 xa = as_i32x8(xf8[ks][i][0], xf8[ks][i][1]);
+                        const i32x8 wa = as_i32x8(wf8[ks][jj][0], wf8[ks][jj][1]);
+                        if constexpr (decltype(TR)::value)
+                            acc[i][jj] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wa, xa, acc[i][jj],
+                                                                                        0, 0, 0, 0, 0, 0);
+                        else
+                            acc[i][jj] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(xa, wa, acc[i][jj],
+                                                                                        0, 0, 0, 0, 0, 0);
+                    }
+            return;
+        }
         bf16x8 xf[BK / 16][2], wf_[BK / 16][4];
         auto rd = [&](int ks) {
             const int kv = ks * 2 + hf;
@@ -264,7 +319,8 @@ __global__ __launch_bounds__(PNT, 1) void proj_publish_kernel(ProjArgs a) {
     __syncthreads();                               // stage buffers free, time table visible
     if (!live) return;
 
-    // ---- epilogue: bias, RoPE (Q, K), bf16, then out to the Q buffer / pages,
+    // ---- epilogue: (e4m3: token and channel scales,) bias, RoPE (Q, K), bf16,
+    // then out to the Q buffer / pages,
     // in two passes of 64 channels. Each wave stages a 64 x 64 bf16 block in
     // LDS in the destination's order and writes it out with 16-byte stores:
     // 1 KB contiguous per K or V instruction, 128-byte row pieces for Q.
@@ -282,6 +338,7 @@ __global__ __launch_bounds__(PNT, 1) void proj_publish_kernel(ProjArgs a) {
             for (int i = 0; i < 2; ++i) {
                 const int t = i * 32 + l32;
                 const int n = min(tb + t, N - 1);
+                const float sxt = F8 ? a.xs[(int64_t)sr * N + n] : 1.f;
                 const int f = n / HW - f_lo;
                 const int yy = (n / a.frame_w) % a.frame_h;
                 const int xw = n % a.frame_w;
@@ -293,11 +350,18 @@ __global__ __launch_bounds__(PNT, 1) void proj_publish_kernel(ProjArgs a) {
                         const int d0 = (cb + cl) % D;
                         const uint2 bq = a.bias ? *reinterpret_cast<const uint2*>(a.bias + oc + cl) : make_uint2(0, 0);
                         const f32x16& A = acc[i][2 * h2 + jj];
-                        float v[4];
-                        v[0] = A[4 * g + 0] + __uint_as_float(bq.x << 16);
-                        v[1] = A[4 * g + 1] + __uint_as_float(bq.x & 0xFFFF0000u);
-                        v[2] = A[4 * g + 2] + __uint_as_float(bq.y << 16);
-                        v[3] = A[4 * g + 3] + __uint_as_float(bq.y & 0xFFFF0000u);
+                        float v[4] = {A[4 * g + 0], A[4 * g + 1], A[4 * g + 2], A[4 * g + 3]};
+                        if constexpr (F8) {
+                            const float4 sw = *reinterpret_cast<const float4*>(a.ws + oc + cl);
+                            v[0] = v[0] * sxt * sw.x;
+                            v[1] = v[1] * sxt * sw.y;
+                            v[2] = v[2] * sxt * sw.z;
+                            v[3] = v[3] * sxt * sw.w;
+                        }
+                        v[0] += __uint_as_float(bq.x << 16);
+                        v[1] += __uint_as_float(bq.x & 0xFFFF0000u);
+                        v[2] += __uint_as_float(bq.y << 16);
+                        v[3] += __uint_as_float(bq.y & 0xFFFF0000u);
 #pragma unroll
                         for (int pr = 0; pr < 2; ++pr) {
                             const int dc = d0 + 2 * pr;
@@ -349,15 +413,25 @@ __global__ __launch_bounds__(PNT, 1) void proj_publish_kernel(ProjArgs a) {
             for (int jj = 0; jj < 2; ++jj) {
                 const int c = jj * 32 + l32;
                 const float bb = a.bias ? bf_to_f(a.bias[oc + c]) : 0.f;
+                const float swc = F8 ? a.ws[oc + c] : 1.f;
 #pragma unroll
                 for (int i = 0; i < 2; ++i)
 #pragma unroll
                     for (int g = 0; g < 4; ++g) {
                         const f32x16& Ai = acc[i][2 * h2 + jj];
                         const int chunk = i * 4 + g;                        // tokens 8*chunk + 4*hf .. +3
+                        float v[4] = {Ai[4 * g], Ai[4 * g + 1], Ai[4 * g + 2], Ai[4 * g + 3]};
+                        if constexpr (F8) {
+                            // N is a multiple of 8: these 4 tokens are all inside the chunk or all past it
+                            const int n4 = min(tb + 8 * chunk + 4 * hf, N - 4);
+                            const float4 sx = *reinterpret_cast<const float4*>(a.xs + (int64_t)sr * N + n4);
+                            v[0] = v[0] * sx.x * swc;
+                            v[1] = v[1] * sx.y * swc;
+                            v[2] = v[2] * sx.z * swc;
+                            v[3] = v[3] * sx.w * swc;
+                        }
                         *reinterpret_cast<uint2*>(st + c * 128 + ((chunk ^ (c & 7)) << 4) + hf * 8) =
-                            make_uint2(pack_bf16x2(Ai[4 * g] + bb, Ai[4 * g + 1] + bb),
-                                       pack_bf16x2(Ai[4 * g + 2] + bb, Ai[4 * g + 3] + bb));
+                            make_uint2(pack_bf16x2(v[0] + bb, v[1] + bb), pack_bf16x2(v[2] + bb, v[3] + bb));
                     }
             }
             // V pages [phys][head][pt/8][D][8]: one lane per channel, one 8-token group per store
@@ -376,15 +450,85 @@ __global__ __launch_bounds__(PNT, 1) void proj_publish_kernel(ProjArgs a) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// Per-row e4m3 quantisation of W8A8 operands (a token row of the activations,
+// an output-channel row of the weights). One wave per row, held in registers:
+// the row's absmax is reduced across the wave, scale = absmax / 448 (IEEE
+// divide; 1 for an all-zero row), and every code is decided on the IEEE fp32
+// quotient x / scale, rounded to nearest even and saturated at +-448.
+constexpr int QV = kQuantMaxCols / 8 / 64;     // 16-byte vectors per lane
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+    return v;
+}
+
+__device__ __forceinline__ uint32_t code2(float p, float q) {
+    // v_cvt_pk_fp8_f32 rounds to nearest even; out-of-range inputs would
+    // become NaN, so saturate first
+    p = fminf(fmaxf(p, -448.f), 448.f);
+    q = fminf(fmaxf(q, -448.f), 448.f);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(p, q, 0, false) & 0xFFFFu;
+}
+
+__global__ __launch_bounds__(256) void quant_rows_kernel(const uint16_t* x, int64_t rows, int cols,
+                                                         int64_t x_stride, uint8_t* codes,
+                                                         int64_t code_stride, float* scales) {
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= rows) return;                       // whole waves
+    const int lane = threadIdx.x & 63;
+    const int nv = cols >> 3;
+    const uint16_t* xr = x + row * x_stride;
+    uint4 v[QV];
+    uint32_t amax_bits = 0;                        // |bf16| bit patterns order like their values
+#pragma unroll
+    for (int i = 0; i < QV; ++i) {
+        const int vi = lane + 64 * i;
+        v[i] = vi < nv ? *reinterpret_cast<const uint4*>(xr + vi * 8) : make_uint4(0, 0, 0, 0);
+        const uint32_t w4[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            amax_bits = max(amax_bits, max(w4[e] & 0x7FFFu, (w4[e] >> 16) & 0x7FFFu));
+    }
+    const float amax = wave_max(__uint_as_float(amax_bits << 16));
+    const float sc = amax > 0.f ? amax / 448.f : 1.f;
+    uint8_t* cr = codes + row * code_stride;
+#pragma unroll
+    for (int i = 0; i < QV; ++i) {
+        const int vi = lane + 64 * i;
+        if (vi >= nv) continue;
+        const uint32_t w4[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+        uint32_t c[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            c[e] = code2(__uint_as_float(w4[e] << 16) / sc, __uint_as_float(w4[e] & 0xFFFF0000u) / sc);
+        *reinterpret_cast<uint2*>(cr + vi * 8) = make_uint2(c[0] | (c[1] << 16), c[2] | (c[3] << 16));
+    }
+    if (lane == 0) scales[row] = sc;
+}
+
 }  // namespace
 
 int proj_frames_per_tile(int hw) { return (PM - 1) / hw + 2; }
 
-hipError_t launch_project(const ProjArgs& a, int nblocks, hipStream_t st) {
-    if (a.D == 128)
-        hipLaunchKernelGGL((proj_publish_kernel<128>), dim3(nblocks), dim3(PNT), 0, st, a);
+hipError_t launch_quant_rows(const uint16_t* x, int64_t rows, int cols, int64_t x_stride, uint8_t* codes,
+                             int64_t code_stride, float* scales, hipStream_t st) {
+    const int64_t blocks = (rows + 3) / 4;
+    hipLaunchKernelGGL(quant_rows_kernel, dim3((unsigned)blocks), dim3(256), 0, st, x, rows, cols, x_stride,
+                       codes, code_stride, scales);
+    return hipGetLastError();
+}
+
+hipError_t launch_project(const ProjArgs& a, bool f8, int nblocks, hipStream_t st) {
+    if (a.D == 128 && f8)
+        hipLaunchKernelGGL((proj_publish_kernel<128, true>), dim3(nblocks), dim3(PNT), 0, st, a);
+    else if (a.D == 128)
+        hipLaunchKernelGGL((proj_publish_kernel<128, false>), dim3(nblocks), dim3(PNT), 0, st, a);
+    else if (a.D == 64 && f8)
+        hipLaunchKernelGGL((proj_publish_kernel<64, true>), dim3(nblocks), dim3(PNT), 0, st, a);
     else if (a.D == 64)
-        hipLaunchKernelGGL((proj_publish_kernel<64>), dim3(nblocks), dim3(PNT), 0, st, a);
+        hipLaunchKernelGGL((proj_publish_kernel<64, false>), dim3(nblocks), dim3(PNT), 0, st, a);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();
