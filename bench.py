@@ -25,6 +25,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "wavefront-round attention TFLOP/s + rounds/sec, 1 MI355X, Wan2.1-1.3B S=4 shape"
 PEAK_BF16_TFLOPS = 2500.0          # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0           # MI355X dense fp8 MFMA
 PEAK_HBM_GBPS = 8000.0             # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_bf16_wan1.3b_s4_traffic.txt")
 # the attention kernel and the host code that orders its work (the order
@@ -71,9 +72,11 @@ def parse():
     ap.add_argument("--layers", type=int, default=1,
                     help="layers sharing one pool and page table; a step is then one model round "
                          "(publish + attention of every layer, one advance)")
-    ap.add_argument("--project", action="store_true",
+    ap.add_argument("--project", nargs="?", const="bf16", default=None, choices=["bf16", "w8a8"],
                     help="publish through the fused QKV projection (hidden states -> RoPE'd Q/K/V pages) "
-                         "instead of from a projection output; also times hipBLASLt addmm + publish")
+                         "instead of from a projection output; also times hipBLASLt addmm + publish. "
+                         "w8a8: the hidden states are quantised to e4m3 per token each step and the "
+                         "projection runs on e4m3 operands (weight quantised once, per output channel)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=1536, help="query rows per (slot, head) in the CPU sample")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -140,6 +143,9 @@ def main():
         wt_np, b_np = W.projection_weights(w)
         wproj = torch.from_numpy(wt_np).to(torch.bfloat16).to(dev)            # [3hd, hidden]
         bproj = torch.from_numpy(b_np).to(torch.bfloat16).to(dev)
+        if args.project == "w8a8":
+            w8, sw8 = wf.quantize_rows_fp8(wproj)                              # once, like a checkpoint
+            x8, sx8 = wf.quantize_rows_fp8(xh)                                 # buffers reused every step
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()
@@ -150,7 +156,11 @@ def main():
         for layer in range(L):
             if ev is not None and layer == 0:
                 ev[0].record(stream)
-            if args.project:
+            if args.project == "w8a8":
+                wf.quantize_rows_fp8(xh, x8, sx8, stream=stream)
+                pool.project_publish_w8a8(layer, 0, w.S + 1, x8, x8.stride(0), sx8, w.hd, w8, sw8, bproj,
+                                          q_out=q, stream=stream)
+            elif args.project:
                 pool.project_publish(layer, 0, w.S + 1, xh, w.hd, w.hd, wproj, bproj, q_out=q, stream=stream)
             else:
                 pool.publish(layer, 0, w.S + 1, qd, kd, vd, stride, q_out=q, q_scales=qs, stream=stream)
@@ -196,10 +206,10 @@ def main():
     proj = None
     if args.project:
         # the same projection unfused: hipBLASLt addmm to a [tokens, 3hd] bf16
-        # output, then the publish kernel reads it back
+        # output, then the publish kernel reads it back; and each part alone
         wT = wproj.t().contiguous()                                   # [hidden, 3hd]
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-        mm, pb = [], []
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+        parts = {"addmm": [], "publish": [], "bf16_fused": [], "quantize": [], "w8a8": []}
         for i in range(K + 2):
             ev[0].record(stream)
             y = torch.addmm(bproj, xh, wT)
@@ -207,21 +217,51 @@ def main():
             pool.publish(0, 0, w.S + 1, y[:, :w.hd], y[:, w.hd:2 * w.hd], y[:, 2 * w.hd:], 3 * w.hd,
                          q_out=q, stream=stream)
             ev[2].record(stream)
+            pool.project_publish(0, 0, w.S + 1, xh, w.hd, w.hd, wproj, bproj, q_out=q, stream=stream)
+            ev[3].record(stream)
+            if args.project == "w8a8":
+                wf.quantize_rows_fp8(xh, x8, sx8, stream=stream)
+                ev[4].record(stream)
+                pool.project_publish_w8a8(0, 0, w.S + 1, x8, x8.stride(0), sx8, w.hd, w8, sw8, bproj,
+                                          q_out=q, stream=stream)
+                ev[5].record(stream)
             torch.cuda.synchronize()
             if i >= 2:
-                mm.append(ev[0].elapsed_time(ev[1]))
-                pb.append(ev[1].elapsed_time(ev[2]))
+                parts["addmm"].append(ev[0].elapsed_time(ev[1]))
+                parts["publish"].append(ev[1].elapsed_time(ev[2]))
+                parts["bf16_fused"].append(ev[2].elapsed_time(ev[3]))
+                if args.project == "w8a8":
+                    parts["quantize"].append(ev[3].elapsed_time(ev[4]))
+                    parts["w8a8"].append(ev[4].elapsed_time(ev[5]))
+        avg = {k: float(np.mean(v)) for k, v in parts.items() if v}
         pf = 2.0 * (w.S + 1) * w.N * 3 * w.hd * w.hd
         fused_ms = float(np.mean(pub_ms))
-        proj = {"fused_ms": round(fused_ms, 4),
-                "fused_tflops": round(pf / (fused_ms * 1e-3) / 1e12, 1),
-                "roofline": {"bound": "mfma", "achieved": round(pf / (fused_ms * 1e-3) / 1e12, 1),
-                             "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                             "frac": round(pf / (fused_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)},
-                "flops": pf,
-                "unfused_addmm_ms": round(float(np.mean(mm)), 4),
-                "unfused_publish_ms": round(float(np.mean(pb)), 4),
-                "unfused_ms": round(float(np.mean(mm)) + float(np.mean(pb)), 4)}
+        if args.project == "w8a8":
+            tf = pf / (avg["w8a8"] * 1e-3) / 1e12
+            qbytes = (w.S + 1) * w.N * w.hd * 3 + (w.S + 1) * w.N * 4     # read bf16, write codes + scales
+            proj = {"mode": "w8a8",
+                    "step_ms": round(fused_ms, 4),
+                    "quantize_ms": round(avg["quantize"], 4),
+                    "quantize_gbps": round(qbytes / (avg["quantize"] * 1e-3) / 1e9, 1),
+                    "w8a8_projection_ms": round(avg["w8a8"], 4),
+                    "w8a8_tflops": round(tf, 1),
+                    "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": PEAK_FP8_TFLOPS,
+                                 "unit": "TFLOP/s", "frac": round(tf / PEAK_FP8_TFLOPS, 4)},
+                    "flops": pf,
+                    "bf16_fused_ms": round(avg["bf16_fused"], 4),
+                    "unfused_addmm_ms": round(avg["addmm"], 4),
+                    "unfused_publish_ms": round(avg["publish"], 4),
+                    "unfused_ms": round(avg["addmm"] + avg["publish"], 4)}
+        else:
+            proj = {"fused_ms": round(fused_ms, 4),
+                    "fused_tflops": round(pf / (fused_ms * 1e-3) / 1e12, 1),
+                    "roofline": {"bound": "mfma", "achieved": round(pf / (fused_ms * 1e-3) / 1e12, 1),
+                                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                                 "frac": round(pf / (fused_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)},
+                    "flops": pf,
+                    "unfused_addmm_ms": round(avg["addmm"], 4),
+                    "unfused_publish_ms": round(avg["publish"], 4),
+                    "unfused_ms": round(avg["addmm"] + avg["publish"], 4)}
 
     if args.calibrate_copy_mib > 0:
         nb = args.calibrate_copy_mib * (1 << 20)
@@ -271,7 +311,8 @@ def main():
     }
     if proj is not None:
         res["projection"] = proj
-        res["config"]["publish"] = "fused QKV projection + RoPE + publish"
+        res["config"]["publish"] = ("per-token e4m3 quantisation + W8A8 fused QKV projection + RoPE + publish"
+                                    if args.project == "w8a8" else "fused QKV projection + RoPE + publish")
         del res["publish_roofline"]
         del res["publish_gbps"]
     if not args.no_cpu_baseline:
