@@ -257,8 +257,27 @@ int wf_attention_round(wf_handle* h, int32_t layer, int32_t slot_first, int32_t 
  * when the store holds a chunk; WF_E_INVALID_ARG past the last round of a
  * C-chunk video. Live slots become unpublished; history keeps its readiness; a
  * stored anchor chunk stays published at its anchor position.
+ *
+ * The rotation is driven by a round counter in the pool's device memory, from
+ * which the publish launches of live slots also take their chunks' RoPE time
+ * offsets (unless chunk_t0_host is given). A round's launches captured into a
+ * HIP graph (publish or projection, attention, this advance) therefore stay
+ * right when the graph is replayed in later rounds. Called on a stream that is
+ * capturing, the advance is enqueued and the host state is left in the
+ * captured round: call wf_round_replayed after every replay. Only steady
+ * rounds (every position holds a chunk, the store holds no anchor chunk, this
+ * round and the next) can be captured (WF_E_INVALID_ARG otherwise).
  */
 int wf_round_advance(wf_handle* h, void* stream);
+
+/*
+ * Host bookkeeping for one replay of a captured round (see wf_round_advance):
+ * the host state moves to the next round as the replayed advance left the
+ * device, with the replayed round's store taken as published in every layer.
+ * Launches nothing. WF_E_INVALID_ARG for a round that is not steady or the
+ * last round of a video.
+ */
+int wf_round_replayed(wf_handle* h);
 
 /*
  * Attention launch order (host only, no handle or device needed): the list

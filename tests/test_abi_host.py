@@ -462,3 +462,60 @@ def test_quantize_rows_validates_before_any_launch(lib, kw, status):
 
 def test_quantize_rows_zero_rows_launches_nothing(lib):
     wf.wf_quantize_rows_fp8(FAKE, 0, 64, 64, FAKE, 64, FAKE, 0)
+
+
+def _publish_live(h, w, layers=1):
+    for layer in range(layers):
+        wf.wf_kv_publish(h, layer, 0, w.S + 1, FAKE, FAKE, FAKE, w.hd, None, FAKE, None, None)
+
+
+@pytest.mark.parametrize("layers", [1, 2])
+def test_round_replayed_leaves_the_host_where_eager_rounds_do(lib, layers):
+    """A captured round publishes every live slot, attends and advances once;
+    its replays run without the host. After each replay wf_round_replayed must
+    leave the host state (round, readiness per layer, page groups) exactly where
+    the same rounds run eagerly leave it."""
+    w = W.WORKLOADS["ragged128"]
+    eager = wf.wf_pool_create_host_model(cfg_of(w, num_layers=layers))
+    graph = wf.wf_pool_create_host_model(cfg_of(w, num_layers=layers))
+    try:
+        npages = w.T * (w.N // w.page_tokens)
+        for h in (eager, graph):                       # seed anchor and history
+            for layer in range(layers):
+                wf.wf_kv_publish(h, layer, w.S + 1, w.T - w.S - 1, None, FAKE, FAKE, w.hd, None, None, None, None)
+        _publish_live(graph, w, layers)                # the captured round's publishes
+        for r in range(2 * w.T + 1):
+            _publish_live(eager, w, layers)
+            for layer in range(layers):
+                wf.wf_attention_round(eager, layer, 0, w.S + 1, FAKE, None, FAKE, wf.WF_DTYPE_FP32, None)
+            wf.wf_round_advance(eager, None)
+            wf.wf_round_replayed(graph)
+            assert wf.wf_round_index(graph) == wf.wf_round_index(eager)
+            for layer in range(layers):
+                assert wf.wf_ready_mask(graph, layer) == wf.wf_ready_mask(eager, layer), (r, layer)
+            assert wf.wf_page_table_host(graph, npages) == wf.wf_page_table_host(eager, npages)
+            assert wf.wf_schedule_chunk_ids(graph, w.T) == wf.wf_schedule_chunk_ids(eager, w.T)
+        # after the replays the graph pool's host state takes eager calls again
+        _publish_live(graph, w, layers)
+        wf.wf_attention_round(graph, 0, 0, w.S + 1, FAKE, None, FAKE, wf.WF_DTYPE_FP32, None)
+        wf.wf_round_advance(graph, None)
+    finally:
+        wf.wf_pool_destroy(eager)
+        wf.wf_pool_destroy(graph)
+
+
+def test_round_replayed_only_in_steady_rounds(lib):
+    w = W.WORKLOADS["tiny"]
+    fill = wf.wf_pool_create_host_model(cfg_of(w, first_round=0))      # fill rounds: positions empty
+    last = wf.wf_pool_create_host_model(cfg_of(w, first_round=w.S + w.H + w.A, total_chunks=w.S + w.H + w.A + 1))
+    try:
+        with pytest.raises(wf.WfError) as e:
+            wf.wf_round_replayed(fill)
+        assert e.value.status == wf.WF_E_INVALID_ARG and wf.wf_round_index(fill) == 0
+        # steady now, but the next round starts the drain: not replayable
+        with pytest.raises(wf.WfError) as e:
+            wf.wf_round_replayed(last)
+        assert e.value.status == wf.WF_E_INVALID_ARG
+    finally:
+        wf.wf_pool_destroy(fill)
+        wf.wf_pool_destroy(last)

@@ -13,7 +13,7 @@ from ._lib import (WF_DTYPE_BF16, WF_DTYPE_FP32, WF_DTYPE_FP8_E4M3, WF_E_HIP, WF
                    wf_geometry, wf_kv_publish, wf_page_table_host, wf_pool_bytes, wf_pool_create,
                    wf_qkv_project_publish, wf_qkv_project_publish_w8a8, wf_quantize_rows_fp8,
                    wf_pool_create_host_model, wf_pool_destroy, wf_ready_mask, wf_round_advance,
-                   wf_round_index, wf_schedule_chunk_ids)
+                   wf_round_index, wf_round_replayed, wf_schedule_chunk_ids)
 
 _DT = {"bf16": WF_DTYPE_BF16, "fp32": WF_DTYPE_FP32, "fp8": WF_DTYPE_FP8_E4M3}
 
@@ -108,6 +108,10 @@ class Pool:
 
     def advance(self, stream=None):
         wf_round_advance(self.handle, stream)
+
+    def round_replayed(self):
+        """Host bookkeeping after one replay of a captured round."""
+        wf_round_replayed(self.handle)
 
     def round_index(self):
         return wf_round_index(self.handle)

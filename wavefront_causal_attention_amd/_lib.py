@@ -85,6 +85,7 @@ def load() -> ctypes.CDLL:
         "wf_quantize_rows_fp8": (ctypes.c_int, [P, I64, I32, I64, P, I64, P, P]),
         "wf_attention_round": (ctypes.c_int, [P, I32, I32, I32, P, P, P, I32, P]),
         "wf_round_advance": (ctypes.c_int, [P, P]),
+        "wf_round_replayed": (ctypes.c_int, [P]),
         "wf_attention_work_list": (ctypes.c_int, [ctypes.POINTER(wf_config), I32, I32, I32, P, I64,
                                                   ctypes.POINTER(I64)]),
         "wf_round_index": (ctypes.c_int, [P, ctypes.POINTER(I64)]),
@@ -207,6 +208,10 @@ def wf_round_advance(h, stream=None) -> None:
     _check(load().wf_round_advance(h, _stream(stream)), "wf_round_advance", h)
 
 
+def wf_round_replayed(h) -> None:
+    _check(load().wf_round_replayed(h), "wf_round_replayed", h)
+
+
 def wf_round_index(h) -> int:
     k = ctypes.c_int64()
     _check(load().wf_round_index(h, ctypes.byref(k)), "wf_round_index")
@@ -254,7 +259,7 @@ def wf_geometry(h):
 EXPORTED = [
     "wf_pool_bytes", "wf_pool_create", "wf_pool_create_host_model", "wf_pool_destroy",
     "wf_kv_publish", "wf_qkv_project_publish", "wf_qkv_project_publish_w8a8", "wf_quantize_rows_fp8",
-    "wf_attention_round", "wf_round_advance", "wf_round_index",
+    "wf_attention_round", "wf_round_advance", "wf_round_replayed", "wf_round_index",
     "wf_attention_work_list",
     "wf_schedule_chunk_ids", "wf_page_table_host", "wf_ready_mask", "wf_geometry",
     "wf_status_string", "wf_last_error",

@@ -25,6 +25,7 @@ struct Layout {
     size_t scale_off = 0, mean_off = 0, part_off = 0;        // fp8 metadata
     size_t scale_layer = 0, mean_layer = 0, part_layer = 0;
     size_t htab_off = 0, wtab_off = 0, omega_off = 0;
+    size_t ring_off = 0;                   // device round counter (int64): advances since creation
     size_t work_off = 0, work_stride = 0;  // attention work lists, one per slot range
     int work_len = 0;                      // entries per list
     size_t pool_bytes = 0, table_bytes = 0;
@@ -227,6 +228,7 @@ int validate(const wf_config* c, Layout* L) {
     L->htab_off = off;  off += align_up((size_t)c->frame_h * (dh / 2) * 8 + 8, 256);
     L->wtab_off = off;  off += align_up((size_t)c->frame_w * (dw / 2) * 8 + 8, 256);
     L->omega_off = off; off += align_up((size_t)(dt / 2) * 8 + 8, 256);
+    L->ring_off = off;  off += 256;
     {
         const int qtiles = (int)((N + wf::kAttnBM - 1) / wf::kAttnBM);
         const int64_t units = (int64_t)(c->S + 1) * c->heads * qtiles;
@@ -302,6 +304,13 @@ struct wf_handle {
         return A() + (int)(((int64_t)(p - A()) + ring) % L.R);
     }
     uint64_t prefix_bits(int n) const { return n >= 64 ? ~0ull : ((1ull << n) - 1); }
+    int64_t* ring_dev() const { return host_model ? nullptr : (int64_t*)(pool + L.ring_off); }
+    // every position holds a chunk and the store holds no anchor chunk
+    bool steady_at_round(int64_t k) const {
+        for (int p = 0; p < L.T; ++p)
+            if (!present_at_round(p, k)) return false;
+        return store_anchor_at_round(k) < 0;
+    }
 
     int fail_hip(hipError_t e, const char* what) {
         snprintf(err, sizeof err, "%s: %s", what, hipGetErrorString(e));
@@ -385,6 +394,8 @@ int wf_pool_create(const wf_config* cfg, void* pool_dev, size_t pool_bytes,
         e = hipMemcpy(h->pool + L.wtab_off, wtab.data(), wtab.size() * 4, hipMemcpyHostToDevice);
     if (e == hipSuccess)
         e = hipMemcpy(h->pool + L.omega_off, om.data(), om.size() * 8, hipMemcpyHostToDevice);
+    const int64_t ring0 = 0;
+    if (e == hipSuccess) e = hipMemcpy(h->pool + L.ring_off, &ring0, sizeof ring0, hipMemcpyHostToDevice);
     const int qtiles = (L.N + wf::kAttnBM - 1) / wf::kAttnBM;
     int cus = 0;
     if (e == hipSuccess) {
@@ -403,7 +414,7 @@ int wf_pool_create(const wf_config* cfg, void* pool_dev, size_t pool_bytes,
                           wl.data(), wl.size() * 4, hipMemcpyHostToDevice);
         }
     if (e == hipSuccess)
-        e = wf::launch_page_table(h->table, L.T, cfg->anchor_chunks, L.ppc, h->ring,
+        e = wf::launch_page_table(h->table, L.T, cfg->anchor_chunks, L.ppc, h->ring, nullptr,
                                   cfg->anchor_chunks + cfg->history_chunks,
                                   h->store_anchor_at_round(h->round()), nullptr);
     if (e == hipSuccess) e = hipDeviceSynchronize();
@@ -450,6 +461,13 @@ int wf_kv_publish(wf_handle* h, int32_t layer, int32_t slot_first, int32_t nslot
                                : (int64_t)c.chunk_frames * h->chunk_at(h->position_of_slot(slot_first + i));
         if (t0 < 0 || t0 > INT32_MAX / 2) return WF_E_INVALID_ARG;
         a.t0[i] = (int)t0;
+    }
+    // live slots take their chunk id from the device round counter (the same
+    // values in eager use; right in every round a captured launch replays)
+    if (!chunk_t0_host && slot_first + nslots <= c.S + 1) {
+        a.ring = h->ring_dev();
+        a.t0_round = c.first_round - slot_first;
+        a.chunk_frames = c.chunk_frames;
     }
     if (!h->host_model) {
         a.q = q; a.k = k; a.v = v;
@@ -519,6 +537,13 @@ static int project_publish(wf_handle* h, int32_t layer, int32_t slot_first, int3
                                : (int64_t)c.chunk_frames * h->chunk_at(h->position_of_slot(slot_first + i));
         if (t0 < 0 || t0 > INT32_MAX / 2) return WF_E_INVALID_ARG;
         a.t0[i] = (int)t0;
+    }
+    // live slots take their chunk id from the device round counter (the same
+    // values in eager use; right in every round a captured launch replays)
+    if (!chunk_t0_host && slot_first + nslots <= c.S + 1) {
+        a.ring = h->ring_dev();
+        a.t0_round = c.first_round - slot_first;
+        a.chunk_frames = c.chunk_frames;
     }
     if (!h->host_model) {
         a.x = x;
@@ -669,29 +694,13 @@ int wf_attention_round(wf_handle* h, int32_t layer, int32_t slot_first, int32_t 
     return WF_OK;
 }
 
-int wf_round_advance(wf_handle* h, void* stream) {
-    if (!h) return WF_E_INVALID_ARG;
+// Host side of an advance: one more round, readiness as the advance leaves
+// it (anchor kept, history one cleaner, the store's chunk the newest history
+// or its anchor, live slots cleared, empty positions unready).
+static void advance_host(wf_handle* h) {
     const int A = h->A(), H = h->H();
     const int store = A + H;
-    const int64_t k = h->round();
-    if (h->cfg.total_chunks > 0 && k + 1 > (int64_t)h->cfg.total_chunks - 1 + h->S()) {
-        snprintf(h->err, sizeof h->err, "round %lld is the last of a %d-chunk video", (long long)k,
-                 h->cfg.total_chunks);
-        return WF_E_INVALID_ARG;
-    }
-    const bool store_held = h->present(store);
-    const int store_anchor = h->store_anchor_at_round(k);
-    if (store_held)
-        for (int l = 0; l < h->cfg.num_layers; ++l)
-            if (!(h->ready[l] >> store & 1)) {
-                snprintf(h->err, sizeof h->err, "layer %d: store not published", l);
-                return WF_E_NOT_READY;
-            }
-    if (!h->host_model) {
-        const hipError_t e = wf::launch_page_table(h->table, h->L.T, A, h->L.ppc, h->ring + 1, store,
-                                                   h->store_anchor_at_round(k + 1), (hipStream_t)stream);
-        if (e != hipSuccess) return h->fail_hip(e, "wf_round_advance launch");
-    }
+    const int store_anchor = h->store_anchor_at_round(h->round());
     h->ring += 1;
     for (int l = 0; l < h->cfg.num_layers; ++l) {
         const uint64_t old = h->ready[l];
@@ -706,6 +715,68 @@ int wf_round_advance(wf_handle* h, void* stream) {
             if (!h->present(p)) nw &= ~(1ull << p);
         h->ready[l] = nw;                                            // live slots cleared
     }
+}
+
+static int check_not_last(wf_handle* h) {
+    const int64_t k = h->round();
+    if (h->cfg.total_chunks > 0 && k + 1 > (int64_t)h->cfg.total_chunks - 1 + h->S()) {
+        snprintf(h->err, sizeof h->err, "round %lld is the last of a %d-chunk video", (long long)k,
+                 h->cfg.total_chunks);
+        return WF_E_INVALID_ARG;
+    }
+    return WF_OK;
+}
+
+static int check_steady(wf_handle* h) {
+    const int64_t k = h->round();
+    if (!h->steady_at_round(k) || !h->steady_at_round(k + 1)) {
+        snprintf(h->err, sizeof h->err, "round %lld: only steady rounds (every position held, no anchor "
+                 "stored) can be captured and replayed", (long long)k);
+        return WF_E_INVALID_ARG;
+    }
+    return WF_OK;
+}
+
+int wf_round_advance(wf_handle* h, void* stream) {
+    if (!h) return WF_E_INVALID_ARG;
+    const int A = h->A(), H = h->H();
+    const int store = A + H;
+    const int64_t k = h->round();
+    int st = check_not_last(h);
+    if (st != WF_OK) return st;
+    if (h->present(store))
+        for (int l = 0; l < h->cfg.num_layers; ++l)
+            if (!(h->ready[l] >> store & 1)) {
+                snprintf(h->err, sizeof h->err, "layer %d: store not published", l);
+                return WF_E_NOT_READY;
+            }
+    bool capturing = false;
+    if (!h->host_model) {
+        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+        hipError_t e = hipStreamIsCapturing((hipStream_t)stream, &cs);
+        if (e != hipSuccess) return h->fail_hip(e, "wf_round_advance capture query");
+        capturing = cs == hipStreamCaptureStatusActive;
+        if (capturing && (st = check_steady(h)) != WF_OK) return st;
+        e = wf::launch_page_table(h->table, h->L.T, A, h->L.ppc, h->ring + 1, h->ring_dev(), store,
+                                  h->store_anchor_at_round(k + 1), (hipStream_t)stream);
+        if (e != hipSuccess) return h->fail_hip(e, "wf_round_advance launch");
+    }
+    // a captured advance moves the device counter only when it runs; the host
+    // follows each replay through wf_round_replayed
+    if (!capturing) advance_host(h);
+    return WF_OK;
+}
+
+int wf_round_replayed(wf_handle* h) {
+    if (!h) return WF_E_INVALID_ARG;
+    int st = check_not_last(h);
+    if (st == WF_OK) st = check_steady(h);
+    if (st != WF_OK) return st;
+    // the replayed round published every layer's store (its advance checked
+    // that when it was captured)
+    const int store = h->A() + h->H();
+    for (int l = 0; l < h->cfg.num_layers; ++l) h->ready[l] |= 1ull << store;
+    advance_host(h);
     return WF_OK;
 }
 

@@ -66,8 +66,19 @@ struct PublishArgs {
     int slot_first, nslots;
     int in_fp32;              // 1: input fp32, 0: bf16
     int nblk;                 // fp8 blocks per chunk
-    int t0[kMaxSlots];        // RoPE time offset per published slot
+    int t0[kMaxSlots];        // RoPE time offset per published slot (ring == NULL)
+    // live slots: the time offsets follow the pool's device round counter,
+    // t0 = chunk_frames * (ring + t0_round - i) for published slot i, so a
+    // captured launch stays right when it is replayed in later rounds
+    const int64_t* ring;
+    int64_t t0_round;         // first_round - slot_first
+    int chunk_frames;
 };
+// RoPE time offset of published slot i of a launch
+template <typename Args>
+__device__ __forceinline__ int slot_t0(const Args& a, int i) {
+    return a.ring ? a.chunk_frames * (int)(a.ring[0] + a.t0_round - i) : a.t0[i];
+}
 
 // Attention over the paged context for `nslots` query slots of one layer.
 struct AttnArgs {
@@ -124,7 +135,10 @@ struct ProjArgs {
     int ctiles;               // 256-channel tiles of the 3 * heads * D outputs (the last may be half)
     int mrows;                // nslots * mtiles
     int g_ct, g_mt;           // XCD blocking: channel-tile groups x token-row groups = 8
-    int t0[kMaxSlots];        // RoPE time offset per slot
+    int t0[kMaxSlots];        // RoPE time offset per slot (ring == NULL)
+    const int64_t* ring;      // as for PublishArgs
+    int64_t t0_round;
+    int chunk_frames;
 };
 int proj_frames_per_tile(int hw);
 // f8: x and w are e4m3 codes with per-row scales (xs, ws), else bf16
@@ -134,7 +148,9 @@ constexpr int kQuantMaxCols = 8192;  // row width of the per-row e4m3 quantiser 
 hipError_t launch_quant_rows(const uint16_t* x, int64_t rows, int cols, int64_t x_stride, uint8_t* codes,
                              int64_t code_stride, float* scales, hipStream_t st);
 
-hipError_t launch_page_table(int32_t* table, int T, int A, int ppc, int64_t ring, int store_pos,
+// ring_dev == NULL: write the table for ring offset `ring`; else for the
+// device counter's value + 1, then store that value back (one block)
+hipError_t launch_page_table(int32_t* table, int T, int A, int ppc, int64_t ring, int64_t* ring_dev, int store_pos,
                              int store_anchor, hipStream_t st);
 hipError_t launch_publish(const PublishArgs& a, bool fp8, hipStream_t st);
 hipError_t launch_attention(const AttnArgs& a, bool fp8, hipStream_t st);

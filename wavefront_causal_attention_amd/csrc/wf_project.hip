@@ -216,7 +216,7 @@ __global__ __launch_bounds__(PNT, 1) void proj_publish_kernel(ProjArgs a) {
     if (tt) {
         const int fi = tid / hp, m = tid - fi * hp;
         double sn, cs;
-        sincos((double)(a.t0[sr] + f_lo + fi) * om, &sn, &cs);
+        sincos((double)(slot_t0(a, sr) + f_lo + fi) * om, &sn, &cs);
         g_pttab[fi * 32 + m] = make_float2((float)cs, (float)sn);
     }
 

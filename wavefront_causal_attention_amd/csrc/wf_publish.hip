@@ -183,7 +183,7 @@ __global__ __launch_bounds__(256) void publish_bf16_kernel(PublishArgs a) {
         // time-axis angles in fp64: positions grow with the stream
         for (int i = tid; i < nf * hp; i += 256) {
             const int fi = i / hp, m = i - fi * hp;
-            const double phi = (double)(a.t0[sr] + f_lo + fi) * a.omega_t[m];
+            const double phi = (double)(slot_t0(a, sr) + f_lo + fi) * a.omega_t[m];
             double sn, cs;
             sincos(phi, &sn, &cs);
             ttab[fi][m] = make_float2((float)cs, (float)sn);
@@ -202,7 +202,7 @@ __global__ __launch_bounds__(256) void publish_bf16_kernel(PublishArgs a) {
     } else {
         for (int i = tid; i < nf * hp; i += 256) {
             const int fi = i / hp, m = i - fi * hp;
-            const double phi = (double)(a.t0[sr] + f_lo + fi) * a.omega_t[m];
+            const double phi = (double)(slot_t0(a, sr) + f_lo + fi) * a.omega_t[m];
             double sn, cs;
             sincos(phi, &sn, &cs);
             ttab[fi][m] = make_float2((float)cs, (float)sn);
@@ -283,7 +283,7 @@ __device__ __forceinline__ void fill_ttab(float2 (*ttab)[32], const PublishArgs&
     const int hp = a.dt >> 1;
     for (int i = threadIdx.x; i < nf * hp; i += 256) {
         const int fi = i / hp, m = i - fi * hp;
-        const double phi = (double)(a.t0[sr] + f_lo + fi) * a.omega_t[m];
+        const double phi = (double)(slot_t0(a, sr) + f_lo + fi) * a.omega_t[m];
         double sn, cs;
         sincos(phi, &sn, &cs);
         ttab[fi][m] = make_float2((float)cs, (float)sn);
@@ -497,23 +497,32 @@ __global__ __launch_bounds__(256) void publish_fp8_kernel(PublishArgs a) {
 // A + ((p - A + ring) mod (T - A)); while the store holds an anchor chunk
 // (store_anchor >= 0, pipeline fill) the store position writes that anchor's
 // group.
-__global__ void page_table_kernel(int32_t* table, int T, int A, int ppc, int64_t ring, int store_pos,
-                                  int store_anchor) {
-    const int i = blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= T * ppc) return;
-    const int p = i / ppc, pg = i - p * ppc;
+// One block. With a device round counter the ring offset is read from it
+// (the next round's) and written back once every thread has read it, so the
+// same launch advances the pool whichever round it runs in.
+__global__ __launch_bounds__(1024) void page_table_kernel(int32_t* table, int T, int A, int ppc, int64_t ring,
+                                                          int64_t* ring_dev, int store_pos, int store_anchor) {
+    if (ring_dev) ring = ring_dev[0] + 1;
     const int R = T - A;
-    int g = p < A ? p : A + (int)(((int64_t)(p - A) + ring) % R);
-    if (p == store_pos && store_anchor >= 0) g = store_anchor;
-    table[i] = g * ppc + pg;
+    for (int i = threadIdx.x; i < T * ppc; i += blockDim.x) {
+        const int p = i / ppc, pg = i - p * ppc;
+        int g = p < A ? p : A + (int)(((int64_t)(p - A) + ring) % R);
+        if (p == store_pos && store_anchor >= 0) g = store_anchor;
+        table[i] = g * ppc + pg;
+    }
+    if (ring_dev) {
+        __syncthreads();
+        if (threadIdx.x == 0) ring_dev[0] = ring;
+    }
 }
 
 }  // namespace
 
-hipError_t launch_page_table(int32_t* table, int T, int A, int ppc, int64_t ring, int store_pos,
+hipError_t launch_page_table(int32_t* table, int T, int A, int ppc, int64_t ring, int64_t* ring_dev, int store_pos,
                              int store_anchor, hipStream_t st) {
     const int n = T * ppc;
-    hipLaunchKernelGGL(page_table_kernel, dim3((n + 255) / 256), dim3(256), 0, st, table, T, A, ppc, ring,
+    const int threads = n < 1024 ? (n + 63) / 64 * 64 : 1024;
+    hipLaunchKernelGGL(page_table_kernel, dim3(1), dim3(threads), 0, st, table, T, A, ppc, ring, ring_dev,
                        store_pos, store_anchor);
     return hipGetLastError();
 }
