@@ -66,6 +66,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="wan1.3b_s4")
     ap.add_argument("--out-dtype", default="bf16", choices=["bf16", "fp32"])
+    ap.add_argument("--graph", action="store_true",
+                    help="also capture one step in a HIP graph and time its replays (the pool's device round "
+                         "counter advances each replay)")
     ap.add_argument("--live-mask", default="wavefront", choices=["wavefront", "all"],
                     help="all: every live slot reads every live slot (no tile skipped), for "
                          "measuring what the wavefront mask saves")
@@ -152,7 +155,7 @@ def main():
 
     # every layer publishes the same resident projection output into its own
     # pages and attends over them: the work per layer is the real one
-    def step(ev=None):
+    def step(ev=None, stream=stream):
         for layer in range(L):
             if ev is not None and layer == 0:
                 ev[0].record(stream)
@@ -187,6 +190,36 @@ def main():
         step(evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+
+    graph = None
+    if args.graph:
+        # the same step captured once and replayed; each replay is one more round
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step(stream=torch.cuda.current_stream())
+        for _ in range(args.warmup):
+            g.replay()
+            pool.round_replayed()
+        torch.cuda.synchronize()
+        # alternate blocks of K replays and K eager steps, so that clock drift
+        # over the run does not favour either
+        blocks = {"graph": [], "eager": []}
+        ge = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        for b in range(6):
+            mode = "graph" if b % 2 == 0 else "eager"
+            ge[0].record(stream)
+            for _ in range(K):
+                if mode == "graph":
+                    g.replay()
+                    pool.round_replayed()
+                else:
+                    step()
+            ge[1].record(stream)
+            torch.cuda.synchronize()
+            blocks[mode].append(ge[0].elapsed_time(ge[1]) / K)
+        graph = {"replay_stream_ms_per_step": round(float(np.median(blocks["graph"])), 4),
+                 "eager_stream_ms_per_step": round(float(np.median(blocks["eager"])), 4),
+                 "blocks": "3 x %d replays alternated with 3 x %d eager steps, medians" % (K, K)}
 
     pub_ms = [e[0].elapsed_time(e[1]) for e in evs]          # layer 0's kernels
     att_ms = [e[1].elapsed_time(e[2]) for e in evs]
@@ -309,6 +342,8 @@ def main():
                              "frac": round(pub_bytes / (pub_avg * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
                              "algorithmic_bytes": pub_bytes},
     }
+    if graph is not None:
+        res["graph"] = graph
     if proj is not None:
         res["projection"] = proj
         res["config"]["publish"] = ("per-token e4m3 quantisation + W8A8 fused QKV projection + RoPE + publish"
