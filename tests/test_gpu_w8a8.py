@@ -72,6 +72,7 @@ def _rows(seed, rows, cols):
 @pytest.mark.parametrize("rows,cols,x_stride,code_stride", [
     (37, 1536, 1536, 1536),       # Wan2.1-1.3B width, a partial last workgroup of rows
     (3, 8, 16, 16),               # the narrowest row, padded strides
+    (11, 3072, 3080, 3088),       # 8 vectors per lane
     (9, 8192, 8192, 8192),        # the widest row the quantiser holds
     (130, 5120, 5128, 5136),      # Wan2.1-14B width, padded strides
 ])
@@ -256,3 +257,48 @@ def test_w8a8_full_size_sampled():
     say("attention rows", len(rows), "heads", heads, "max_abs %.3e rel_l2 %.3e" % (mx, rel))
     assert mx <= BF16_MAX_ABS and rel <= BF16_REL_L2
     assert torch.isfinite(out).all().item()
+
+
+@pytest.mark.parametrize("name,C", [("tiny", 5), ("edge_s1_h0", 5)])
+def test_w8a8_whole_video(name, C):
+    """Every round of a short video published through the W8A8 projection,
+    from the first fill round to the last drain round: the store's projected
+    K/V becomes anchor or history, and each occupied slot matches the oracle's
+    fill schedule over the positions that hold a chunk."""
+    import wavefront_causal_attention_amd as wf
+    from _gpu_round import config_of
+    w = W.WORKLOADS[name]
+    say("case", name, "W8A8 projection, whole video of", C, "chunks")
+    pool = wf.Pool(config_of(w, first_round=0, total_chunks=C))
+    q = pool.q_buffer()
+    wt, b = W.projection_weights(w)
+    w8, sw = wf.quantize_rows_fp8(to_dev(wt, "bf16"))
+    wc, ws = quantize_rows_fp8(wt)
+    bd = to_dev(b, "bf16")
+    clean = {}
+    for k in range(C + w.S):
+        sch = RoundSchedule(w.S, w.A, w.H, k, fill=True, total_chunks=C)
+        present = [s for s in range(w.S + 1) if sch.slot_present(s)]
+        lo, hi = present[0], present[-1]
+        xs = {s: W.draw_hidden(w, k, s) for s in present}
+        x8, sx = wf.quantize_rows_fp8(to_dev(np.concatenate([xs[s] for s in present], 0), "bf16"))
+        pool.project_publish_w8a8(0, lo, hi - lo + 1, x8, x8.stride(0), sx, w.hd, w8, sw, bd, q_out=q)
+        out = pool.out_buffer("fp32")
+        out.fill_(float("nan"))
+        pool.attention(0, lo, hi - lo + 1, q, out)
+        torch.cuda.synchronize()
+        live = [None] * (w.S + 1)
+        for s in present:
+            c8, s8 = quantize_rows_fp8(xs[s])
+            live[s] = tuple(split_qkv(project_qkv_w8a8(c8, s8, wc, ws, b), w.hd))
+        cl = {c: clean[c] for c in sch.present_chunk_ids()[:w.A + w.H] if c is not None}
+        ref = oracle_round(w, k, live, cl, storage="bf16", fill=True, total_chunks=C, slots=range(lo, hi + 1))
+        o = out.cpu().numpy().reshape(w.S + 1, w.N, w.heads, w.head_dim).astype(np.float64)
+        assert np.isnan(np.delete(o, list(range(lo, hi + 1)), axis=0)).all()
+        mx, rel = err_stats(o[lo:hi + 1], ref)
+        say(name, "round", k, "slots", lo, "..", hi, "max_abs %.3e rel_l2 %.3e" % (mx, rel))
+        assert mx <= BF16_MAX_ABS and rel <= BF16_REL_L2, (k, mx, rel)
+        if w.S in present:
+            clean[sch.slot_chunk(w.S)] = tuple(live[w.S][1:])
+        if k < C - 1 + w.S:
+            pool.advance()

@@ -455,8 +455,10 @@ __global__ __launch_bounds__(PNT, 1) void proj_publish_kernel(ProjArgs a) {
 // an output-channel row of the weights). One wave per row, held in registers:
 // the row's absmax is reduced across the wave, scale = absmax / 448 (IEEE
 // divide; 1 for an all-zero row), and every code is decided on the IEEE fp32
-// quotient x / scale, rounded to nearest even and saturated at +-448.
-constexpr int QV = kQuantMaxCols / 8 / 64;     // 16-byte vectors per lane
+// quotient x / scale, rounded to nearest even and saturated at +-448. QV
+// 16-byte vectors per lane hold the row: the smallest of 4, 8, 16 that fits,
+// so narrow rows leave registers for more waves in flight.
+constexpr int kQuantMaxQV = kQuantMaxCols / 8 / 64;
 
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
@@ -472,6 +474,7 @@ __device__ __forceinline__ uint32_t code2(float p, float q) {
     return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(p, q, 0, false) & 0xFFFFu;
 }
 
+template <int QV>
 __global__ __launch_bounds__(256) void quant_rows_kernel(const uint16_t* x, int64_t rows, int cols,
                                                          int64_t x_stride, uint8_t* codes,
                                                          int64_t code_stride, float* scales) {
@@ -515,8 +518,17 @@ int proj_frames_per_tile(int hw) { return (PM - 1) / hw + 2; }
 hipError_t launch_quant_rows(const uint16_t* x, int64_t rows, int cols, int64_t x_stride, uint8_t* codes,
                              int64_t code_stride, float* scales, hipStream_t st) {
     const int64_t blocks = (rows + 3) / 4;
-    hipLaunchKernelGGL(quant_rows_kernel, dim3((unsigned)blocks), dim3(256), 0, st, x, rows, cols, x_stride,
-                       codes, code_stride, scales);
+    const int per_lane = (cols / 8 + 63) / 64;
+    static_assert(kQuantMaxQV == 16, "vectors per lane of the widest row");
+    if (per_lane <= 4)
+        hipLaunchKernelGGL(quant_rows_kernel<4>, dim3((unsigned)blocks), dim3(256), 0, st, x, rows, cols, x_stride,
+                           codes, code_stride, scales);
+    else if (per_lane <= 8)
+        hipLaunchKernelGGL(quant_rows_kernel<8>, dim3((unsigned)blocks), dim3(256), 0, st, x, rows, cols, x_stride,
+                           codes, code_stride, scales);
+    else
+        hipLaunchKernelGGL(quant_rows_kernel<16>, dim3((unsigned)blocks), dim3(256), 0, st, x, rows, cols, x_stride,
+                           codes, code_stride, scales);
     return hipGetLastError();
 }
 
