@@ -91,7 +91,7 @@ def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the wavefront round is built and timed on a single "
-              "MI355X; multi-GPU runs are not part of this build (requested %d)" % args.gpus,
+              "MI355X; multi-GPU runs are not supported (requested %d)" % args.gpus,
               file=sys.stderr)
         sys.exit(2)
 
