@@ -152,3 +152,62 @@ def test_graph_replays_equal_eager_rounds(name, kind):
     mx, rel = err_stats(gpu_rows(out_g, w, np.arange(w.N)), ref)
     say(name, kind, "eager round", k, "after the replays: max_abs %.3e rel_l2 %.3e" % (mx, rel))
     assert mx <= mx_bar and rel <= rel_bar
+
+
+def test_graph_replays_two_layers():
+    """One captured round of a two-layer pool (both layers' publish and
+    attention, one advance): each replay equals the same rounds run eagerly on
+    a twin pool, in both layers, and leaves the same shared page table."""
+    import wavefront_causal_attention_amd as wf
+    from _gpu_round import config_of, stack_dev
+    w = W.WORKLOADS["ragged128"]
+    say("case ragged128, two layers, graph capture +", REPLAYS, "replays")
+    pools = [wf.Pool(config_of(w, first_round=w.steady_round, num_layers=2)) for _ in range(2)]
+    ids = pools[0].chunk_ids()
+    for pool in pools:                                  # seed anchor and history of both layers
+        for layer in range(2):
+            cl = [W.stored_draw(w, ids[w.T - 1 - slot] + 1000 * layer) for slot in range(w.S + 1, w.T)]
+            pool.publish(layer, w.S + 1, w.T - w.S - 1, None, stack_dev([x[1] for x in cl], w.in_dtype),
+                         stack_dev([x[2] for x in cl], w.in_dtype), w.hd)
+    bufs = [[torch.empty((w.S + 1) * w.N, 3 * w.hd, dtype=torch.bfloat16, device="cuda") for _ in range(2)]
+            for _ in range(2)]
+    qs = [pool.q_buffer() for pool in pools]
+    outs = [[pool.out_buffer("fp32") for _ in range(2)] for pool in pools]
+
+    def set_round(i, k):
+        for layer in range(2):
+            live = [W.draw(w, k + 1000 * layer, s) for s in range(w.S + 1)]
+            host = np.concatenate([np.concatenate(x, axis=1) for x in live], axis=0)
+            bufs[i][layer].copy_(torch.from_numpy(host).to(torch.bfloat16))
+
+    def round_launches(i):
+        hd = w.hd
+        for layer in range(2):
+            b = bufs[i][layer]
+            pools[i].publish(layer, 0, w.S + 1, b[:, :hd], b[:, hd:2 * hd], b[:, 2 * hd:], 3 * hd, q_out=qs[i])
+            pools[i].attention(layer, 0, w.S + 1, qs[i], outs[i][layer])
+        pools[i].advance()
+
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        round_launches(1)
+    k0 = w.steady_round
+    for r in range(REPLAYS):
+        set_round(0, k0 + r)
+        set_round(1, k0 + r)
+        for o in outs[1]:
+            o.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        pools[1].round_replayed()
+        round_launches(0)
+        torch.cuda.synchronize()
+        for layer in range(2):
+            assert not torch.isnan(outs[1][layer]).any()
+            assert torch.equal(outs[1][layer], outs[0][layer]), (r, layer)
+        assert pools[1].round_index() == pools[0].round_index() == k0 + r + 1
+        assert torch.equal(pools[1].table, pools[0].table)
+        for layer in range(2):
+            assert pools[1].ready_mask(layer) == pools[0].ready_mask(layer)
+    say("two layers: %d replays equal to the eager rounds" % REPLAYS)

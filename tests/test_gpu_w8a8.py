@@ -302,3 +302,51 @@ def test_w8a8_whole_video(name, C):
             clean[sch.slot_chunk(w.S)] = tuple(live[w.S][1:])
         if k < C - 1 + w.S:
             pool.advance()
+
+
+def test_w8a8_14b_sampled_pages():
+    """14B-class widths (hidden 5120, 40 heads, 15360 projection outputs): the
+    quantiser's 16-vectors-per-lane form on every weight row (codes and scales
+    bit-exact against the oracle), and W8A8 pages on sampled tokens of every
+    live slot within the summation bound."""
+    import wavefront_causal_attention_amd as wf
+    w = W.WORKLOADS["wan14b_s4"]
+    say("case wan14b_s4, W8A8 projection, sampled tokens")
+    r = RoundRunner(w)
+    wt, b = W.projection_weights(w)
+    w8, sw = wf.quantize_rows_fp8(to_dev(wt, "bf16"))
+    xs = [W.draw_hidden(w, r.k, s) for s in range(w.S + 1)]
+    x8, sx = wf.quantize_rows_fp8(to_dev(np.concatenate(xs, 0), "bf16"))
+    r.pool.project_publish_w8a8(0, 0, w.S + 1, x8, x8.stride(0), sx, w.hd, w8, sw, to_dev(b, "bf16"), q_out=r.q)
+    torch.cuda.synchronize()
+    wc, ws = quantize_rows_fp8(wt)
+    assert np.array_equal(w8.cpu().numpy(), wc) and np.array_equal(sw.cpu().numpy(), ws)
+    wabs = np.abs(fp8_e4m3_decode(wc) * ws.astype(np.float64)[:, None])
+    rng = np.random.default_rng(23)
+    toks = np.array(sorted(set([0, 1, 1559, 1560, w.N - 1] + list(rng.integers(0, w.N, 20)))))
+    sch = RoundSchedule(w.S, w.A, w.H, r.k)
+    kp, vp = read_pages(r.pool, w)
+    table = r.pool.table.cpu().numpy()
+    qf = bf16_dev_bits_to_f32(r.q)
+    x8h, sxh = x8.cpu().numpy(), sx.cpu().numpy()
+    heads = lambda m: m.reshape(len(toks), w.heads, w.head_dim).transpose(1, 0, 2)
+    diff = total = 0
+    worst = 0.0
+    for s in range(w.S + 1):
+        c8, s8 = quantize_rows_fp8(xs[s][toks])
+        rows = s * w.N + toks
+        assert np.array_equal(x8h[rows], c8) and np.array_equal(sxh[rows], s8)
+        q, k, v = split_qkv(project_qkv_w8a8(c8, s8, wc, ws, b), w.hd)
+        a = ACC_REL * (np.abs(fp8_e4m3_decode(c8) * s8.astype(np.float64)[:, None]) @ wabs.T)
+        t, y, x = token_grid(sch.slot_chunk(s), w.chunk_frames, w.frame_h, w.frame_w)
+        rot = lambda m: bf16_round(rope_3d(m.reshape(len(toks), w.heads, w.head_dim), t[toks], y[toks], x[toks],
+                                           w.rope_split, w.rope_theta))
+        p = w.T - 1 - s
+        for got, ref, bound, what in (
+                (qf[s][:, toks], rot(q).transpose(1, 0, 2), _pair_sum(heads(a[:, :w.hd])), "Q"),
+                (position_rows(kp, table, p, r.pool.ppc)[:, toks], rot(k).transpose(1, 0, 2),
+                 _pair_sum(heads(a[:, w.hd:2 * w.hd])), "K"),
+                (position_rows(vp, table, p, r.pool.ppc)[:, toks], bf16_round(heads(v)), heads(a[:, 2 * w.hd:]), "V")):
+            d, tt, u = _bound_check(got, ref, bound, "slot %d %s" % (s, what))
+            diff, total, worst = diff + d, total + tt, max(worst, u)
+    say("sampled elements differing from the oracle: %d of %d; worst share of the allowance %.3f" % (diff, total, worst))
