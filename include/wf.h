@@ -17,11 +17,16 @@
  * slots S-1..s) and never a noisier slot.
  *
  * The library holds host state only (configuration, round index, readiness
- * bits). The caller owns all device memory: the K/V pool, the page table, Q,
- * O and scales. Every launching call enqueues its work on the given stream
- * (a hipStream_t passed as void*, NULL for the default stream) and returns
- * without synchronising. No exception crosses the ABI; every call returns a
- * status and on any error launches nothing and changes no state.
+ * bits) and allocates no device memory. The caller owns all of it: the pool
+ * (K/V pages plus the RoPE tables, attention work lists, fp8 metadata and a
+ * device round counter that wf_pool_create writes into it), the page table,
+ * Q, O, scales and projection operands. Every launching call enqueues its
+ * work on the given stream (a hipStream_t passed as void*, NULL for the
+ * default stream) and returns without synchronising. A pool's launches must
+ * run in the order they were issued (one stream, or streams ordered by
+ * events), and calls on one handle must not overlap (a handle is not
+ * thread-safe). No exception crosses the ABI; every call returns a status and
+ * on any error launches nothing and changes no state.
  *
  * Slot numbering used by wf_kv_publish: slot s in [0, T) is context position
  * T-1-s. Slots 0..S are the live slots (s = S is the store); slots S+1..T-1
