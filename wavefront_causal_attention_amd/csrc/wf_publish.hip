@@ -33,8 +33,8 @@ __host__ __device__ inline int frames_per_tile(int hw) {
 __device__ __forceinline__ float bf_to_f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
 // Projection rows are read exactly once, so their loads take the
-// non-temporal path. Page and Q stores stay ordinary: non-temporal stores
-// measured 7% slower here (the attention that follows reads the pages).
+// non-temporal path. Page and Q stores stay ordinary: with non-temporal
+// stores this kernel measured 7% slower (the attention after it unchanged).
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ uint4 ld_stream16(const void* p) {
     const u32x4 v = __builtin_nontemporal_load(static_cast<const u32x4*>(p));
