@@ -271,6 +271,12 @@ __global__ __launch_bounds__(NTH, NW == 4 ? 2 : 1) void attn_kernel(AttnArgs a) 
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
     const int qrow = qt * BM + wave * 32 + l32;
+    // A wave whose 32 query rows all lie past the chunk (in the last query
+    // tile of a chunk that is not a multiple of BM rows) runs the pipeline
+    // without its MFMA and softmax work: it issues its share of every tile's
+    // DMA and takes every wait and barrier, so the workgroup's schedule is
+    // unchanged, and its SIMD runs the other wave alone.
+    const bool idle = qt * BM + wave * 32 >= N;
     // K row read for accumulator row l32: bits 2 and 3 swapped. Element j of a
     // lane's S^T accumulator block kb then holds key 32*kb + key_in_block(j) +
     // 8*hf, with key_in_block(j) = 16*(j/8) + j%8.
@@ -593,11 +599,16 @@ __global__ __launch_bounds__(NTH, NW == 4 ? 2 : 1) void attn_kernel(AttnArgs a) 
     using Tail = std::integral_constant<bool, false>;  // one of the last steps
     auto step = [&](int t, const uint16_t* k_next, uint16_t* k_fill, const uint16_t* v_cur,
                     uint16_t* v_fill, TileS& Scur, TileS& Snext,
-                    auto mainc) __attribute__((always_inline)) {
+                    auto mainc, auto idlec) __attribute__((always_inline)) {
         constexpr bool kMain = decltype(mainc)::value;
         tile_barrier();
         if (kMain || t + NSTG < ntiles) dma_k(k_fill);
         if (kMain || t + NSTG - 1 < ntiles) dma_v(v_fill);
+        if constexpr (decltype(idlec)::value) {
+            if constexpr (kMain) wait_older_dma();
+            else wait_vmem();
+            return;
+        }
         bf16x8 P[4];
         compute_s(k_next, Snext);
         exp_pack(Scur, P);
@@ -614,54 +625,62 @@ __global__ __launch_bounds__(NTH, NW == 4 ? 2 : 1) void attn_kernel(AttnArgs a) 
         chunk_advance(t + 2);
     };
 
-    // prologue: K(0..NSTG-1) and V(0..NSTG-2) in flight, then S(0)
-    static_for<0, NSTG>([&](auto j) __attribute__((always_inline)) {
-        if (j < ntiles) dma_k(kbuf<j>());
-        if (j + 1 < NSTG && j < ntiles) dma_v(vbuf<j>());
-    });
-    wait_vmem();
-    __syncthreads();
-    TileS SA, SB;
-    if constexpr (FP8) bcur = chunk_bias(0);
-    compute_s(kbuf<0>(), SA);
-    update_max(SA, 0, Mask{});
-    chunk_advance(1);
-    int t = 0;
-    // steady state, NSTG steps per iteration with fixed buffers: step t + j
-    // reads K buffer (j+1) % NSTG and V buffer j, fills K buffer j and V
-    // buffer (j-1) % NSTG; the score accumulators alternate SA/SB
-    if constexpr (NSTG % 2 == 0) {
-        for (; t + 2 * NSTG - 1 < ntiles; t += NSTG)
-            static_for<0, NSTG>([&](auto j) __attribute__((always_inline)) {
-                constexpr int J = decltype(j)::value;
-                if constexpr (J % 2 == 0)
-                    step(t + J, kbuf<(J + 1) % NSTG>(), kbuf<J>(), vbuf<J>(), vbuf<(J + NSTG - 1) % NSTG>(),
-                         SA, SB, Main{});
-                else
-                    step(t + J, kbuf<(J + 1) % NSTG>(), kbuf<J>(), vbuf<J>(), vbuf<(J + NSTG - 1) % NSTG>(),
-                         SB, SA, Main{});
-            });
-    } else {
-        // odd stage count: unroll 2*NSTG steps so the accumulators return to SA
-        for (; t + 3 * NSTG - 1 < ntiles; t += 2 * NSTG)
-            static_for<0, 2 * NSTG>([&](auto j) __attribute__((always_inline)) {
-                constexpr int J = decltype(j)::value;
-                constexpr int B = J % NSTG;
-                if constexpr (J % 2 == 0)
-                    step(t + J, kbuf<(B + 1) % NSTG>(), kbuf<B>(), vbuf<B>(), vbuf<(B + NSTG - 1) % NSTG>(),
-                         SA, SB, Main{});
-                else
-                    step(t + J, kbuf<(B + 1) % NSTG>(), kbuf<B>(), vbuf<B>(), vbuf<(B + NSTG - 1) % NSTG>(),
-                         SB, SA, Main{});
-            });
-    }
-    // remaining steps, buffers chosen at run time
-    for (; t < ntiles; ++t) {
-        const int b = t % NSTG;
-        step(t, kbuf_rt((b + 1) % NSTG), kbuf_rt(b), vbuf_rt(b), vbuf_rt((b + NSTG - 1) % NSTG), SA, SB,
-             Tail{});
-        SA = SB;
-    }
+    // the pipeline, instantiated for computing and for idle waves: the same
+    // DMA, waits and barriers in the same order in both
+    auto run = [&](auto idlec) __attribute__((always_inline)) {
+        // prologue: K(0..NSTG-1) and V(0..NSTG-2) in flight, then S(0)
+        static_for<0, NSTG>([&](auto j) __attribute__((always_inline)) {
+            if (j < ntiles) dma_k(kbuf<j>());
+            if (j + 1 < NSTG && j < ntiles) dma_v(vbuf<j>());
+        });
+        wait_vmem();
+        __syncthreads();
+        TileS SA, SB;
+        if constexpr (FP8) bcur = chunk_bias(0);
+        if constexpr (!decltype(idlec)::value) {
+            compute_s(kbuf<0>(), SA);
+            update_max(SA, 0, Mask{});
+            chunk_advance(1);
+        }
+        int t = 0;
+        // steady state, NSTG steps per iteration with fixed buffers: step t + j
+        // reads K buffer (j+1) % NSTG and V buffer j, fills K buffer j and V
+        // buffer (j-1) % NSTG; the score accumulators alternate SA/SB
+        if constexpr (NSTG % 2 == 0) {
+            for (; t + 2 * NSTG - 1 < ntiles; t += NSTG)
+                static_for<0, NSTG>([&](auto j) __attribute__((always_inline)) {
+                    constexpr int J = decltype(j)::value;
+                    if constexpr (J % 2 == 0)
+                        step(t + J, kbuf<(J + 1) % NSTG>(), kbuf<J>(), vbuf<J>(), vbuf<(J + NSTG - 1) % NSTG>(),
+                             SA, SB, Main{}, idlec);
+                    else
+                        step(t + J, kbuf<(J + 1) % NSTG>(), kbuf<J>(), vbuf<J>(), vbuf<(J + NSTG - 1) % NSTG>(),
+                             SB, SA, Main{}, idlec);
+                });
+        } else {
+            // odd stage count: unroll 2*NSTG steps so the accumulators return to SA
+            for (; t + 3 * NSTG - 1 < ntiles; t += 2 * NSTG)
+                static_for<0, 2 * NSTG>([&](auto j) __attribute__((always_inline)) {
+                    constexpr int J = decltype(j)::value;
+                    constexpr int B = J % NSTG;
+                    if constexpr (J % 2 == 0)
+                        step(t + J, kbuf<(B + 1) % NSTG>(), kbuf<B>(), vbuf<B>(), vbuf<(B + NSTG - 1) % NSTG>(),
+                             SA, SB, Main{}, idlec);
+                    else
+                        step(t + J, kbuf<(B + 1) % NSTG>(), kbuf<B>(), vbuf<B>(), vbuf<(B + NSTG - 1) % NSTG>(),
+                             SB, SA, Main{}, idlec);
+                });
+        }
+        // remaining steps, buffers chosen at run time
+        for (; t < ntiles; ++t) {
+            const int b = t % NSTG;
+            step(t, kbuf_rt((b + 1) % NSTG), kbuf_rt(b), vbuf_rt(b), vbuf_rt((b + NSTG - 1) % NSTG), SA, SB,
+                 Tail{}, idlec);
+            SA = SB;
+        }
+    };
+    if (idle) run(std::true_type{});
+    else run(std::false_type{});
 
     // normalise and store: lane holds O[qrow][32*db + 8*(j/4) + 4*hf + j%4]
     const uint32_t lb = __float_as_uint(l_run);
