@@ -23,6 +23,15 @@ def _cost(w, s):
     return w.T if w.live_mask == "all" else w.T - s
 
 
+def _run_cost(w, s, q):
+    """The packer's run-time estimate: key chunks read, with the last query
+    tile discounted to 0.6 when at most 4 of its 8 waves (32 rows each) hold
+    rows of the chunk, since the others skip their compute."""
+    qt = math.ceil(w.N / 256)
+    tail_waves = math.ceil((w.N - (qt - 1) * 256) / 32)
+    return _cost(w, s) * (0.6 if q == qt - 1 and tail_waves <= 4 else 1.0)
+
+
 def _ranges(S):
     return [(f, n) for f in range(S + 1) for n in range(1, S + 2 - f)]
 
@@ -43,10 +52,12 @@ def test_every_unit_listed_exactly_once(name):
 def test_xcd_pieces_balanced_and_packed_order_fills_the_cus(name, mask):
     """Each XCD's share of the key-chunk cost is within one unit of an
     eighth. Handing the XCD's entries in list order to whichever of its 32
-    CUs frees first (the hardware dispatcher) ends within one unit of the
-    average CU load, and for the wavefront mask's mixed unit costs keeps the
-    CUs >= 97% busy (all-live units all cost T, so 142.5 units on 32 CUs
-    cannot do better than 4.45 / 5)."""
+    CUs frees first (the hardware dispatcher), with the packer's run-time
+    estimates, ends within one unit of the average CU load, and for the
+    wavefront mask's mixed unit costs keeps the CUs >= 96% busy: a CU takes
+    only 3-4 units of 2.4-8 key chunks, so the span cannot come closer to the
+    average load than a fraction of a unit (all-live units cost T or 0.6 T, so
+    142.5 units on 32 CUs cannot either)."""
     w = dataclasses.replace(W.WORKLOADS[name], live_mask=mask)
     lst = wf.wf_attention_work_list(config_of(w), 0, w.S + 1, 32)
     per = [[u for b, u in enumerate(lst) if b % XCDS == x and u is not None] for x in range(XCDS)]
@@ -57,13 +68,13 @@ def test_xcd_pieces_balanced_and_packed_order_fills_the_cus(name, mask):
     for p in per:
         free = [0] * 32
         heapq.heapify(free)
-        for s, _, _ in p:
-            heapq.heappush(free, heapq.heappop(free) + _cost(w, s))
+        for s, _, q in p:
+            heapq.heappush(free, heapq.heappop(free) + _run_cost(w, s, q))
         span = max(free)
-        work = sum(_cost(w, s) for s, _, _ in p)
+        work = sum(_run_cost(w, s, q) for s, _, q in p)
         assert span <= work / 32 + umax
         if mask == "wavefront":
-            assert work / (32 * span) >= 0.97, (name, work / (32 * span))
+            assert work / (32 * span) >= 0.96, (name, work / (32 * span))
 
 
 def test_work_list_validation():

@@ -32,7 +32,8 @@ struct Layout {
 };
 
 // Attention work order for query slots [first, first + n): every (slot, head,
-// query tile) unit, cost = key chunks it reads. Units are laid out head-major
+// query tile) unit, cost = key chunks it reads (for packing, the run-time
+// estimate pcost, which discounts a mostly idle last query tile). Units are laid out head-major
 // and cut into kXcds contiguous pieces of equal cost (each unit goes to the
 // piece holding its cost midpoint), so one head's K/V is streamed by one or
 // two XCDs (each XCD has its own L2). Workgroup b runs piece b % kXcds, entry
@@ -46,14 +47,15 @@ struct Layout {
 // when run times follow the cost model and still adapts when they do not.
 struct WorkUnit {
     int s, h, q;
-    int64_t cost;
+    int64_t cost;     // key chunks x 10: cuts the list into XCD pieces
+    int64_t pcost;    // run-time estimate used to pack a piece onto CUs
 };
 
 static void order_piece(std::vector<WorkUnit>& p, int bins) {
     const int n = (int)p.size();
     std::vector<int> idx(n);
     for (int i = 0; i < n; ++i) idx[i] = i;
-    std::stable_sort(idx.begin(), idx.end(), [&](int x, int y) { return p[x].cost > p[y].cost; });
+    std::stable_sort(idx.begin(), idx.end(), [&](int x, int y) { return p[x].pcost > p[y].pcost; });
     if (bins <= 1 || n <= 1) {
         std::vector<WorkUnit> out;
         for (int i : idx) out.push_back(p[i]);
@@ -65,7 +67,7 @@ static void order_piece(std::vector<WorkUnit>& p, int bins) {
     for (int i : idx) {
         const int b = (int)(std::min_element(load.begin(), load.end()) - load.begin());
         bin[b].push_back(i);
-        load[b] += p[i].cost;
+        load[b] += p[i].pcost;
     }
     // descent on the most loaded bin; every accepted move or swap makes the
     // pair's loads more even, so the sum of squared loads strictly falls
@@ -80,14 +82,14 @@ static void order_piece(std::vector<WorkUnit>& p, int bins) {
             int64_t best = load[hi];
             int bi = -1, bj = -1;
             for (size_t i = 0; i < bin[hi].size(); ++i) {
-                const int64_t ci = p[bin[hi][i]].cost;
+                const int64_t ci = p[bin[hi][i]].pcost;
                 if (std::max(load[hi] - ci, load[lo] + ci) < best) {
                     best = std::max(load[hi] - ci, load[lo] + ci);
                     bi = (int)i;
                     bj = -1;
                 }
                 for (size_t j = 0; j < bin[lo].size(); ++j) {
-                    const int64_t d = ci - p[bin[lo][j]].cost;
+                    const int64_t d = ci - p[bin[lo][j]].pcost;
                     if (d > 0 && std::max(load[hi] - d, load[lo] + d) < best) {
                         best = std::max(load[hi] - d, load[lo] + d);
                         bi = (int)i;
@@ -100,14 +102,14 @@ static void order_piece(std::vector<WorkUnit>& p, int bins) {
             if (bj < 0) {
                 bin[hi].erase(bin[hi].begin() + bi);
                 bin[lo].push_back(ui);
-                load[hi] -= p[ui].cost;
-                load[lo] += p[ui].cost;
+                load[hi] -= p[ui].pcost;
+                load[lo] += p[ui].pcost;
             } else {
                 const int uj = bin[lo][bj];
                 bin[hi][bi] = uj;
                 bin[lo][bj] = ui;
-                load[hi] += p[uj].cost - p[ui].cost;
-                load[lo] += p[ui].cost - p[uj].cost;
+                load[hi] += p[uj].pcost - p[ui].pcost;
+                load[lo] += p[ui].pcost - p[uj].pcost;
             }
             moved = true;
             break;
@@ -119,11 +121,11 @@ static void order_piece(std::vector<WorkUnit>& p, int bins) {
     std::vector<Start> st;
     st.reserve(n);
     for (auto& b : bin) {
-        std::stable_sort(b.begin(), b.end(), [&](int x, int y) { return p[x].cost > p[y].cost; });
+        std::stable_sort(b.begin(), b.end(), [&](int x, int y) { return p[x].pcost > p[y].pcost; });
         int64_t t = 0;
         for (int i : b) {
-            st.push_back({t, -p[i].cost, i});
-            t += p[i].cost;
+            st.push_back({t, -p[i].pcost, i});
+            t += p[i].pcost;
         }
     }
     std::sort(st.begin(), st.end(), [](const Start& x, const Start& y) {
@@ -136,13 +138,23 @@ static void order_piece(std::vector<WorkUnit>& p, int bins) {
 }
 
 // cus_per_xcd <= 0 skips the ordering (list sizes do not depend on it).
-std::vector<int32_t> build_work_list(int first, int n, int heads, int qtiles, int T, bool all_live,
+std::vector<int32_t> build_work_list(int first, int n, int heads, int N, int T, bool all_live,
                                      int cus_per_xcd) {
+    const int qtiles = (N + wf::kAttnBM - 1) / wf::kAttnBM;
+    // costs in tenths of a key chunk. The last query tile, when at most half
+    // its waves hold rows of the chunk, runs one computing wave per SIMD (the
+    // others idle): packing counts it as 0.6 of a full tile (0.6, 0.7 and 0.8
+    // measured at three Wan shapes; 0.6 was never slower than 1.0). The XCD
+    // cut keeps whole-tile costs.
+    const int tail_waves = (N - (qtiles - 1) * wf::kAttnBM + 31) / 32;
+    const int64_t tail_w = tail_waves <= wf::kAttnBM / 64 ? 6 : 10;
     std::vector<WorkUnit> u;
     u.reserve((size_t)n * heads * qtiles);
     for (int h = 0; h < heads; ++h)
         for (int s = first; s < first + n; ++s)
-            for (int q = 0; q < qtiles; ++q) u.push_back({s, h, q, (int64_t)(all_live ? T : T - s)});
+            for (int q = 0; q < qtiles; ++q)
+                u.push_back({s, h, q, (int64_t)(all_live ? T : T - s) * 10,
+                             (int64_t)(all_live ? T : T - s) * (q == qtiles - 1 ? tail_w : 10)});
     int64_t total = 0;
     for (const WorkUnit& x : u) total += x.cost;
     std::vector<std::vector<WorkUnit>> piece(wf::kXcds);
@@ -236,7 +248,7 @@ int validate(const wf_config* c, Layout* L) {
         size_t longest = 0;
         for (int first = 0; first <= c->S; ++first)
             for (int n = 1; first + n <= c->S + 1; ++n)
-                longest = std::max(longest, build_work_list(first, n, c->heads, qtiles, T,
+                longest = std::max(longest, build_work_list(first, n, c->heads, (int)N, T,
                                                             c->live_mask == WF_MASK_ALL_LIVE, 0).size());
         L->work_len = (int)longest;
         L->work_stride = align_up(longest * 4, 256);
@@ -406,7 +418,7 @@ int wf_pool_create(const wf_config* cfg, void* pool_dev, size_t pool_bytes,
     const int cus_per_xcd = std::max(1, cus / wf::kXcds);
     for (int first = 0; first <= cfg->S && e == hipSuccess; ++first)
         for (int n = 1; first + n <= cfg->S + 1 && e == hipSuccess; ++n) {
-            std::vector<int32_t> wl = build_work_list(first, n, cfg->heads, qtiles, L.T,
+            std::vector<int32_t> wl = build_work_list(first, n, cfg->heads, L.N, L.T,
                                                       cfg->live_mask == WF_MASK_ALL_LIVE, cus_per_xcd);
             if ((int)wl.size() > L.work_len) { e = hipErrorInvalidValue; break; }
             h->work_count[first * (cfg->S + 1) + n - 1] = (int)wl.size();
@@ -794,7 +806,7 @@ int wf_attention_work_list(const wf_config* cfg, int32_t slot_first, int32_t nsl
     if (!count || nslots < 1 || slot_first < 0 || slot_first + nslots > cfg->S + 1 || cus_per_xcd < 1)
         return WF_E_INVALID_ARG;
     const int qtiles = (L.N + wf::kAttnBM - 1) / wf::kAttnBM;
-    const std::vector<int32_t> wl = build_work_list(slot_first, nslots, cfg->heads, qtiles, L.T,
+    const std::vector<int32_t> wl = build_work_list(slot_first, nslots, cfg->heads, L.N, L.T,
                                                     cfg->live_mask == WF_MASK_ALL_LIVE, cus_per_xcd);
     *count = (int64_t)wl.size();
     if (units) {
