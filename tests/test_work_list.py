@@ -24,12 +24,13 @@ def _cost(w, s):
 
 
 def _run_cost(w, s, q):
-    """The packer's run-time estimate: key chunks read, with the last query
-    tile discounted to 0.6 when at most 4 of its 8 waves (32 rows each) hold
-    rows of the chunk, since the others skip their compute."""
+    """The packer's run-time estimate: key chunks read, with the bf16 last
+    query tile discounted to 0.6 when at most 4 of its 8 waves (32 rows each)
+    hold rows of the chunk, since the others skip their compute."""
     qt = math.ceil(w.N / 256)
     tail_waves = math.ceil((w.N - (qt - 1) * 256) / 32)
-    return _cost(w, s) * (0.6 if q == qt - 1 and tail_waves <= 4 else 1.0)
+    tail = w.qk_dtype == "bf16" and q == qt - 1 and tail_waves <= 4
+    return _cost(w, s) * (0.6 if tail else 1.0)
 
 
 def _ranges(S):
@@ -48,7 +49,8 @@ def test_every_unit_listed_exactly_once(name):
 
 
 @pytest.mark.parametrize("name,mask", [("wan1.3b_s4", "wavefront"), ("wan14b_s4", "wavefront"),
-                                       ("wan1.3b_s5_30", "wavefront"), ("wan1.3b_s4", "all")])
+                                       ("wan1.3b_s5_30", "wavefront"), ("wan1.3b_s4", "all"),
+                                       ("wan1.3b_s4_fp8", "wavefront")])
 def test_xcd_pieces_balanced_and_packed_order_fills_the_cus(name, mask):
     """Each XCD's share of the key-chunk cost is within one unit of an
     eighth. Handing the XCD's entries in list order to whichever of its 32

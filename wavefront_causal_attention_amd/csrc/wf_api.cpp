@@ -138,16 +138,17 @@ static void order_piece(std::vector<WorkUnit>& p, int bins) {
 }
 
 // cus_per_xcd <= 0 skips the ordering (list sizes do not depend on it).
-std::vector<int32_t> build_work_list(int first, int n, int heads, int N, int T, bool all_live,
+std::vector<int32_t> build_work_list(int first, int n, int heads, int N, int T, bool all_live, bool fp8,
                                      int cus_per_xcd) {
     const int qtiles = (N + wf::kAttnBM - 1) / wf::kAttnBM;
     // costs in tenths of a key chunk. The last query tile, when at most half
     // its waves hold rows of the chunk, runs one computing wave per SIMD (the
-    // others idle): packing counts it as 0.6 of a full tile (0.6, 0.7 and 0.8
-    // measured at three Wan shapes; 0.6 was never slower than 1.0). The XCD
-    // cut keeps whole-tile costs.
+    // others idle): for bf16, packing counts it as 0.6 of a full tile (0.6,
+    // 0.7 and 0.8 measured at three Wan shapes; 0.6 was never slower than
+    // 1.0). The fp8 kernel's tail tiles measured no faster, so fp8 keeps whole
+    // tiles, as does the XCD cut.
     const int tail_waves = (N - (qtiles - 1) * wf::kAttnBM + 31) / 32;
-    const int64_t tail_w = tail_waves <= wf::kAttnBM / 64 ? 6 : 10;
+    const int64_t tail_w = !fp8 && tail_waves <= wf::kAttnBM / 64 ? 6 : 10;
     std::vector<WorkUnit> u;
     u.reserve((size_t)n * heads * qtiles);
     for (int h = 0; h < heads; ++h)
@@ -249,7 +250,7 @@ int validate(const wf_config* c, Layout* L) {
         for (int first = 0; first <= c->S; ++first)
             for (int n = 1; first + n <= c->S + 1; ++n)
                 longest = std::max(longest, build_work_list(first, n, c->heads, (int)N, T,
-                                                            c->live_mask == WF_MASK_ALL_LIVE, 0).size());
+                                                            c->live_mask == WF_MASK_ALL_LIVE, fp8, 0).size());
         L->work_len = (int)longest;
         L->work_stride = align_up(longest * 4, 256);
         L->work_off = off;
@@ -419,7 +420,8 @@ int wf_pool_create(const wf_config* cfg, void* pool_dev, size_t pool_bytes,
     for (int first = 0; first <= cfg->S && e == hipSuccess; ++first)
         for (int n = 1; first + n <= cfg->S + 1 && e == hipSuccess; ++n) {
             std::vector<int32_t> wl = build_work_list(first, n, cfg->heads, L.N, L.T,
-                                                      cfg->live_mask == WF_MASK_ALL_LIVE, cus_per_xcd);
+                                                      cfg->live_mask == WF_MASK_ALL_LIVE,
+                                                      cfg->qk_dtype == WF_DTYPE_FP8_E4M3, cus_per_xcd);
             if ((int)wl.size() > L.work_len) { e = hipErrorInvalidValue; break; }
             h->work_count[first * (cfg->S + 1) + n - 1] = (int)wl.size();
             e = hipMemcpy(h->pool + L.work_off + L.work_stride * (first * (cfg->S + 1) + n - 1),
@@ -805,9 +807,9 @@ int wf_attention_work_list(const wf_config* cfg, int32_t slot_first, int32_t nsl
     if (st != WF_OK) return st;
     if (!count || nslots < 1 || slot_first < 0 || slot_first + nslots > cfg->S + 1 || cus_per_xcd < 1)
         return WF_E_INVALID_ARG;
-    const int qtiles = (L.N + wf::kAttnBM - 1) / wf::kAttnBM;
     const std::vector<int32_t> wl = build_work_list(slot_first, nslots, cfg->heads, L.N, L.T,
-                                                    cfg->live_mask == WF_MASK_ALL_LIVE, cus_per_xcd);
+                                                    cfg->live_mask == WF_MASK_ALL_LIVE,
+                                                    cfg->qk_dtype == WF_DTYPE_FP8_E4M3, cus_per_xcd);
     *count = (int64_t)wl.size();
     if (units) {
         if (capacity < (int64_t)wl.size()) return WF_E_INVALID_ARG;
