@@ -211,3 +211,33 @@ def test_graph_replays_two_layers():
         for layer in range(2):
             assert pools[1].ready_mask(layer) == pools[0].ready_mask(layer)
     say("two layers: %d replays equal to the eager rounds" % REPLAYS)
+
+
+def test_capture_of_a_fill_round_is_refused():
+    """Only steady rounds can be replayed, so an advance captured in a round
+    that fills the pipeline is refused on the host before anything is
+    enqueued, and the pool's state is left as it was."""
+    import wavefront_causal_attention_amd as wf
+    from _gpu_round import config_of, stack_dev
+    w = W.WORKLOADS["tiny"]
+    say("case tiny, capture in fill round 0")
+    pool = wf.Pool(config_of(w, first_round=0))
+    q = pool.q_buffer()
+    live = W.draw(w, 0, 0)
+    qd, kd, vd = (stack_dev([x], w.in_dtype) for x in live)
+    table0 = pool.table.clone()
+    g = torch.cuda.CUDAGraph()
+    with pytest.raises(wf.WfError) as e:
+        with torch.cuda.graph(g):
+            pool.publish(0, 0, 1, qd, kd, vd, w.hd, q_out=q)   # round 0: only slot 0 holds a chunk
+            pool.advance()
+    assert e.value.status == wf.WF_E_INVALID_ARG
+    assert "steady" in str(e.value)
+    torch.cuda.synchronize()
+    assert pool.round_index() == 0
+    assert torch.equal(pool.table, table0)
+    # the pool still runs eagerly
+    pool.publish(0, 0, 1, qd, kd, vd, w.hd, q_out=q)
+    pool.advance()
+    torch.cuda.synchronize()
+    assert pool.round_index() == 1
