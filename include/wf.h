@@ -279,8 +279,10 @@ int wf_round_advance(wf_handle* h, void* stream);
  * Host bookkeeping for one replay of a captured round (see wf_round_advance):
  * the host state moves to the next round as the replayed advance left the
  * device, with the replayed round's store taken as published in every layer.
- * Launches nothing. WF_E_INVALID_ARG for a round that is not steady or the
- * last round of a video.
+ * Launches nothing. WF_E_INVALID_ARG if no advance of this pool was captured,
+ * for a round that is not steady, or for the last round of a video. Publish
+ * and attention calls made while capturing update the host's readiness as if
+ * they had run: replay the graph before relying on what they publish.
  */
 int wf_round_replayed(wf_handle* h);
 

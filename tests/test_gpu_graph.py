@@ -241,3 +241,17 @@ def test_capture_of_a_fill_round_is_refused():
     pool.advance()
     torch.cuda.synchronize()
     assert pool.round_index() == 1
+
+
+def test_replay_bookkeeping_without_a_capture_is_refused():
+    """A device pool from which no advance was captured has no replay to
+    follow: the host state must not move away from the device's."""
+    import wavefront_causal_attention_amd as wf
+    from _gpu_round import config_of
+    w = W.WORKLOADS["tiny"]
+    pool = wf.Pool(config_of(w))
+    k = pool.round_index()
+    with pytest.raises(wf.WfError) as e:
+        pool.round_replayed()
+    assert e.value.status == wf.WF_E_INVALID_ARG and "captured" in str(e.value)
+    assert pool.round_index() == k

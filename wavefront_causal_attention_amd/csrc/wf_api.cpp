@@ -270,6 +270,7 @@ struct wf_handle {
     char* pool = nullptr;
     int32_t* table = nullptr;
     int64_t ring = 0;                    // advances since creation
+    bool captured = false;               // an advance of this pool was captured into a graph
     std::vector<uint64_t> ready;         // per layer, bit p = context position p
     std::vector<int> work_count;         // attention work-list length per slot range
     char err[512] = {0};
@@ -774,6 +775,7 @@ int wf_round_advance(wf_handle* h, void* stream) {
         e = wf::launch_page_table(h->table, h->L.T, A, h->L.ppc, h->ring + 1, h->ring_dev(), store,
                                   h->store_anchor_at_round(k + 1), (hipStream_t)stream);
         if (e != hipSuccess) return h->fail_hip(e, "wf_round_advance launch");
+        if (capturing) h->captured = true;
     }
     // a captured advance moves the device counter only when it runs; the host
     // follows each replay through wf_round_replayed
@@ -783,6 +785,10 @@ int wf_round_advance(wf_handle* h, void* stream) {
 
 int wf_round_replayed(wf_handle* h) {
     if (!h) return WF_E_INVALID_ARG;
+    if (!h->host_model && !h->captured) {
+        snprintf(h->err, sizeof h->err, "no advance of this pool was captured: there is no replay to follow");
+        return WF_E_INVALID_ARG;
+    }
     int st = check_not_last(h);
     if (st == WF_OK) st = check_steady(h);
     if (st != WF_OK) return st;
