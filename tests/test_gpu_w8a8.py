@@ -350,3 +350,34 @@ def test_w8a8_14b_sampled_pages():
             d, tt, u = _bound_check(got, ref, bound, "slot %d %s" % (s, what))
             diff, total, worst = diff + d, total + tt, max(worst, u)
     say("sampled elements differing from the oracle: %d of %d; worst share of the allowance %.3f" % (diff, total, worst))
+
+
+@pytest.mark.parametrize("kind", ["bf16", "w8a8"])
+def test_projection_with_padded_rows_equals_packed_rows(kind):
+    """Hidden-state rows with a padded stride (padding filled with large
+    values the kernels must not read) publish exactly what packed rows do."""
+    import wavefront_causal_attention_amd as wf
+    w = W.WORKLOADS["ragged128"]
+    say("case ragged128,", kind, "projection, padded row stride")
+    xs = np.concatenate([W.draw_hidden(w, w.steady_round, s) for s in range(w.S + 1)], 0)
+    wt, b = W.projection_weights(w)
+    wd, bd = to_dev(wt, "bf16"), to_dev(b, "bf16")
+    pad = 144                                          # elements (bf16) / codes (e4m3) past each row, 16-byte rows
+    xp = np.full((xs.shape[0], w.hd + pad), 3.0e38, dtype=np.float32)
+    xp[:, :w.hd] = xs
+    outs = []
+    for x in (to_dev(xs, "bf16"), to_dev(xp, "bf16")):
+        r = RoundRunner(w)
+        if kind == "bf16":
+            r.pool.project_publish(0, 0, w.S + 1, x, x.stride(0), w.hd, wd, bd, q_out=r.q)
+        else:
+            w8, sw = wf.quantize_rows_fp8(wd)
+            pitch = w.hd + (pad if x.stride(0) > w.hd else 0)
+            codes = torch.full((x.shape[0], pitch), 0x7F, dtype=torch.uint8, device="cuda")  # NaN codes in padding
+            x8, sx = wf.quantize_rows_fp8(x[:, :w.hd], codes[:, :w.hd])
+            r.pool.project_publish_w8a8(0, 0, w.S + 1, x8, x8.stride(0), sx, w.hd, w8, sw, bd, q_out=r.q)
+        torch.cuda.synchronize()
+        kp, vp = read_pages(r.pool, w)
+        outs.append((r.q.clone(), kp, vp))
+    assert torch.equal(outs[0][0], outs[1][0])
+    assert np.array_equal(outs[0][1], outs[1][1]) and np.array_equal(outs[0][2], outs[1][2])
