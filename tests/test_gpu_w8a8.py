@@ -163,7 +163,7 @@ def _check_pages(r, live, slots):
     for s in slots:
         c = sch.slot_chunk(s)
         q, k, v = live[s]
-        a = ACC_REL * r.absum(s)                           # [N, 3 h d]
+        a = getattr(r, "acc_rel", ACC_REL) * r.absum(s)    # [N, 3 h d]
         heads = lambda m: m.reshape(w.N, w.heads, w.head_dim).transpose(1, 0, 2)
         p = w.T - 1 - s
         refs = [(qf[s], bf16_round(rotate_chunk(w, c, q)).transpose(1, 0, 2), _pair_sum(heads(a[:, :w.hd])), "Q"),
@@ -381,3 +381,40 @@ def test_projection_with_padded_rows_equals_packed_rows(kind):
         outs.append((r.q.clone(), kp, vp))
     assert torch.equal(outs[0][0], outs[1][0])
     assert np.array_equal(outs[0][1], outs[1][1]) and np.array_equal(outs[0][2], outs[1][2])
+
+
+@pytest.mark.parametrize("kind,hidden", [("bf16", 256), ("bf16", 640), ("w8a8", 256), ("w8a8", 640)])
+def test_projection_hidden_width_other_than_heads_times_dim(kind, hidden):
+    """A linear layer whose input width differs from h*d (384 here): Q and the
+    pages against the oracle's projection of the same operands, within one
+    bf16 ulp plus the summation bound: for bf16 the fp32 one, hidden x 2^-24 x
+    sum |x w| for any order of additions; for W8A8 the e4m3 MFMA's."""
+    import wavefront_causal_attention_amd as wf
+    from oracle import project_qkv
+    w = W.WORKLOADS["ragged128"]
+    say("case ragged128,", kind, "projection, hidden", hidden)
+    rng = np.random.default_rng(1000 + hidden)
+    xs = [W.round_to_bf16(rng.standard_normal((w.N, hidden), dtype=np.float32)) for _ in range(w.S + 1)]
+    wt = W.round_to_bf16(rng.standard_normal((3 * w.hd, hidden), dtype=np.float32) / np.float32(np.sqrt(hidden)))
+    b = W.round_to_bf16(rng.standard_normal(3 * w.hd, dtype=np.float32) * np.float32(0.1))
+    r = RoundRunner(w)
+    xd, wd, bd = to_dev(np.concatenate(xs, 0), "bf16"), to_dev(wt, "bf16"), to_dev(b, "bf16")
+    if kind == "bf16":
+        r.pool.project_publish(0, 0, w.S + 1, xd, hidden, hidden, wd, bd, q_out=r.q)
+        live = [tuple(split_qkv(project_qkv(x, wt, b), w.hd)) for x in xs]
+        wabs = np.abs(wt.astype(np.float64))
+        r.absum = lambda s, rows=slice(None): np.abs(xs[s][rows].astype(np.float64)) @ wabs.T
+        r.acc_rel = hidden * 2.0 ** -24
+    else:
+        w8, sw = wf.quantize_rows_fp8(wd)
+        x8, sx = wf.quantize_rows_fp8(xd)
+        r.pool.project_publish_w8a8(0, 0, w.S + 1, x8, x8.stride(0), sx, hidden, w8, sw, bd, q_out=r.q)
+        wc, ws = quantize_rows_fp8(wt)
+        q8 = [quantize_rows_fp8(x) for x in xs]
+        live = [tuple(split_qkv(project_qkv_w8a8(c, s, wc, ws, b), w.hd)) for c, s in q8]
+        wabs = np.abs(fp8_e4m3_decode(wc) * ws.astype(np.float64)[:, None])
+        r.absum = lambda s, rows=slice(None): (np.abs(fp8_e4m3_decode(q8[s][0][rows]) *
+                                                      q8[s][1][rows].astype(np.float64)[:, None]) @ wabs.T)
+    torch.cuda.synchronize()
+    diff, total, worst = _check_pages(r, live, range(w.S + 1))
+    say("elements differing from the oracle: %d of %d; worst share of the allowance %.3f" % (diff, total, worst))
