@@ -445,3 +445,49 @@ def test_maximum_positions_and_table_pages():
         dev = r.pool.table.cpu().numpy().tolist()
         assert dev == r.pool.page_table_host()
         r.advance()
+
+
+@pytest.mark.parametrize("path", ["publish", "project"])
+def test_explicit_rope_time_offsets(path):
+    """chunk_t0_host given explicitly: the schedule's own offsets publish
+    exactly what the default (the pool's round counter) does; offsets shifted
+    by 7 frames rotate Q and K by the time positions shifted by 7, as the
+    oracle's RoPE does (within one bf16 ulp)."""
+    import wavefront_causal_attention_amd as wf
+    from oracle import project_qkv, rope_3d, split_qkv, token_grid
+    from _gpu_round import bf16_dev_bits_to_f32, bf16_ulps, position_rows, read_pages, stack_dev, to_dev
+    w = W.WORKLOADS["ragged128"]
+    k = w.steady_round
+    sch = RoundSchedule(w.S, w.A, w.H, k)
+    t0 = [w.chunk_frames * sch.slot_chunk(s) for s in range(w.S + 1)]
+    if path == "publish":
+        live = [W.draw(w, k, s) for s in range(w.S + 1)]
+        qd, kd, vd = (stack_dev([x[i] for x in live], w.in_dtype) for i in range(3))
+        run = lambda r, t: r.pool.publish(0, 0, w.S + 1, qd, kd, vd, w.hd, q_out=r.q, chunk_t0=t)
+    else:
+        xs = [W.draw_hidden(w, k, s) for s in range(w.S + 1)]
+        wt, b = W.projection_weights(w)
+        xd, wd, bd = to_dev(np.concatenate(xs, 0), "bf16"), to_dev(wt, "bf16"), to_dev(b, "bf16")
+        live = [tuple(split_qkv(project_qkv(x, wt, b), w.hd)) for x in xs]
+        run = lambda r, t: r.pool.project_publish(0, 0, w.S + 1, xd, w.hd, w.hd, wd, bd, q_out=r.q, chunk_t0=t)
+    say("case ragged128,", path, "explicit RoPE time offsets", t0)
+    res = []
+    for t in (None, t0, [x + 7 for x in t0]):
+        r = RoundRunner(w)
+        run(r, t)
+        torch.cuda.synchronize()
+        kp, vp = read_pages(r.pool, w)
+        res.append((r.q.clone(), kp, vp, r.pool.table.cpu().numpy(), r.pool.ppc))
+    assert torch.equal(res[0][0], res[1][0])
+    assert np.array_equal(res[0][1], res[1][1]) and np.array_equal(res[0][2], res[1][2])
+    q_sh, kp, vp, table, ppc = res[2]
+    qf = bf16_dev_bits_to_f32(q_sh)
+    for s in range(w.S + 1):
+        t, y, x = token_grid(sch.slot_chunk(s), w.chunk_frames, w.frame_h, w.frame_w)
+        q, kk, v = (a.reshape(w.N, w.heads, w.head_dim) for a in live[s])
+        qr = bf16_round(rope_3d(q, t + 7, y, x, w.rope_split, w.rope_theta)).transpose(1, 0, 2)
+        kr = bf16_round(rope_3d(kk, t + 7, y, x, w.rope_split, w.rope_theta)).transpose(1, 0, 2)
+        p = w.T - 1 - s
+        assert bf16_ulps(qf[s], qr).max() <= 1, s
+        assert bf16_ulps(position_rows(kp, table, p, ppc), kr).max() <= 1, s
+        assert np.array_equal(position_rows(vp, table, p, ppc), position_rows(res[0][2], table, p, ppc))
