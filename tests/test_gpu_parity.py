@@ -479,7 +479,11 @@ def test_explicit_rope_time_offsets(path):
         kp, vp = read_pages(r.pool, w)
         res.append((r.q.clone(), kp, vp, r.pool.table.cpu().numpy(), r.pool.ppc))
     assert torch.equal(res[0][0], res[1][0])
-    assert np.array_equal(res[0][1], res[1][1]) and np.array_equal(res[0][2], res[1][2])
+    for s in range(w.S + 1):                       # the published positions (anchor and history are not)
+        p = w.T - 1 - s
+        for i in (1, 2):
+            assert np.array_equal(position_rows(res[0][i], res[0][3], p, res[0][4]),
+                                  position_rows(res[1][i], res[1][3], p, res[1][4])), (s, i)
     q_sh, kp, vp, table, ppc = res[2]
     qf = bf16_dev_bits_to_f32(q_sh)
     for s in range(w.S + 1):

@@ -378,9 +378,13 @@ def test_projection_with_padded_rows_equals_packed_rows(kind):
             r.pool.project_publish_w8a8(0, 0, w.S + 1, x8, x8.stride(0), sx, w.hd, w8, sw, bd, q_out=r.q)
         torch.cuda.synchronize()
         kp, vp = read_pages(r.pool, w)
-        outs.append((r.q.clone(), kp, vp))
+        outs.append((r.q.clone(), kp, vp, r.pool.table.cpu().numpy(), r.pool.ppc))
     assert torch.equal(outs[0][0], outs[1][0])
-    assert np.array_equal(outs[0][1], outs[1][1]) and np.array_equal(outs[0][2], outs[1][2])
+    for s in range(w.S + 1):                       # the published positions (anchor and history are not)
+        p = w.T - 1 - s
+        for i in (1, 2):
+            assert np.array_equal(position_rows(outs[0][i], outs[0][3], p, outs[0][4]),
+                                  position_rows(outs[1][i], outs[1][3], p, outs[1][4])), (s, i)
 
 
 @pytest.mark.parametrize("kind,hidden", [("bf16", 256), ("bf16", 640), ("w8a8", 256), ("w8a8", 640)])
