@@ -447,6 +447,25 @@ def test_maximum_positions_and_table_pages():
         r.advance()
 
 
+def test_sixty_three_query_slots():
+    """S = 62: query slots 32..62 sit in the high bits of their work entries;
+    every output of every slot of two rounds, across an advance."""
+    w = W.WORKLOADS["slots62"]
+    say("case slots62: 63 query slots")
+    r = RoundRunner(w)
+    r.seed_clean()
+    for i in range(2):
+        r.publish_live(live=W.draw_slots(w, r.k, range(w.S + 1)))
+        out = r.attention("fp32")
+        ref = oracle_round(w, r.k, r.live, r.clean_for_round(), storage="bf16")
+        g = gpu_rows(out, w, np.arange(w.N))
+        assert not np.isnan(g).any()
+        mx, rel = err_stats(g, ref)
+        say("slots62 round", r.k, "max_abs %.3e rel_l2 %.3e" % (mx, rel))
+        assert mx <= BF16_MAX_ABS and rel <= BF16_REL_L2
+        r.advance()
+
+
 @pytest.mark.parametrize("path", ["publish", "project"])
 def test_explicit_rope_time_offsets(path):
     """chunk_t0_host given explicitly: the schedule's own offsets publish

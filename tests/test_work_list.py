@@ -37,10 +37,13 @@ def _ranges(S):
     return [(f, n) for f in range(S + 1) for n in range(1, S + 2 - f)]
 
 
-@pytest.mark.parametrize("name", ["tiny", "ragged128", "edge_s1_h0", "wan1.3b_s4", "wan14b_s4", "max64"])
+@pytest.mark.parametrize("name", ["tiny", "ragged128", "edge_s1_h0", "wan1.3b_s4", "wan14b_s4", "max64",
+                                  "slots62"])
 def test_every_unit_listed_exactly_once(name):
     w = W.WORKLOADS[name]
-    ranges = _ranges(w.S) if w.S < 8 else [(0, w.S + 1), (0, 1), (w.S, 1), (3, 11), (17, 14)]
+    ranges = _ranges(w.S) if w.S < 8 else [(0, w.S + 1), (0, 1), (w.S, 1), (3, 11), (17, 14),
+                                           (31, 2), (32, 1), (w.S - 20, 21)]
+    ranges = [(f, n) for f, n in ranges if f + n <= w.S + 1]
     for first, n in ranges:
         lst = wf.wf_attention_work_list(config_of(w), first, n, 32)
         assert len(lst) % XCDS == 0
@@ -88,3 +91,16 @@ def test_work_list_validation():
     with pytest.raises(wf.WfError) as e:
         wf.wf_attention_work_list(config_of(w), 0, 1, 0)
     assert e.value.status == wf.WF_E_INVALID_ARG
+
+
+@pytest.mark.parametrize("S", [31, 32, 40, 62])
+def test_slots_past_31_are_listed(S):
+    """Slots 32..62 fill the top bits of a work entry: every (slot, head,
+    query tile) of S+1 slots is listed once and none reads as padding."""
+    w = dataclasses.replace(W.WORKLOADS["slots62"], S=S, H=62 - S)
+    assert w.T == 64
+    lst = wf.wf_attention_work_list(config_of(w), 0, w.S + 1, 32)
+    got = [u for u in lst if u is not None]
+    assert len(got) == len(set(got)) == (S + 1) * w.heads
+    assert set(got) == _units(w, 0, S + 1)
+    assert max(s for s, _, _ in got) == S

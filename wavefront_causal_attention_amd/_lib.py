@@ -245,7 +245,8 @@ def wf_attention_work_list(cfg, slot_first, nslots, cus_per_xcd):
     _check(load().wf_attention_work_list(ctypes.byref(cfg), slot_first, nslots, cus_per_xcd,
                                          ctypes.cast(arr, ctypes.c_void_p), n.value, ctypes.byref(n)),
            "wf_attention_work_list")
-    return [None if x < 0 else ((x >> 26) & 63, (x >> 16) & 1023, x & 0xFFFF) for x in arr]
+    # uint32 fields: slot 31..26, head 25..16, query tile 15..0; -1 is padding
+    return [None if x == -1 else ((x & 0xFFFFFFFF) >> 26, (x >> 16) & 1023, x & 0xFFFF) for x in arr]
 
 
 def wf_geometry(h):

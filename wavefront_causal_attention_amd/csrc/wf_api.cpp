@@ -171,7 +171,7 @@ std::vector<int32_t> build_work_list(int first, int n, int heads, int N, int T, 
         if (cus_per_xcd > 0) order_piece(p, cus_per_xcd);
         M = std::max(M, p.size());
     }
-    std::vector<int32_t> out(M * wf::kXcds, -1);
+    std::vector<int32_t> out(M * wf::kXcds, wf::kIdleWork);
     for (int x = 0; x < wf::kXcds; ++x)
         for (size_t j = 0; j < piece[x].size(); ++j)
             out[j * wf::kXcds + x] = wf::pack_work(piece[x][j].s, piece[x][j].h, piece[x][j].q);

@@ -57,7 +57,9 @@ constexpr int BN = 64;          // keys per tile
 #define WF_ATTN_STAGES 3
 #endif
 constexpr int NSTG = WF_ATTN_STAGES;   // K and V tile buffers each
-static_assert(NSTG >= 2 && NSTG <= 4, "2 to 4 tile stages");
+// A step waits only for the DMA issued one step earlier, so the tiles a step
+// reads were issued at least two steps before it: three stages at least.
+static_assert(NSTG >= 3 && NSTG <= 4, "3 or 4 tile stages");
 static_assert(NW >= 4 && NW <= 8 && BM % 32 == 0, "4 to 8 waves of 32 query rows");
 constexpr int kRescaleLog2 = 8; // running max may lag the true max by up to 2^8
 // Buffer offset past every region (each is under 2^31 bytes): loads zeros.
@@ -242,7 +244,7 @@ __global__ __launch_bounds__(NTH, NW == 4 ? 2 : 1) void attn_kernel(AttnArgs a) 
 
     const int tid = threadIdx.x;
     const int32_t unit = a.work[blockIdx.x];
-    if (unit < 0) return;                          // padding of the per-XCD work lists
+    if (unit == kIdleWork) return;                 // padding of the per-XCD work lists
     const int s = work_slot(unit);
     const int head = work_head(unit);
     const int qt = work_qtile(unit);

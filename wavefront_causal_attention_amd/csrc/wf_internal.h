@@ -16,11 +16,17 @@ constexpr int kMaxFp8Tiles = 4096;  // (context chunks) x (64-token blocks per c
 constexpr int kAttnBM = WF_ATTN_BM;  // query rows per attention workgroup (32 per wave)
 constexpr int kXcds = 8;           // MI355X: workgroup b runs on XCD b % 8
 
-// Work-list entry of one attention workgroup: (slot, head, query tile), or -1.
-__host__ __device__ inline int32_t pack_work(int s, int h, int q) { return (s << 26) | (h << 16) | q; }
-__host__ __device__ inline int work_slot(int32_t w) { return (w >> 26) & 63; }
-__host__ __device__ inline int work_head(int32_t w) { return (w >> 16) & 1023; }
-__host__ __device__ inline int work_qtile(int32_t w) { return w & 0xFFFF; }
+// Work-list entry of one attention workgroup: (slot, head, query tile) in the
+// bit fields 31..26, 25..16 and 15..0 of a uint32 (slot < 64, head < 1024,
+// query tile <= 0xFFFE), or kIdleWork for padding. All-ones cannot be a unit
+// because the query-tile field of a real unit is at most 0xFFFE.
+constexpr int32_t kIdleWork = -1;
+__host__ __device__ inline int32_t pack_work(int s, int h, int q) {
+    return (int32_t)(((uint32_t)s << 26) | ((uint32_t)h << 16) | (uint32_t)q);
+}
+__host__ __device__ inline int work_slot(int32_t w) { return (int)((uint32_t)w >> 26); }
+__host__ __device__ inline int work_head(int32_t w) { return (int)(((uint32_t)w >> 16) & 1023u); }
+__host__ __device__ inline int work_qtile(int32_t w) { return (int)((uint32_t)w & 0xFFFFu); }
 
 // Page formats (per layer, physical page `phys`, head `h`, page token `t`,
 // channel `d`). Both are made of 16-byte vectors of 8 bf16 values so that one

@@ -131,6 +131,12 @@ WORKLOADS = {
                       frame_h=8, frame_w=8, page_tokens=8, in_dtype="bf16", qk_dtype="bf16",
                       rope_split=_split(64), rope_theta=1e4, seed=17,
                       description="S=30, A=1, H=32: T=64, chunk 128 (2x8x8), page 8 (1024 pages), 2x64"),
+    # The most query slots the library takes: S = 62 (slots 32..62 use the
+    # work-list entry's high slot bits), T = 64, one 8x8 frame per chunk.
+    "slots62": Workload("slots62", S=62, A=1, H=0, heads=2, head_dim=64, chunk_frames=1,
+                        frame_h=8, frame_w=8, page_tokens=64, in_dtype="bf16", qk_dtype="bf16",
+                        rope_split=_split(64), rope_theta=1e4, seed=18,
+                        description="S=62, A=1, H=0: T=64, 63 query slots, chunk 64 (1x8x8), 2x64"),
     # fp8 QK with chunks shorter than one 64-key tile.
     "tiny_fp8": Workload("tiny_fp8", S=2, A=1, H=1, heads=2, head_dim=64, chunk_frames=1,
                          frame_h=6, frame_w=8, page_tokens=24, in_dtype="bf16", qk_dtype="fp8",
