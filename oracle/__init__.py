@@ -28,14 +28,18 @@ latent-frame position chunk_frames * chunk_id + frame; published Q/K stored as
 bf16 (or fp8 e4m3 with per-64-token-block absmax scales and a per-chunk K mean).
 
 Parity status: every function here is pinned by a CPU test against the pages'
-closed forms, invariants, brute force or a library routine, except the choice
-of the fp8 scale/mean scheme, which the pages do not describe (they only name
-an fp8 payload with scales); its encoder is pinned to torch's float8_e4m3fn
-cast, but the blocking and mean smoothing follow the workload description and
-are "parity unpinned" beyond that. Likewise the W8A8 format (e4m3, one scale
-per token and per output channel) is a reading: its quantiser is pinned to
-brute-force nearest rounding and its projection to exact rational arithmetic,
-but the choice of format and granularity is not fixed by the pages.
+closed forms, invariants, brute force or a library routine. The fp8 storage
+model (per-64-token block scales restarting at each chunk, the per-chunk K mean
+removed and added back) is pinned by properties of that definition: the
+half-step error bound per block, exact reconstruction at each block's absmax
+and of a chunk constant along tokens, a short last block with its own scale,
+power-of-two equivariance, and blocks restarting at every chunk of a built
+context; its encoder is pinned to torch's float8_e4m3fn cast. What the pages
+do not fix is the choice of that scheme (they only name an fp8 payload with
+scales). Likewise the W8A8 format (e4m3, one scale per token and per output
+channel) is a reading: its quantiser is pinned to brute-force nearest rounding
+and its projection to exact rational arithmetic, but the choice of format and
+granularity is not fixed by the pages.
 """
 from .schedule import (RoundSchedule, live_mask, legal_positions, GroupRing,
                        slot_position)
