@@ -80,8 +80,13 @@ def parse():
                          "instead of from a projection output; also times hipBLASLt addmm + publish. "
                          "w8a8: the hidden states are quantised to e4m3 per token each step and the "
                          "projection runs on e4m3 operands (weight quantised once, per output channel)")
+    ap.add_argument("--repeats", type=int, default=3,
+                    help="blocks of --steps steps timed in all (the first is the headline); median and "
+                         "min-max over the blocks are reported")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=1536, help="query rows per (slot, head) in the CPU sample")
+    ap.add_argument("--cpu-rows", type=int, default=0,
+                    help="query rows per (slot, head) in the CPU baseline; 0: the whole round")
+    ap.add_argument("--cpu-workers", type=int, default=16, help="oracle worker processes (at most)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="also run one device copy of this many MiB (counter calibration)")
     return ap.parse_args()
@@ -190,6 +195,32 @@ def main():
         step(evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+
+    # further blocks of K steps, for the median and spread over repeats (the
+    # first block above is the headline)
+    blocks = [{"ms_per_step": wall * 1e3 / K, "attention_ms": float(np.mean([e[1].elapsed_time(e[2]) for e in evs])),
+               "publish_ms": float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))}]
+    for _ in range(max(0, args.repeats - 1)):
+        rev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(K)]
+        torch.cuda.synchronize()
+        tb = time.perf_counter()
+        for i in range(K):
+            step(rev[i])
+        torch.cuda.synchronize()
+        blocks.append({"ms_per_step": (time.perf_counter() - tb) * 1e3 / K,
+                       "attention_ms": float(np.mean([e[1].elapsed_time(e[2]) for e in rev])),
+                       "publish_ms": float(np.mean([e[0].elapsed_time(e[1]) for e in rev]))})
+
+    # one GPU's share of the round: the noisiest slot alone (it reads the
+    # whole context, the critical consumer of the round), K launches
+    cev = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+    torch.cuda.synchronize()
+    cev[0].record(stream)
+    for i in range(K):
+        pool.attention(0, 0, 1, q, out, q_scales=qs, stream=stream)
+        cev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    slot0_ms = [cev[i].elapsed_time(cev[i + 1]) for i in range(K)]
 
     graph = None
     if args.graph:
@@ -342,6 +373,18 @@ def main():
                              "frac": round(pub_bytes / (pub_avg * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
                              "algorithmic_bytes": pub_bytes},
     }
+    def _spread(key):
+        v = [b[key] for b in blocks]
+        return {"median": round(float(np.median(v)), 4), "min": round(min(v), 4), "max": round(max(v), 4),
+                "blocks": [round(x, 4) for x in v]}
+    res["repeats"] = {"blocks": len(blocks), "steps_per_block": K, "ms_per_step": _spread("ms_per_step"),
+                      "attention_ms": _spread("attention_ms"), "publish_ms": _spread("publish_ms")}
+    f0 = 4.0 * w.N * w.N * w.head_dim * w.heads * w.T         # slot 0 reads all T chunks under either mask
+    s0 = float(np.mean(slot0_ms))
+    res["critical_slot"] = {"slot": 0, "key_chunks": w.T, "attention_ms": round(s0, 4),
+                            "attention_ms_minmax": [round(min(slot0_ms), 4), round(max(slot0_ms), 4)],
+                            "flops": f0, "tflops": round(f0 / (s0 * 1e-3) / 1e12, 2),
+                            "launches": K}
     if graph is not None:
         res["graph"] = graph
     if proj is not None:
@@ -351,39 +394,40 @@ def main():
         del res["publish_roofline"]
         del res["publish_gbps"]
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(w, args.cpu_rows)
+        res["cpu_baseline"] = cpu_baseline(w, args.cpu_rows, args.cpu_workers)
     print(json.dumps(res), flush=True)
 
 
-def cpu_baseline(w, rows_per_slot_head):
-    """The fp64 oracle on a bounded sample of the same round, timed on the host.
+def cpu_baseline(w, rows_per_slot_head, max_workers):
+    """The fp64 oracle on the same round, timed on the host's cores.
 
-    Sample: every slot and head, `rows_per_slot_head` query rows each, over
-    the full legal context (RoPE of every context chunk included); FLOPs are
-    the mask-aware QK^T + PV FLOPs of the sampled rows."""
+    The oracle as it stands evaluates every (slot, head) unit of the round
+    (every query row, or `rows_per_slot_head` rows spread over the chunk),
+    each unit in a worker process with single-threaded BLAS, one worker per
+    core up to `max_workers`; each worker draws the round's seeded inputs
+    once and rotates the context chunks of its heads. FLOPs are the
+    mask-aware QK^T + PV FLOPs of the evaluated rows."""
     import numpy as np
-    import wf_inputs as W
-    from oracle import RoundSchedule, rotated_context, round_attention
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-    except Exception:
-        threads = len(os.sched_getaffinity(0))
+    from oracle.parallel import host_workers, oracle_units
+    workers = host_workers(max_workers)
     k = w.steady_round
-    sch = RoundSchedule(w.S, w.A, w.H, k)
-    live = W.draw_slots(w, k, range(w.S + 1))
-    clean = {c: W.stored_draw(w, c)[1:] for c in sch.chunk_ids()[:w.A + w.H]}
-    rows = np.linspace(0, w.N - 1, rows_per_slot_head).astype(np.int64)
+    rows = None if rows_per_slot_head <= 0 else np.linspace(0, w.N - 1, rows_per_slot_head).astype(np.int64)
+    nrows = w.N if rows is None else len(rows)
+    units = [(s, (h,)) for s in range(w.S + 1) for h in range(w.heads)]
+    storage = "fp8" if w.qk_dtype == "fp8" else "bf16"        # the published page format
     t0 = time.perf_counter()
-    Qs, ck, cv, _ = rotated_context(w, k, live, clean, storage=w.qk_dtype)
-    round_attention(Qs, ck, cv, w.S, w.A, w.H, rows=rows)
+    for _ in oracle_units(w, k, units, storage, rows=rows, workers=workers):
+        pass
     dt = time.perf_counter() - t0
-    flops = sum(4.0 * len(rows) * (w.T - s) * w.N * w.head_dim * w.heads for s in range(w.S + 1))
-    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+    pairs = w.key_chunk_pairs()
+    flops = 4.0 * nrows * w.N * w.head_dim * w.heads * pairs
+    what = "the whole round" if rows is None else "%d query rows per (slot, head)" % nrows
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(workers),
             "kind": "oracle",
-            "sample": "%s round k=%d: RoPE of all %d context chunks + attention of %d query rows "
-                      "per (slot, head), all %d slots x %d heads, fp64 numpy; %.1f s"
-                      % (w.name, k, w.T, len(rows), w.S + 1, w.heads, dt)}
+            "sample": "%s round k=%d, %s: all %d slots x %d heads over the full legal context, "
+                      "RoPE and %s storage of the context chunks included; fp64 numpy, %d worker "
+                      "processes x 1 BLAS thread; %.1f s"
+                      % (w.name, k, what, w.S + 1, w.heads, storage, workers, dt)}
 
 
 if __name__ == "__main__":

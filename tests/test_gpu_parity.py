@@ -3,7 +3,8 @@
 Floating-point bar (bf16 path): max-abs <= 1e-2 and relative L2 <= 5e-3 on the
 fp32 output mode, against the oracle with bf16 storage of the published Q/K
 (the pages' BF16 backend publishes bf16 pages). Integer work (page table,
-placement, schedule) is compared bit for bit.
+placement, schedule) is compared bit for bit, and so are the published pages:
+each is the round-to-nearest-even of the fp64 rotation (V: of the input).
 """
 import sys
 
@@ -70,13 +71,16 @@ def test_round_parity_full(name):
     assert np.array_equal(gb, bf16_round(g))
 
 
-@pytest.mark.parametrize("name", ["tiny", "ragged128", "ragged64", "edge_s1_h0"])
+@pytest.mark.parametrize("name", ["tiny", "ragged128", "ragged64", "edge_s1_h0", "wan1.3b_s4", "wan14b_s4"])
 def test_page_table_and_publish_placement(name):
+    """Page table against the closed form; every published Q, K and V element
+    equal, bit for bit, to the bf16 rounding of the oracle's fp64 RoPE (V: of
+    the input), at its closed-form place in the pages."""
     w = W.WORKLOADS[name]
     say("case", name, "placement")
     r = RoundRunner(w)
     r.seed_clean()
-    r.publish_live()
+    r.publish_live(live=W.draw_slots(w, r.k, range(w.S + 1)))
     torch.cuda.synchronize()
     pool = r.pool
     ppc = pool.ppc
@@ -111,7 +115,6 @@ def test_page_table_and_publish_placement(name):
         vref = np.asarray(vv, dtype=np.float64).reshape(w.N, w.heads, w.head_dim).transpose(1, 0, 2)
         assert np.array_equal(vg.astype(np.float64), bf16_round(vref)), p        # V bit-exact
         ulp = _bf16_ulps(kg, kref)
-        assert ulp.max() <= 1, p
         total += ulp.size
         diff += int(np.count_nonzero(ulp))
     # Q rows of the live slots
@@ -119,11 +122,10 @@ def test_page_table_and_publish_placement(name):
     for s in range(w.S + 1):
         qref = bf16_round(rotate_chunk(w, sch.slot_chunk(s), r.live[s][0])).transpose(1, 0, 2)
         ulp = _bf16_ulps(qbits[s], qref)
-        assert ulp.max() <= 1, s
         total += ulp.size
         diff += int(np.count_nonzero(ulp))
-    say(name, "Q/K elements differing by 1 ulp: %d of %d" % (diff, total))
-    assert diff <= 1e-3 * total
+    say(name, "Q/K elements differing from RNE(fp64 RoPE): %d of %d" % (diff, total))
+    assert diff == 0
 
 
 @pytest.mark.parametrize("name", ["ragged128", "tiny", "edge_s1_h0"])
@@ -215,7 +217,7 @@ def _sample_rows(N, seed, extra=16):
 def test_full_size_round_every_output(name):
     """Every output row of every head and slot of a full-size round (fp32
     output mode) against the oracle, which runs on the host's cores."""
-    from _oracle_pool import compare_every_output, host_workers
+    from oracle.parallel import compare_every_output, host_workers
     w = W.WORKLOADS[name]
     say("case", name, "full size, every output;", host_workers(), "oracle workers")
     r = RoundRunner(w)
@@ -234,7 +236,7 @@ def test_thirty_layer_rounds_with_rotation():
     """30 consecutive layer-rounds of one pool, advancing in between: every
     output of the first and the last round, sampled rows of one head in the
     rounds between, and the device page table after every advance."""
-    from _oracle_pool import compare_every_output
+    from oracle.parallel import compare_every_output
     w = W.WORKLOADS["wan1.3b_s5_30"]
     say("case", w.name, "30 consecutive layer-rounds")
     r = RoundRunner(w)

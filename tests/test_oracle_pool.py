@@ -7,7 +7,7 @@ import pytest
 import wf_inputs as W
 from oracle import RoundSchedule, oracle_round
 
-from _oracle_pool import compare_every_output, oracle_units
+from oracle.parallel import compare_every_output, oracle_units
 
 
 def _serial(w, k, storage):

@@ -36,8 +36,9 @@ __host__ __device__ inline int work_qtile(int32_t w) { return (int)((uint32_t)w 
 // With fp8 Q/K the K pages hold e4m3 codes in 16-byte vectors of 16 channels:
 //   K8: [phys][h][D/16][page_tokens][16]  byte (t, d) at ((d/16)*pt + t)*16 + d%16
 // plus, per layer, the scale of each token's 64-token block
-// kscale[phys][h][page_tokens] (fp32), the chunk's K channel mean
-// kmean[group][h][D] (fp32) and per-block partial sums kpart[group][h][nblk][D].
+// kscale[phys][h][page_tokens] (fp32) and the chunk's K channel mean
+// kmean[group][h][D] (fp32); the publish's scratch (sync words and fp64
+// per-block K sums) follows them.
 // Physical page of (context position p, page i of its chunk) = table[p*ppc + i].
 __host__ __device__ inline int64_t k8_byte(int64_t page_head_base, int pt, int t, int d) {
     return page_head_base + ((int64_t)(d >> 4) * pt + t) * 16 + (d & 15);
@@ -61,10 +62,11 @@ struct PublishArgs {
     uint16_t* vpage;          // this layer's V pages (format above)
     float* kscale;            // fp8: per-token K scale [phys][head][pt]
     float* kmean;             // fp8: [group][head][D]
-    float* kpart;             // fp8: [group][head][nblk][D] partial sums
+    uint32_t* fsync;          // fp8 scratch: ticket, error word, 3 words per (published slot, head)
+    double* kpart;            // fp8 scratch: [published slot][head][nblk][D] block sums of RoPE'd K
     const int32_t* table;     // page table [T][ppc]
-    const float2* htab;       // RoPE row-axis (cos, sin) [frame_h][dh/2]
-    const float2* wtab;       // RoPE column-axis (cos, sin) [frame_w][dw/2]
+    const double2* htab;      // RoPE row-axis (cos, sin) [frame_h][dh/2], fp64
+    const double2* wtab;      // RoPE column-axis (cos, sin) [frame_w][dw/2], fp64
     const double* omega_t;    // RoPE time-axis frequencies [dt/2]
     int N, heads, D, pt, ppc, T, S;
     int frame_h, frame_w;
@@ -159,6 +161,11 @@ hipError_t launch_quant_rows(const uint16_t* x, int64_t rows, int cols, int64_t 
 hipError_t launch_page_table(int32_t* table, int T, int A, int ppc, int64_t ring, int64_t* ring_dev, int store_pos,
                              int store_anchor, hipStream_t st);
 hipError_t launch_publish(const PublishArgs& a, bool fp8, hipStream_t st);
+// fp8 publish scratch words per layer for T positions and `heads` heads
+inline size_t fp8_sync_words(int T, int heads) { return 2 + 3 * (size_t)T * heads; }
+// resident fp8 publish blocks per CU (0 if the runtime cannot tell): the
+// blocks of one chunk wait for each other, so they must fit on the GPU at once
+int fp8_publish_blocks_per_cu(int D, bool in_fp32, int frame_hw);
 hipError_t launch_attention(const AttnArgs& a, bool fp8, hipStream_t st);
 
 }  // namespace wf

@@ -23,8 +23,8 @@ constexpr int kMaxFramesPerTile = kTokTile + 2;
 
 // Time-axis (cos, sin) table of the frames one publish block (at most 64
 // tokens) touches, in dynamic LDS sized per launch: frames_per_tile(HW) rows
-// of 32 pairs.
-extern __shared__ float2 g_ttab_dyn[];
+// of 32 fp64 pairs.
+extern __shared__ double2 g_ttab_dyn[];
 __host__ __device__ inline int frames_per_tile(int hw) {
     const int f = (kTokTile + hw - 1) / hw + 1;
     return f < kMaxFramesPerTile ? f : kMaxFramesPerTile;
@@ -106,19 +106,57 @@ __device__ __forceinline__ uint4 pack8(const float* x) {
                       pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7]));
 }
 
-// Rotate the 4 channel pairs of one 8-channel vector starting at channel c0.
-__device__ __forceinline__ void rope8(float* x, int c0, const float2* ttab_f, const float2* hrow,
-                                      const float2* wrow, int dt, int dh) {
+// Rotate the 4 channel pairs of one 8-channel vector starting at channel c0,
+// in fp64 from fp64 (cos, sin) tables: the published page holds the rotated
+// value rounded once to the page format, so the rotation itself must be
+// accurate far below a bf16 (or e4m3) rounding step. In fp32 about one element
+// in 10^5 landed on the other side of a bf16 rounding midpoint, which on a
+// x20 outlier channel moves a score by several units.
+__device__ __forceinline__ void rope8(const float* x, double* y, int c0, const double2* ttab_f,
+                                      const double2* hrow, const double2* wrow, int dt, int dh) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int c = c0 + 2 * i;
-        float2 cs;
+        double2 cs;
         if (c < dt) cs = ttab_f[c >> 1];
         else if (c < dt + dh) cs = hrow[(c - dt) >> 1];
         else cs = wrow[(c - dt - dh) >> 1];
-        const float a = x[2 * i], b = x[2 * i + 1];
-        x[2 * i] = fmaf(a, cs.x, -b * cs.y);
-        x[2 * i + 1] = fmaf(a, cs.y, b * cs.x);
+        const double a = x[2 * i], b = x[2 * i + 1];
+        y[2 * i] = fma(a, cs.x, -(b * cs.y));
+        y[2 * i + 1] = fma(a, cs.y, b * cs.x);
+    }
+}
+
+// fp64 -> fp32 rounding to odd: truncate toward zero and set the last bit if
+// inexact. A round-to-nearest-even of the result into a format at least two
+// significand bits narrower than fp32 (bf16: 8 bits, e4m3: 4) then equals the
+// round-to-nearest-even of the fp64 value itself, with no double rounding.
+// NaN stays NaN; beyond the fp32 range the result is the largest finite value.
+__device__ __forceinline__ float to_f32_odd(double x) {
+    const float y = (float)x;
+    const double yd = (double)y;
+    uint32_t b = __float_as_uint(y);
+    const uint32_t toward_zero = fabs(yd) > fabs(x) ? 1u : 0u;
+    b = yd != x ? ((b - toward_zero) | 1u) : b;
+    return __uint_as_float(b);
+}
+
+__device__ __forceinline__ uint4 pack8_f64(const double* y) {
+    return make_uint4(pack_bf16x2(to_f32_odd(y[0]), to_f32_odd(y[1])), pack_bf16x2(to_f32_odd(y[2]), to_f32_odd(y[3])),
+                      pack_bf16x2(to_f32_odd(y[4]), to_f32_odd(y[5])), pack_bf16x2(to_f32_odd(y[6]), to_f32_odd(y[7])));
+}
+
+// fp64 time-axis (cos, sin) of the frames f_lo .. f_lo + nf - 1 of published
+// slot sr (the slot's absolute time offset plus the frame).
+template <typename Args>
+__device__ __forceinline__ void fill_ttab(double2 (*ttab)[32], const Args& a, int sr, int f_lo, int nf) {
+    const int hp = a.dt >> 1;
+    for (int i = threadIdx.x; i < nf * hp; i += blockDim.x) {
+        const int fi = i / hp, m = i - fi * hp;
+        const double phi = (double)(slot_t0(a, sr) + f_lo + fi) * a.omega_t[m];
+        double sn, cs;
+        sincos(phi, &sn, &cs);
+        ttab[fi][m] = make_double2(cs, sn);
     }
 }
 
@@ -129,7 +167,7 @@ __device__ __forceinline__ void rope8(float* x, int c0, const float2* ttab_f, co
 template <int D, bool IN_FP32>
 __global__ __launch_bounds__(256) void publish_bf16_kernel(PublishArgs a) {
     constexpr int CPR = D / 8;                       // 8-channel vectors per token row
-    float2 (*ttab)[32] = reinterpret_cast<float2 (*)[32]>(g_ttab_dyn);   // time-axis (cos, sin), this tile's frames
+    double2 (*ttab)[32] = reinterpret_cast<double2 (*)[32]>(g_ttab_dyn);   // time-axis (cos, sin), this tile's frames
     __shared__ __align__(16) uint4 kst[CPR * kTokB];       // K vectors, [ch][tok ^ (ch & 7)]
     __shared__ __align__(16) uint16_t vst[kTokB * D];      // V rows, [tok][d]
 
@@ -143,7 +181,6 @@ __global__ __launch_bounds__(256) void publish_bf16_kernel(PublishArgs a) {
     const int f_lo = n0 / HW;
     const int n_hi = min(n0 + kTokB, a.N) - 1;
     const int nf = n_hi / HW - f_lo + 1;
-    const int hp = a.dt >> 1;
 
     const int64_t row0 = (int64_t)sr * a.N;
     const int64_t col = (int64_t)head * D;
@@ -153,15 +190,16 @@ __global__ __launch_bounds__(256) void publish_bf16_kernel(PublishArgs a) {
         const int f = n / HW;
         const int yy = (n / a.frame_w) % a.frame_h;
         const int xw = n % a.frame_w;
-        const float2* tf = ttab[f - f_lo];
-        const float2* hrow = a.htab + yy * (a.dh >> 1);
-        const float2* wrow = a.wtab + xw * (a.dw >> 1);
-        rope8(x, ch * 8, tf, hrow, wrow, a.dt, a.dh);
-        kst[ch * kTokB + (tk ^ (ch & 7))] = pack8(x);
+        const double2* tf = ttab[f - f_lo];
+        const double2* hrow = a.htab + yy * (a.dh >> 1);
+        const double2* wrow = a.wtab + xw * (a.dw >> 1);
+        double r[8];
+        rope8(x, r, ch * 8, tf, hrow, wrow, a.dt, a.dh);
+        kst[ch * kTokB + (tk ^ (ch & 7))] = pack8_f64(r);
         if (a.q) {
-            rope8(y, ch * 8, tf, hrow, wrow, a.dt, a.dh);
+            rope8(y, r, ch * 8, tf, hrow, wrow, a.dt, a.dh);
             uint16_t* qp = static_cast<uint16_t*>(a.q_out) + (((int64_t)s * a.heads + head) * a.N + n) * D + ch * 8;
-            st16(qp, pack8(y));
+            st16(qp, pack8_f64(r));
         }
         *reinterpret_cast<uint4*>(&vst[tk * D + ch * 8]) = pack8(z);
     };
@@ -180,14 +218,7 @@ __global__ __launch_bounds__(256) void publish_bf16_kernel(PublishArgs a) {
             vr[i] = ld_stream16(static_cast<const uint16_t*>(a.v) + e);
             qr[i] = a.q ? ld_stream16(static_cast<const uint16_t*>(a.q) + e) : make_uint4(0, 0, 0, 0);
         }
-        // time-axis angles in fp64: positions grow with the stream
-        for (int i = tid; i < nf * hp; i += 256) {
-            const int fi = i / hp, m = i - fi * hp;
-            const double phi = (double)(slot_t0(a, sr) + f_lo + fi) * a.omega_t[m];
-            double sn, cs;
-            sincos(phi, &sn, &cs);
-            ttab[fi][m] = make_float2((float)cs, (float)sn);
-        }
+        fill_ttab(ttab, a, sr, f_lo, nf);
         __syncthreads();
 #pragma unroll
         for (int i = 0; i < IT; ++i) {
@@ -200,13 +231,7 @@ __global__ __launch_bounds__(256) void publish_bf16_kernel(PublishArgs a) {
             rotate_and_stage(tk, ch, x, y, z);
         }
     } else {
-        for (int i = tid; i < nf * hp; i += 256) {
-            const int fi = i / hp, m = i - fi * hp;
-            const double phi = (double)(slot_t0(a, sr) + f_lo + fi) * a.omega_t[m];
-            double sn, cs;
-            sincos(phi, &sn, &cs);
-            ttab[fi][m] = make_float2((float)cs, (float)sn);
-        }
+        fill_ttab(ttab, a, sr, f_lo, nf);
         __syncthreads();
         for (int c = tid; c < kTokB * CPR; c += 256) {
             const int tk = c / CPR, ch = c - tk * CPR;
@@ -251,13 +276,38 @@ __global__ __launch_bounds__(256) void publish_bf16_kernel(PublishArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// fp8 e4m3 publish. Q and K are quantised per 64-token block of their chunk
-// (blocks restart at each chunk start, so a publish block is exactly one
-// quantisation block): scale = absmax / 448, codes = RNE(x / scale) clamped to
-// +-448. K first has its chunk's per-channel mean removed; attention adds the
-// mean back exactly as q . mean. V stays bf16. Three launches, all with fixed
-// summation orders: per-block partial sums of RoPE'd K, their reduction to the
-// chunk mean, then the quantising publish.
+// fp8 e4m3 publish, one launch. Q and K are quantised per 64-token block of
+// their chunk (blocks restart at each chunk start, so a publish block is
+// exactly one quantisation block): scale = fp32 absmax / 448 (IEEE divide, 1
+// for an all-zero block), code = round-to-nearest-even of value / scale,
+// saturating at +-448, every decision taken on the fp64 value. K first has its
+// chunk's per-channel mean removed, the mean rounded to fp32; attention adds
+// it back exactly as q . mean. V stays bf16.
+//
+// The K codes need the mean of the whole chunk, so the blocks of one (slot,
+// head) chunk meet once: each block posts the fp64 sum of its RoPE'd K rows,
+// and the chunk's last block to post sums the posts in block order, stores
+// the mean and raises the chunk's flag, which the other blocks wait for. A
+// block writes its Q codes and V pages before it waits and keeps its RoPE'd K
+// in registers across the wait, so Q, K and V are read from HBM once.
+//
+// Blocks take their unit (slot, head, block) from a ticket counter in the
+// order they start, a chunk's blocks consecutively, so every ticket below a
+// waiting block's belongs to a block that has started. Every chunk whose
+// tickets all lie below the highest ticket issued so far has all its posts
+// in, so its blocks finish and make room; only the chunk holding that ticket
+// can wait, and its blocks fit on the GPU together as long as one chunk has
+// no more blocks than the GPU holds at once (checked on the host when the
+// pool is created). The wait is bounded all the same: after kFp8SpinLimit
+// polls a block gives up, raises the error word and proceeds.
+//
+// Scratch (per layer): sync words [0] ticket, [1] error, then per (published
+// slot, head) unit u: [2 + 3u] arrivals, [3 + 3u] flag, [4 + 3u] departures,
+// all zero between launches (the last ticket resets the ticket counter, the
+// last arrival the arrivals, the last departure the flag and departures);
+// then the partial sums kpart[unit][block][D] in fp64.
+
+constexpr uint32_t kFp8SpinLimit = 1u << 22;
 
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
@@ -277,207 +327,139 @@ __device__ __forceinline__ uint32_t fp8x4(float a, float b, float c, float d) {
     return lo | (hi << 16);
 }
 
-// Fill the time-axis (cos, sin) table for the frames of one 64-token block.
-__device__ __forceinline__ void fill_ttab(float2 (*ttab)[32], const PublishArgs& a, int sr, int f_lo,
-                                          int nf) {
-    const int hp = a.dt >> 1;
-    for (int i = threadIdx.x; i < nf * hp; i += 256) {
-        const int fi = i / hp, m = i - fi * hp;
-        const double phi = (double)(slot_t0(a, sr) + f_lo + fi) * a.omega_t[m];
-        double sn, cs;
-        sincos(phi, &sn, &cs);
-        ttab[fi][m] = make_float2((float)cs, (float)sn);
+// x / scale to nearest even e4m3 for 8 values: the quotient in fp64 from the
+// reciprocal r = 1/scale (correctly rounded) and one remainder correction
+// (q0 = x r, e = x - q0 scale exactly by fma, q = q0 + e r), then rounded
+// to odd into fp32, which the hardware's nearest-even conversion keeps exact.
+__device__ __forceinline__ uint2 quant8(const double* x, double sc, double r) {
+    float q[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const double q0 = x[e] * r;
+        const double rem = fma(-q0, sc, x[e]);
+        q[e] = to_f32_odd(fma(rem, r, q0));
     }
+    return make_uint2(fp8x4(q[0], q[1], q[2], q[3]), fp8x4(q[4], q[5], q[6], q[7]));
 }
 
-// grid (ceil(N/64), heads, nslots): per 64-token block, the per-channel sum of
-// RoPE'd K over its valid tokens -> kpart[group][head][block][D].
-template <int D, bool IN_FP32>
-__global__ __launch_bounds__(256) void kmean_partial_kernel(PublishArgs a) {
-    constexpr int CPR = D / 8;
-    constexpr int ROWS = 256 / CPR;                  // token lanes per channel vector
-    float2 (*ttab)[32] = reinterpret_cast<float2 (*)[32]>(g_ttab_dyn);
-    __shared__ float part[ROWS][D];
-    const int tid = threadIdx.x;
-    const int sr = blockIdx.z, s = a.slot_first + sr, head = blockIdx.y, n0 = blockIdx.x * kTokTile;
-    const int p = a.T - 1 - s;
-    const int HW = a.frame_h * a.frame_w;
-    const int f_lo = n0 / HW;
-    const int nf = (min(n0 + kTokTile, a.N) - 1) / HW - f_lo + 1;
-    const int ch = tid % CPR, row = tid / CPR;
-    constexpr int IT = kTokTile / ROWS;
-    // rows of this thread, loaded before the time table is built (rows past
-    // the chunk are clamped to its last row and not summed)
-    Raw8<IN_FP32> kin[IT];
-#pragma unroll
-    for (int i = 0; i < IT; ++i) {
-        const int n = min(n0 + row + ROWS * i, a.N - 1);
-        kin[i].load(a.k, ((int64_t)sr * a.N + n) * a.row_stride + (int64_t)head * D + ch * 8);
-    }
-    fill_ttab(ttab, a, sr, f_lo, nf);
+// Largest |x| of the block, as fp32 (rounding is monotonic, so the fp32
+// rounding of the fp64 maximum); `red` holds one float per wave.
+__device__ __forceinline__ float block_absmax(float v, float* red) {
+    v = wave_max(v);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
     __syncthreads();
-    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-#pragma unroll
-    for (int i = 0; i < IT; ++i) {
-        const int n = n0 + row + ROWS * i;
-        if (n >= a.N) break;
-        const int y = (n / a.frame_w) % a.frame_h, xw = n % a.frame_w;
-        float x[8];
-        kin[i].unpack(x);
-        rope8(x, ch * 8, ttab[n / HW - f_lo], a.htab + y * (a.dh >> 1), a.wtab + xw * (a.dw >> 1), a.dt, a.dh);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] += x[e];
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) part[row][ch * 8 + e] = acc[e];
+    const float m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
     __syncthreads();
-    if (tid < D) {
-        float sum = 0.f;
-        for (int r = 0; r < ROWS; ++r) sum += part[r][tid];
-        const int g = a.table[p * a.ppc] / a.ppc;
-        a.kpart[(((int64_t)g * a.heads + head) * a.nblk + blockIdx.x) * D + tid] = sum;
-    }
+    return m;
 }
 
-// grid (heads, nslots), block D: kmean[group][head][d] = sum of the chunk's
-// block partials (fixed order) / N.
-template <int D>
-__global__ void kmean_reduce_kernel(PublishArgs a) {
-    const int s = a.slot_first + blockIdx.y, head = blockIdx.x, d = threadIdx.x;
-    const int g = a.table[(a.T - 1 - s) * a.ppc] / a.ppc;
-    const float* src = a.kpart + ((int64_t)g * a.heads + head) * a.nblk * D + d;
-    // eight loads in flight per iteration, summed in block order
-    float sum = 0.f;
-    int b = 0;
-    for (; b + 8 <= a.nblk; b += 8) {
-        float v[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = src[(int64_t)(b + u) * D];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) sum += v[u];
-    }
-    for (; b < a.nblk; ++b) sum += src[(int64_t)b * D];
-    a.kmean[((int64_t)g * a.heads + head) * D + d] = sum / (float)a.N;
-}
-
-// grid (ceil(N/64), heads, nslots): quantise and publish one 64-token block.
+// grid: nslots * heads * ceil(N/64) blocks of 256 threads; one block per
+// (slot, head, 64-token block), assigned by ticket.
 template <int D, bool IN_FP32>
 __global__ __launch_bounds__(256) void publish_fp8_kernel(PublishArgs a) {
     constexpr int CPR = D / 8;                       // 8-channel vectors per token row
-    constexpr int ITEMS = kTokTile * CPR / 256;
+    constexpr int ITEMS = kTokTile * CPR / 256;      // vectors per thread
+    constexpr int ROWS = 256 / CPR;                  // token rows a pass of the block covers
     constexpr int C16 = D / 16;                      // 16-byte code vectors per token row
-    float2 (*ttab)[32] = reinterpret_cast<float2 (*)[32]>(g_ttab_dyn);
+    double2 (*ttab)[32] = reinterpret_cast<double2 (*)[32]>(g_ttab_dyn);
+    __shared__ double part[ROWS][D];
     __shared__ float mu[D];
-    __shared__ float red[2][4];
+    __shared__ float red[4];
+    __shared__ int s_unit, s_last;
     __shared__ __align__(16) uint8_t kcodes[kTokTile * D];   // [tok][16-byte vector ^ (tok % C16)]
     __shared__ __align__(16) uint16_t vst[kTokTile * D];     // V rows, [tok][d]
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int sr = blockIdx.z, s = a.slot_first + sr, head = blockIdx.y, n0 = blockIdx.x * kTokTile;
+    const int tid = threadIdx.x;
+    const int nunit = a.nslots * a.heads;
+    uint32_t* const sync = a.fsync;
+    if (tid == 0) {
+        const uint32_t t = __hip_atomic_fetch_add(sync, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (t == (uint32_t)(nunit * a.nblk) - 1u)     // the last ticket: every block has one
+            __hip_atomic_store(sync, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_unit = (int)t;
+    }
+    __syncthreads();
+    const int ticket = s_unit;
+    const int blk = ticket % a.nblk;
+    const int u = ticket / a.nblk;                   // (published slot, head) unit
+    const int head = u % a.heads, sr = u / a.heads;
+    const int s = a.slot_first + sr, n0 = blk * kTokTile;
     const int p = a.T - 1 - s;
     const int HW = a.frame_h * a.frame_w;
     const int f_lo = n0 / HW;
     const int nf = (min(n0 + kTokTile, a.N) - 1) / HW - f_lo + 1;
     const int64_t row0 = (int64_t)sr * a.N;
     const int64_t col = (int64_t)head * D;
-    // K and V rows of this thread are loaded before the tables are built
-    // (rows past the chunk are clamped to its last row and not used)
+    const int ch = tid % CPR, row = tid / CPR;       // every item of this thread: channels ch*8 .. +7
+    // rows of this thread, loaded before the tables are built (rows past the
+    // chunk are clamped to its last row and not used)
     Raw8<IN_FP32> kin[ITEMS], qin[ITEMS], vin[ITEMS];
 #pragma unroll
     for (int i = 0; i < ITEMS; ++i) {
-        const int c = tid + 256 * i;
-        const int tk = c / CPR, ch = c - tk * CPR;
+        const int tk = row + ROWS * i;
         const int64_t e0 = (row0 + min(n0 + tk, a.N - 1)) * a.row_stride + col + ch * 8;
         kin[i].load(a.k, e0);
         vin[i].load(a.v, e0);
         if (a.q) qin[i].load(a.q, e0);
     }
     fill_ttab(ttab, a, sr, f_lo, nf);
-    const int g = a.table[p * a.ppc] / a.ppc;
-    if (tid < D) mu[tid] = a.kmean[((int64_t)g * a.heads + head) * D + tid];
     __syncthreads();
 
-    float kx[ITEMS][8], qx[ITEMS][8];
-    float kmax = 0.f, qmax = 0.f;
+    // K rotated in fp64 (kept for after the mean), its column sums; V staged
+    double kx[ITEMS][8];
+    double ksum[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
     for (int i = 0; i < ITEMS; ++i) {
-        const int c = tid + 256 * i;
-        const int tk = c / CPR, ch = c - tk * CPR;
-        const int n = n0 + tk;
+        const int tk = row + ROWS * i, n = n0 + tk;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) kx[i][e] = qx[i][e] = 0.f;
+        for (int e = 0; e < 8; ++e) kx[i][e] = 0.0;
         if (n >= a.N) continue;
-        kin[i].unpack(kx[i]);
         const int y = (n / a.frame_w) % a.frame_h, xw = n % a.frame_w;
-        const float2* tf = ttab[n / HW - f_lo];
-        const float2* hrow = a.htab + y * (a.dh >> 1);
-        const float2* wrow = a.wtab + xw * (a.dw >> 1);
-        rope8(kx[i], ch * 8, tf, hrow, wrow, a.dt, a.dh);
+        float x[8];
+        kin[i].unpack(x);
+        rope8(x, kx[i], ch * 8, ttab[n / HW - f_lo], a.htab + y * (a.dh >> 1), a.wtab + xw * (a.dw >> 1), a.dt,
+              a.dh);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            kx[i][e] -= mu[ch * 8 + e];
-            kmax = fmaxf(kmax, fabsf(kx[i][e]));
-        }
-        if (a.q) {
-            qin[i].unpack(qx[i]);
-            rope8(qx[i], ch * 8, tf, hrow, wrow, a.dt, a.dh);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) qmax = fmaxf(qmax, fabsf(qx[i][e]));
-        }
-        float vx[8];
-        vin[i].unpack(vx);
-        *reinterpret_cast<uint4*>(&vst[tk * D + ch * 8]) = pack8(vx);
+        for (int e = 0; e < 8; ++e) ksum[e] += kx[i][e];
+        vin[i].unpack(x);
+        *reinterpret_cast<uint4*>(&vst[tk * D + ch * 8]) = pack8(x);
     }
-    kmax = wave_max(kmax);
-    qmax = wave_max(qmax);
-    if (lane == 0) {
-        red[0][wave] = kmax;
-        red[1][wave] = qmax;
-    }
-    __syncthreads();
-    kmax = fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3]));
-    qmax = fmaxf(fmaxf(red[1][0], red[1][1]), fmaxf(red[1][2], red[1][3]));
-    const float ks = kmax > 0.f ? kmax / 448.f : 1.f;     // per-block scales (IEEE divide)
-    const float qs = qmax > 0.f ? qmax / 448.f : 1.f;
-    const float kinv = 1.f / ks, qinv = 1.f / qs;
 #pragma unroll
-    for (int i = 0; i < ITEMS; ++i) {
-        const int c = tid + 256 * i;
-        const int tk = c / CPR, ch = c - tk * CPR;
-        const int n = n0 + tk;
-        if (n >= a.N) continue;
-        const int v16 = ch >> 1;                     // 16-byte vector of this 8-channel group
-        uint2 kc = make_uint2(fp8x4(kx[i][0] * kinv, kx[i][1] * kinv, kx[i][2] * kinv, kx[i][3] * kinv),
-                              fp8x4(kx[i][4] * kinv, kx[i][5] * kinv, kx[i][6] * kinv, kx[i][7] * kinv));
-        *reinterpret_cast<uint2*>(&kcodes[(tk * C16 + (v16 ^ (tk % C16))) * 16 + (ch & 1) * 8]) = kc;
-        if (a.q) {
-            uint2 qc = make_uint2(fp8x4(qx[i][0] * qinv, qx[i][1] * qinv, qx[i][2] * qinv, qx[i][3] * qinv),
-                                  fp8x4(qx[i][4] * qinv, qx[i][5] * qinv, qx[i][6] * qinv, qx[i][7] * qinv));
+    for (int e = 0; e < 8; ++e) part[row][ch * 8 + e] = ksum[e];
+
+    // Q: rotate, block absmax, codes, scale (no mean)
+    if (a.q) {
+        double qx[ITEMS][8];
+        float qm = 0.f;
+#pragma unroll
+        for (int i = 0; i < ITEMS; ++i) {
+            const int n = n0 + row + ROWS * i;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) qx[i][e] = 0.0;
+            if (n >= a.N) continue;
+            const int y = (n / a.frame_w) % a.frame_h, xw = n % a.frame_w;
+            float x[8];
+            qin[i].unpack(x);
+            rope8(x, qx[i], ch * 8, ttab[n / HW - f_lo], a.htab + y * (a.dh >> 1), a.wtab + xw * (a.dw >> 1), a.dt,
+                  a.dh);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) qm = fmaxf(qm, (float)fabs(qx[i][e]));
+        }
+        qm = block_absmax(qm, red);
+        const float qs = qm > 0.f ? qm / 448.f : 1.f;
+        const double qr = 1.0 / (double)qs;
+#pragma unroll
+        for (int i = 0; i < ITEMS; ++i) {
+            const int n = n0 + row + ROWS * i;
+            if (n >= a.N) continue;
             uint8_t* qp = static_cast<uint8_t*>(a.q_out) + (((int64_t)s * a.heads + head) * a.N + n) * D + ch * 8;
-            *reinterpret_cast<uint2*>(qp) = qc;
+            *reinterpret_cast<uint2*>(qp) = quant8(qx[i], (double)qs, qr);
         }
+        if (tid == 0) a.q_scales[((int64_t)s * a.heads + head) * a.nblk + blk] = qs;
     }
-    if (a.q && tid == 0) a.q_scales[((int64_t)s * a.heads + head) * a.nblk + blockIdx.x] = qs;
     __syncthreads();
 
-    // K code pages: one 16-byte vector (16 channels of one token) per thread, tokens fastest
-    for (int j = tid; j < C16 * kTokTile; j += 256) {
-        const int v16 = j / kTokTile, tk = j - v16 * kTokTile;
-        const int n = n0 + tk;
-        if (n >= a.N) continue;
-        const int pg = n / a.pt, tok = n - pg * a.pt;
-        const int phys = a.table[p * a.ppc + pg];
-        const int64_t base = ((int64_t)phys * a.heads + head) * a.pt * D;
-        st16(static_cast<uint8_t*>(a.kpage) + k8_byte(base, a.pt, tok, v16 * 16),
-                    *reinterpret_cast<const uint4*>(&kcodes[(tk * C16 + (v16 ^ (tk % C16))) * 16]));
-    }
-    if (tid < kTokTile && n0 + tid < a.N) {
-        const int n = n0 + tid;
-        const int pg = n / a.pt, tok = n - pg * a.pt;
-        const int phys = a.table[p * a.ppc + pg];
-        a.kscale[((int64_t)phys * a.heads + head) * a.pt + tok] = ks;
-    }
-    // V pages as in the bf16 publish
+    // V pages as in the bf16 publish (independent of the mean)
     for (int j = tid; j < (kTokTile / 8) * D; j += 256) {
         const int kc = j / D, d = j - kc * D;
         const int n = n0 + kc * 8;
@@ -490,6 +472,114 @@ __global__ __launch_bounds__(256) void publish_fp8_kernel(PublishArgs a) {
         const int phys = a.table[p * a.ppc + pg];
         const int64_t base = ((int64_t)phys * a.heads + head) * a.pt * D;
         st16(a.vpage + v_elem(base, D, tok, d), make_uint4(w[0], w[1], w[2], w[3]));
+    }
+
+    // post this block's column sums of K (rows summed in a fixed order)
+    double* const kpart = a.kpart + (int64_t)u * a.nblk * D;
+    if (tid < D) {
+        double t = 0.0;
+        for (int r = 0; r < ROWS; ++r) t += part[r][tid];
+        kpart[(int64_t)blk * D + tid] = t;
+        __threadfence();                             // the post reaches L2 before the arrival count
+    }
+    uint32_t* const arrive = sync + 2 + 3 * u;
+    uint32_t* const flag = arrive + 1;
+    uint32_t* const depart = arrive + 2;
+    const int g = a.table[p * a.ppc] / a.ppc;
+    float* const kmean = a.kmean + ((int64_t)g * a.heads + head) * D;
+    __syncthreads();
+    if (tid == 0) {
+        const uint32_t before = __hip_atomic_fetch_add(arrive, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        s_last = before == (uint32_t)a.nblk - 1u;
+    }
+    __syncthreads();
+    if (s_last) {
+        // every post is in: the chunk mean from the posts in block order
+        if (tid < D) {
+            const double* src = kpart + tid;
+            double t = 0.0;
+            int b = 0;
+            for (; b + 8 <= a.nblk; b += 8) {
+                double v[8];
+#pragma unroll
+                for (int q = 0; q < 8; ++q) v[q] = src[(int64_t)(b + q) * D];
+#pragma unroll
+                for (int q = 0; q < 8; ++q) t += v[q];
+            }
+            for (; b < a.nblk; ++b) t += src[(int64_t)b * D];
+            const float m = (float)(t / (double)a.N);
+            mu[tid] = m;
+            kmean[tid] = m;
+            __threadfence();                         // the mean reaches L2 before the flag
+        }
+        __syncthreads();
+        if (tid == 0) {
+            __hip_atomic_store(arrive, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(flag, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    } else {
+        if (tid == 0) {
+            uint32_t spins = 0;
+            while (__hip_atomic_load(flag, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
+                if (++spins == kFp8SpinLimit) {
+                    __hip_atomic_store(sync + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(2);
+            }
+        }
+        __syncthreads();
+        if (tid < D) mu[tid] = __hip_atomic_load(kmean + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    if (tid == 0) {
+        const uint32_t left = __hip_atomic_fetch_add(depart, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (left == (uint32_t)a.nblk - 1u) {         // every block has read the mean
+            __hip_atomic_store(flag, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(depart, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+
+    // K: subtract the mean, block absmax, codes, per-token scales
+    float km = 0.f;
+#pragma unroll
+    for (int i = 0; i < ITEMS; ++i) {
+        const int n = n0 + row + ROWS * i;
+        if (n >= a.N) continue;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            kx[i][e] -= (double)mu[ch * 8 + e];
+            km = fmaxf(km, (float)fabs(kx[i][e]));
+        }
+    }
+    km = block_absmax(km, red);
+    const float ks = km > 0.f ? km / 448.f : 1.f;
+    const double kr = 1.0 / (double)ks;
+#pragma unroll
+    for (int i = 0; i < ITEMS; ++i) {
+        const int tk = row + ROWS * i;
+        if (n0 + tk >= a.N) continue;
+        const int v16 = ch >> 1;                     // 16-byte vector of this 8-channel group
+        *reinterpret_cast<uint2*>(&kcodes[(tk * C16 + (v16 ^ (tk % C16))) * 16 + (ch & 1) * 8]) =
+            quant8(kx[i], (double)ks, kr);
+    }
+    __syncthreads();
+    // K code pages: one 16-byte vector (16 channels of one token) per thread, tokens fastest
+    for (int j = tid; j < C16 * kTokTile; j += 256) {
+        const int v16 = j / kTokTile, tk = j - v16 * kTokTile;
+        const int n = n0 + tk;
+        if (n >= a.N) continue;
+        const int pg = n / a.pt, tok = n - pg * a.pt;
+        const int phys = a.table[p * a.ppc + pg];
+        const int64_t base = ((int64_t)phys * a.heads + head) * a.pt * D;
+        st16(static_cast<uint8_t*>(a.kpage) + k8_byte(base, a.pt, tok, v16 * 16),
+             *reinterpret_cast<const uint4*>(&kcodes[(tk * C16 + (v16 ^ (tk % C16))) * 16]));
+    }
+    if (tid < kTokTile && n0 + tid < a.N) {
+        const int n = n0 + tid;
+        const int pg = n / a.pt, tok = n - pg * a.pt;
+        const int phys = a.table[p * a.ppc + pg];
+        a.kscale[((int64_t)phys * a.heads + head) * a.pt + tok] = ks;
     }
 }
 
@@ -529,23 +619,37 @@ hipError_t launch_page_table(int32_t* table, int T, int A, int ppc, int64_t ring
 
 template <int D, bool IN_FP32>
 hipError_t launch_publish_t(const PublishArgs& a, bool fp8, hipStream_t st) {
-    const dim3 grid((a.N + kTokTile - 1) / kTokTile, a.heads, a.nslots);
-    const size_t tbytes = (size_t)frames_per_tile(a.frame_h * a.frame_w) * 32 * sizeof(float2);
+    const size_t tbytes = (size_t)frames_per_tile(a.frame_h * a.frame_w) * 32 * sizeof(double2);
     if (!fp8) {
         const dim3 gb((a.N + kTokB - 1) / kTokB, a.heads, a.nslots);
         hipLaunchKernelGGL((publish_bf16_kernel<D, IN_FP32>), gb, dim3(256), tbytes, st, a);
         return hipGetLastError();
     }
-    hipLaunchKernelGGL((kmean_partial_kernel<D, IN_FP32>), grid, dim3(256), tbytes, st, a);
-    hipLaunchKernelGGL((kmean_reduce_kernel<D>), dim3(a.heads, a.nslots), dim3(D), 0, st, a);
-    hipLaunchKernelGGL((publish_fp8_kernel<D, IN_FP32>), grid, dim3(256), tbytes, st, a);
+    const unsigned nb = (unsigned)(a.nslots * a.heads * ((a.N + kTokTile - 1) / kTokTile));
+    hipLaunchKernelGGL((publish_fp8_kernel<D, IN_FP32>), dim3(nb), dim3(256), tbytes, st, a);
     return hipGetLastError();
+}
+
+template <int D, bool IN_FP32>
+int fp8_blocks_per_cu_t(int hw) {
+    int n = 0;
+    const size_t tbytes = (size_t)frames_per_tile(hw) * 32 * sizeof(double2);
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, publish_fp8_kernel<D, IN_FP32>, 256, tbytes) !=
+        hipSuccess)
+        return 0;
+    return n;
 }
 
 hipError_t launch_publish(const PublishArgs& a, bool fp8, hipStream_t st) {
     if (a.D == 128) return a.in_fp32 ? launch_publish_t<128, true>(a, fp8, st) : launch_publish_t<128, false>(a, fp8, st);
     if (a.D == 64) return a.in_fp32 ? launch_publish_t<64, true>(a, fp8, st) : launch_publish_t<64, false>(a, fp8, st);
     return hipErrorInvalidValue;
+}
+
+int fp8_publish_blocks_per_cu(int D, bool in_fp32, int frame_hw) {
+    if (D == 128) return in_fp32 ? fp8_blocks_per_cu_t<128, true>(frame_hw) : fp8_blocks_per_cu_t<128, false>(frame_hw);
+    if (D == 64) return in_fp32 ? fp8_blocks_per_cu_t<64, true>(frame_hw) : fp8_blocks_per_cu_t<64, false>(frame_hw);
+    return 0;
 }
 
 }  // namespace wf
