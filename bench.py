@@ -214,6 +214,7 @@ def main():
     # one GPU's share of the round: the noisiest slot alone (it reads the
     # whole context, the critical consumer of the round), K launches
     cev = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+    pool.publish(0, 0, w.S + 1, qd, kd, vd, stride, q_out=q, q_scales=qs, stream=stream)   # this round's slots
     torch.cuda.synchronize()
     cev[0].record(stream)
     for i in range(K):

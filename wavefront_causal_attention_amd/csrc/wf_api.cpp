@@ -24,7 +24,6 @@ struct Layout {
     size_t k_off = 0, v_off = 0;           // region offsets
     size_t scale_off = 0, mean_off = 0, part_off = 0;        // fp8 metadata and publish scratch
     size_t scale_layer = 0, mean_layer = 0, part_layer = 0;
-    size_t sync_layer = 0;                 // fp8 publish sync words at the start of each part region
     size_t htab_off = 0, wtab_off = 0, omega_off = 0;
     size_t htab64_off = 0, wtab64_off = 0; // fp64 (cos, sin) row / column tables of the publish
     size_t ring_off = 0;                   // device round counter (int64): advances since creation
@@ -231,12 +230,11 @@ int validate(const wf_config* c, Layout* L) {
     L->v_off = off;  off += L->v_layer * c->num_layers;
     if (fp8) {
         // K scale per token (its 64-token block's scale, replicated), K mean
-        // per (group, head), and the publish's scratch: sync words, then the
-        // fp64 sums of RoPE'd K per (published slot, head, 64-token block)
+        // per (group, head), and the publish's scratch: the fp64 sums of
+        // RoPE'd K per (published slot, head, 64-token block)
         L->scale_layer = align_up(pages * c->heads * c->page_tokens * 4, 256);
         L->mean_layer = align_up((size_t)T * c->heads * c->head_dim * 4, 256);
-        L->sync_layer = align_up(wf::fp8_sync_words(T, c->heads) * 4, 256);
-        L->part_layer = L->sync_layer + align_up((size_t)T * c->heads * L->nblk * c->head_dim * 8, 256);
+        L->part_layer = align_up((size_t)T * c->heads * L->nblk * c->head_dim * 8, 256);
         if (L->scale_layer >= (1ull << 31)) return WF_E_SHAPE;
         L->scale_off = off;  off += L->scale_layer * c->num_layers;
         L->mean_off = off;   off += L->mean_layer * c->num_layers;
@@ -414,20 +412,6 @@ int wf_pool_create(const wf_config* cfg, void* pool_dev, size_t pool_bytes,
     for (size_t i = 0; i < htab64.size(); ++i) htab[i] = (float)htab64[i];
     for (size_t i = 0; i < wtab64.size(); ++i) wtab[i] = (float)wtab64[i];
 
-    // fp8: the blocks of one chunk wait for each other inside the publish, so
-    // one chunk's blocks must fit on the GPU at once, with room to spare
-    if (cfg->qk_dtype == WF_DTYPE_FP8_E4M3) {
-        int dev = 0, ncu = 0;
-        hipError_t q = hipGetDevice(&dev);
-        if (q == hipSuccess) q = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
-        const int per_cu = wf::fp8_publish_blocks_per_cu(cfg->head_dim, cfg->in_dtype == WF_DTYPE_FP32,
-                                                         cfg->frame_h * cfg->frame_w);
-        if (q != hipSuccess || per_cu < 1 || (int64_t)L.nblk * 2 > (int64_t)ncu * per_cu) {
-            delete h;
-            return q != hipSuccess ? WF_E_HIP : WF_E_SHAPE;
-        }
-    }
-
     hipError_t e = hipMemcpy(h->pool + L.htab_off, htab.data(), htab.size() * 4, hipMemcpyHostToDevice);
     if (e == hipSuccess)
         e = hipMemcpy(h->pool + L.wtab_off, wtab.data(), wtab.size() * 4, hipMemcpyHostToDevice);
@@ -435,9 +419,7 @@ int wf_pool_create(const wf_config* cfg, void* pool_dev, size_t pool_bytes,
         e = hipMemcpy(h->pool + L.htab64_off, htab64.data(), htab64.size() * 8, hipMemcpyHostToDevice);
     if (e == hipSuccess)
         e = hipMemcpy(h->pool + L.wtab64_off, wtab64.data(), wtab64.size() * 8, hipMemcpyHostToDevice);
-    // the fp8 publish's sync words start at zero and every launch leaves them so
-    for (int l = 0; e == hipSuccess && L.sync_layer && l < cfg->num_layers; ++l)
-        e = hipMemset(h->pool + L.part_off + L.part_layer * l, 0, L.sync_layer);
+
     if (e == hipSuccess)
         e = hipMemcpy(h->pool + L.omega_off, om.data(), om.size() * 8, hipMemcpyHostToDevice);
     const int64_t ring0 = 0;
@@ -525,8 +507,7 @@ int wf_kv_publish(wf_handle* h, int32_t layer, int32_t slot_first, int32_t nslot
         a.vpage = (uint16_t*)(h->pool + L.v_off + L.v_layer * layer);
         a.kscale = fp8 ? (float*)(h->pool + L.scale_off + L.scale_layer * layer) : nullptr;
         a.kmean = fp8 ? (float*)(h->pool + L.mean_off + L.mean_layer * layer) : nullptr;
-        a.fsync = fp8 ? (uint32_t*)(h->pool + L.part_off + L.part_layer * layer) : nullptr;
-        a.kpart = fp8 ? (double*)(h->pool + L.part_off + L.part_layer * layer + L.sync_layer) : nullptr;
+        a.kpart = fp8 ? (double*)(h->pool + L.part_off + L.part_layer * layer) : nullptr;
         a.table = h->table;
         a.htab = (const double2*)(h->pool + L.htab64_off);
         a.wtab = (const double2*)(h->pool + L.wtab64_off);

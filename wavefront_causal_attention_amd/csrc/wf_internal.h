@@ -62,7 +62,6 @@ struct PublishArgs {
     uint16_t* vpage;          // this layer's V pages (format above)
     float* kscale;            // fp8: per-token K scale [phys][head][pt]
     float* kmean;             // fp8: [group][head][D]
-    uint32_t* fsync;          // fp8 scratch: ticket, error word, 3 words per (published slot, head)
     double* kpart;            // fp8 scratch: [published slot][head][nblk][D] block sums of RoPE'd K
     const int32_t* table;     // page table [T][ppc]
     const double2* htab;      // RoPE row-axis (cos, sin) [frame_h][dh/2], fp64
@@ -161,11 +160,7 @@ hipError_t launch_quant_rows(const uint16_t* x, int64_t rows, int cols, int64_t 
 hipError_t launch_page_table(int32_t* table, int T, int A, int ppc, int64_t ring, int64_t* ring_dev, int store_pos,
                              int store_anchor, hipStream_t st);
 hipError_t launch_publish(const PublishArgs& a, bool fp8, hipStream_t st);
-// fp8 publish scratch words per layer for T positions and `heads` heads
-inline size_t fp8_sync_words(int T, int heads) { return 2 + 3 * (size_t)T * heads; }
-// resident fp8 publish blocks per CU (0 if the runtime cannot tell): the
-// blocks of one chunk wait for each other, so they must fit on the GPU at once
-int fp8_publish_blocks_per_cu(int D, bool in_fp32, int frame_hw);
+
 hipError_t launch_attention(const AttnArgs& a, bool fp8, hipStream_t st);
 
 }  // namespace wf

@@ -127,23 +127,34 @@ __device__ __forceinline__ void rope8(const float* x, double* y, int c0, const d
     }
 }
 
-// fp64 -> fp32 rounding to odd: truncate toward zero and set the last bit if
-// inexact. A round-to-nearest-even of the result into a format at least two
-// significand bits narrower than fp32 (bf16: 8 bits, e4m3: 4) then equals the
-// round-to-nearest-even of the fp64 value itself, with no double rounding.
-// NaN stays NaN; beyond the fp32 range the result is the largest finite value.
-__device__ __forceinline__ float to_f32_odd(double x) {
-    const float y = (float)x;
+// Rounding an fp64 value once into bf16 (or e4m3) through fp32: the fp32
+// nearest value y can only mislead the narrow format's nearest-even rounding
+// when y lands exactly on one of that format's rounding midpoints while x does
+// not (double rounding). Such y (bf16: low 16 bits 0x8000) are rare, about
+// one value in 2^16; only they are moved one fp32 step toward x, off the
+// midpoint, so the narrow rounding goes to x's side. An exact tie stays on the
+// midpoint and is rounded to even, as the fp64 value would be.
+__device__ __forceinline__ float off_midpoint(float y, double x) {
     const double yd = (double)y;
-    uint32_t b = __float_as_uint(y);
-    const uint32_t toward_zero = fabs(yd) > fabs(x) ? 1u : 0u;
-    b = yd != x ? ((b - toward_zero) | 1u) : b;
-    return __uint_as_float(b);
+    const uint32_t b = __float_as_uint(y);          // sign-magnitude: +1 moves away from zero
+    return fabs(yd) < fabs(x) ? __uint_as_float(b + 1u) : (fabs(yd) > fabs(x) ? __uint_as_float(b - 1u) : y);
 }
 
 __device__ __forceinline__ uint4 pack8_f64(const double* y) {
-    return make_uint4(pack_bf16x2(to_f32_odd(y[0]), to_f32_odd(y[1])), pack_bf16x2(to_f32_odd(y[2]), to_f32_odd(y[3])),
-                      pack_bf16x2(to_f32_odd(y[4]), to_f32_odd(y[5])), pack_bf16x2(to_f32_odd(y[6]), to_f32_odd(y[7])));
+    float f[8];
+    bool mid = false;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        f[e] = (float)y[e];
+        mid |= (__float_as_uint(f[e]) & 0xFFFFu) == 0x8000u;
+    }
+    if (mid) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            if ((__float_as_uint(f[e]) & 0xFFFFu) == 0x8000u) f[e] = off_midpoint(f[e], y[e]);
+    }
+    return make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]),
+                      pack_bf16x2(f[6], f[7]));
 }
 
 // fp64 time-axis (cos, sin) of the frames f_lo .. f_lo + nf - 1 of published
@@ -276,38 +287,19 @@ __global__ __launch_bounds__(256) void publish_bf16_kernel(PublishArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// fp8 e4m3 publish, one launch. Q and K are quantised per 64-token block of
-// their chunk (blocks restart at each chunk start, so a publish block is
-// exactly one quantisation block): scale = fp32 absmax / 448 (IEEE divide, 1
-// for an all-zero block), code = round-to-nearest-even of value / scale,
-// saturating at +-448, every decision taken on the fp64 value. K first has its
-// chunk's per-channel mean removed, the mean rounded to fp32; attention adds
-// it back exactly as q . mean. V stays bf16.
+// fp8 e4m3 publish. Q and K are quantised per 64-token block of their chunk
+// (blocks restart at each chunk start, so a publish block is exactly one
+// quantisation block): scale = fp32 absmax / 448 (IEEE divide, 1 for an
+// all-zero block), code = round-to-nearest-even of value / scale, saturating
+// at +-448, every decision taken on the fp64 value. K first has its chunk's
+// per-channel mean removed, the mean rounded to fp32; attention adds it back
+// exactly as q . mean. V stays bf16.
 //
-// The K codes need the mean of the whole chunk, so the blocks of one (slot,
-// head) chunk meet once: each block posts the fp64 sum of its RoPE'd K rows,
-// and the chunk's last block to post sums the posts in block order, stores
-// the mean and raises the chunk's flag, which the other blocks wait for. A
-// block writes its Q codes and V pages before it waits and keeps its RoPE'd K
-// in registers across the wait, so Q, K and V are read from HBM once.
-//
-// Blocks take their unit (slot, head, block) from a ticket counter in the
-// order they start, a chunk's blocks consecutively, so every ticket below a
-// waiting block's belongs to a block that has started. Every chunk whose
-// tickets all lie below the highest ticket issued so far has all its posts
-// in, so its blocks finish and make room; only the chunk holding that ticket
-// can wait, and its blocks fit on the GPU together as long as one chunk has
-// no more blocks than the GPU holds at once (checked on the host when the
-// pool is created). The wait is bounded all the same: after kFp8SpinLimit
-// polls a block gives up, raises the error word and proceeds.
-//
-// Scratch (per layer): sync words [0] ticket, [1] error, then per (published
-// slot, head) unit u: [2 + 3u] arrivals, [3 + 3u] flag, [4 + 3u] departures,
-// all zero between launches (the last ticket resets the ticket counter, the
-// last arrival the arrivals, the last departure the flag and departures);
-// then the partial sums kpart[unit][block][D] in fp64.
-
-constexpr uint32_t kFp8SpinLimit = 1u << 22;
+// Three launches with fixed summation orders: kmean_partial_kernel writes the
+// fp64 column sums of each 64-token block of RoPE'd K into scratch
+// (kpart[published slot][head][block][D]), kmean_reduce_kernel adds a chunk's
+// block sums in block order into its fp32 mean, and publish_fp8_kernel
+// quantises and publishes Q, K and V.
 
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
@@ -327,17 +319,46 @@ __device__ __forceinline__ uint32_t fp8x4(float a, float b, float c, float d) {
     return lo | (hi << 16);
 }
 
+// An fp32 value on an e4m3 rounding midpoint, or in e4m3's subnormal range
+// (below 2^-6), where the midpoints are the odd multiples of 2^-10: the two
+// cases in which rounding x to fp32 first could change its e4m3 rounding.
+__device__ __forceinline__ bool e4m3_suspect(float y) {
+    const uint32_t b = __float_as_uint(y);
+    return (b & 0xFFFFFu) == 0x80000u || fabsf(y) < 0.015625f;
+}
+
 // x / scale to nearest even e4m3 for 8 values: the quotient in fp64 from the
 // reciprocal r = 1/scale (correctly rounded) and one remainder correction
-// (q0 = x r, e = x - q0 scale exactly by fma, q = q0 + e r), then rounded
-// to odd into fp32, which the hardware's nearest-even conversion keeps exact.
+// (q0 = x r, e = x - q0 scale exactly by fma, q = q0 + e r), rounded to fp32;
+// a value that lands on an e4m3 midpoint or in the subnormal range is moved
+// off the midpoint toward the fp64 quotient (see off_midpoint), the exact
+// e4m3 rounding of a subnormal-range value being taken on fp32 values within
+// one step of 2^-30 of it.
 __device__ __forceinline__ uint2 quant8(const double* x, double sc, double r) {
     float q[8];
+    double qd[8];
+    bool sus = false;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
         const double q0 = x[e] * r;
         const double rem = fma(-q0, sc, x[e]);
-        q[e] = to_f32_odd(fma(rem, r, q0));
+        qd[e] = fma(rem, r, q0);
+        q[e] = (float)qd[e];
+        sus |= e4m3_suspect(q[e]);
+    }
+    if (sus) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            if (!e4m3_suspect(q[e])) continue;
+            if (fabsf(q[e]) < 0.015625f) {
+                // subnormal range: the nearest-even multiple of 2^-9, computed
+                // exactly in fp64 (the value is far inside fp64's range)
+                const double m = rint(qd[e] * 512.0);
+                q[e] = (float)(m * (1.0 / 512.0));
+            } else {
+                q[e] = off_midpoint(q[e], qd[e]);
+            }
+        }
     }
     return make_uint2(fp8x4(q[0], q[1], q[2], q[3]), fp8x4(q[4], q[5], q[6], q[7]));
 }
@@ -353,8 +374,78 @@ __device__ __forceinline__ float block_absmax(float v, float* red) {
     return m;
 }
 
-// grid: nslots * heads * ceil(N/64) blocks of 256 threads; one block per
-// (slot, head, 64-token block), assigned by ticket.
+// grid (ceil(N/64), heads, nslots), 256 threads: the fp64 column sums of one
+// 64-token block of RoPE'd K -> kpart[published slot][head][block][D].
+template <int D, bool IN_FP32>
+__global__ __launch_bounds__(256) void kmean_partial_kernel(PublishArgs a) {
+    constexpr int CPR = D / 8;                       // 8-channel vectors per token row
+    constexpr int ROWS = 256 / CPR;                  // token rows a pass of the block covers
+    constexpr int IT = kTokTile / ROWS;
+    double2 (*ttab)[32] = reinterpret_cast<double2 (*)[32]>(g_ttab_dyn);
+    __shared__ double part[ROWS][D];
+    const int tid = threadIdx.x;
+    const int sr = blockIdx.z, head = blockIdx.y, blk = blockIdx.x;
+    const int n0 = blk * kTokTile;
+    const int HW = a.frame_h * a.frame_w;
+    const int f_lo = n0 / HW;
+    const int nf = (min(n0 + kTokTile, a.N) - 1) / HW - f_lo + 1;
+    const int ch = tid % CPR, row = tid / CPR;
+    // rows of this thread, loaded before the time table is built (rows past
+    // the chunk are clamped to its last row and not summed)
+    Raw8<IN_FP32> kin[IT];
+#pragma unroll
+    for (int i = 0; i < IT; ++i) {
+        const int n = min(n0 + row + ROWS * i, a.N - 1);
+        kin[i].load(a.k, ((int64_t)sr * a.N + n) * a.row_stride + (int64_t)head * D + ch * 8);
+    }
+    fill_ttab(ttab, a, sr, f_lo, nf);
+    __syncthreads();
+    double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+    for (int i = 0; i < IT; ++i) {
+        const int n = n0 + row + ROWS * i;
+        if (n >= a.N) break;
+        const int y = (n / a.frame_w) % a.frame_h, xw = n % a.frame_w;
+        float x[8];
+        double r[8];
+        kin[i].unpack(x);
+        rope8(x, r, ch * 8, ttab[n / HW - f_lo], a.htab + y * (a.dh >> 1), a.wtab + xw * (a.dw >> 1), a.dt, a.dh);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] += r[e];
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) part[row][ch * 8 + e] = acc[e];
+    __syncthreads();
+    if (tid < D) {
+        double t = 0.0;
+        for (int r = 0; r < ROWS; ++r) t += part[r][tid];
+        a.kpart[(((int64_t)sr * a.heads + head) * a.nblk + blk) * D + tid] = t;
+    }
+}
+
+// grid (heads, nslots), block D: kmean[group][head][d] = the chunk's block sums
+// added in block order, / N, rounded to fp32.
+template <int D>
+__global__ void kmean_reduce_kernel(PublishArgs a) {
+    const int sr = blockIdx.y, s = a.slot_first + sr, head = blockIdx.x, d = threadIdx.x;
+    const int g = a.table[(a.T - 1 - s) * a.ppc] / a.ppc;
+    const double* src = a.kpart + ((int64_t)sr * a.heads + head) * a.nblk * D + d;
+    // eight loads in flight per iteration, summed in block order
+    double sum = 0.0;
+    int b = 0;
+    for (; b + 8 <= a.nblk; b += 8) {
+        double v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = src[(int64_t)(b + u) * D];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) sum += v[u];
+    }
+    for (; b < a.nblk; ++b) sum += src[(int64_t)b * D];
+    a.kmean[((int64_t)g * a.heads + head) * D + d] = (float)(sum / (double)a.N);
+}
+
+// grid (ceil(N/64), heads, nslots), 256 threads: quantise and publish one
+// 64-token block.
 template <int D, bool IN_FP32>
 __global__ __launch_bounds__(256) void publish_fp8_kernel(PublishArgs a) {
     constexpr int CPR = D / 8;                       // 8-channel vectors per token row
@@ -362,28 +453,14 @@ __global__ __launch_bounds__(256) void publish_fp8_kernel(PublishArgs a) {
     constexpr int ROWS = 256 / CPR;                  // token rows a pass of the block covers
     constexpr int C16 = D / 16;                      // 16-byte code vectors per token row
     double2 (*ttab)[32] = reinterpret_cast<double2 (*)[32]>(g_ttab_dyn);
-    __shared__ double part[ROWS][D];
     __shared__ float mu[D];
     __shared__ float red[4];
-    __shared__ int s_unit, s_last;
     __shared__ __align__(16) uint8_t kcodes[kTokTile * D];   // [tok][16-byte vector ^ (tok % C16)]
     __shared__ __align__(16) uint16_t vst[kTokTile * D];     // V rows, [tok][d]
 
     const int tid = threadIdx.x;
-    const int nunit = a.nslots * a.heads;
-    uint32_t* const sync = a.fsync;
-    if (tid == 0) {
-        const uint32_t t = __hip_atomic_fetch_add(sync, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (t == (uint32_t)(nunit * a.nblk) - 1u)     // the last ticket: every block has one
-            __hip_atomic_store(sync, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        s_unit = (int)t;
-    }
-    __syncthreads();
-    const int ticket = s_unit;
-    const int blk = ticket % a.nblk;
-    const int u = ticket / a.nblk;                   // (published slot, head) unit
-    const int head = u % a.heads, sr = u / a.heads;
-    const int s = a.slot_first + sr, n0 = blk * kTokTile;
+    const int sr = blockIdx.z, s = a.slot_first + sr, head = blockIdx.y, blk = blockIdx.x;
+    const int n0 = blk * kTokTile;
     const int p = a.T - 1 - s;
     const int HW = a.frame_h * a.frame_w;
     const int f_lo = n0 / HW;
@@ -403,30 +480,25 @@ __global__ __launch_bounds__(256) void publish_fp8_kernel(PublishArgs a) {
         if (a.q) qin[i].load(a.q, e0);
     }
     fill_ttab(ttab, a, sr, f_lo, nf);
+    const int g = a.table[p * a.ppc] / a.ppc;
+    if (tid < D) mu[tid] = a.kmean[((int64_t)g * a.heads + head) * D + tid];
     __syncthreads();
-
-    // K rotated in fp64 (kept for after the mean), its column sums; V staged
-    double kx[ITEMS][8];
-    double ksum[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-#pragma unroll
-    for (int i = 0; i < ITEMS; ++i) {
-        const int tk = row + ROWS * i, n = n0 + tk;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) kx[i][e] = 0.0;
-        if (n >= a.N) continue;
+    auto rotate = [&](const Raw8<IN_FP32>& in, int n, double* out) {
         const int y = (n / a.frame_w) % a.frame_h, xw = n % a.frame_w;
         float x[8];
-        kin[i].unpack(x);
-        rope8(x, kx[i], ch * 8, ttab[n / HW - f_lo], a.htab + y * (a.dh >> 1), a.wtab + xw * (a.dw >> 1), a.dt,
-              a.dh);
+        in.unpack(x);
+        rope8(x, out, ch * 8, ttab[n / HW - f_lo], a.htab + y * (a.dh >> 1), a.wtab + xw * (a.dw >> 1), a.dt, a.dh);
+    };
+
+    // V staged for the page stores
 #pragma unroll
-        for (int e = 0; e < 8; ++e) ksum[e] += kx[i][e];
+    for (int i = 0; i < ITEMS; ++i) {
+        const int tk = row + ROWS * i;
+        if (n0 + tk >= a.N) continue;
+        float x[8];
         vin[i].unpack(x);
         *reinterpret_cast<uint4*>(&vst[tk * D + ch * 8]) = pack8(x);
     }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) part[row][ch * 8 + e] = ksum[e];
-
     // Q: rotate, block absmax, codes, scale (no mean)
     if (a.q) {
         double qx[ITEMS][8];
@@ -437,11 +509,7 @@ __global__ __launch_bounds__(256) void publish_fp8_kernel(PublishArgs a) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) qx[i][e] = 0.0;
             if (n >= a.N) continue;
-            const int y = (n / a.frame_w) % a.frame_h, xw = n % a.frame_w;
-            float x[8];
-            qin[i].unpack(x);
-            rope8(x, qx[i], ch * 8, ttab[n / HW - f_lo], a.htab + y * (a.dh >> 1), a.wtab + xw * (a.dw >> 1), a.dt,
-                  a.dh);
+            rotate(qin[i], n, qx[i]);
 #pragma unroll
             for (int e = 0; e < 8; ++e) qm = fmaxf(qm, (float)fabs(qx[i][e]));
         }
@@ -457,95 +525,16 @@ __global__ __launch_bounds__(256) void publish_fp8_kernel(PublishArgs a) {
         }
         if (tid == 0) a.q_scales[((int64_t)s * a.heads + head) * a.nblk + blk] = qs;
     }
-    __syncthreads();
-
-    // V pages as in the bf16 publish (independent of the mean)
-    for (int j = tid; j < (kTokTile / 8) * D; j += 256) {
-        const int kc = j / D, d = j - kc * D;
-        const int n = n0 + kc * 8;
-        if (n >= a.N) continue;
-        uint32_t w[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-            w[r] = (uint32_t)vst[(kc * 8 + 2 * r) * D + d] | ((uint32_t)vst[(kc * 8 + 2 * r + 1) * D + d] << 16);
-        const int pg = n / a.pt, tok = n - pg * a.pt;
-        const int phys = a.table[p * a.ppc + pg];
-        const int64_t base = ((int64_t)phys * a.heads + head) * a.pt * D;
-        st16(a.vpage + v_elem(base, D, tok, d), make_uint4(w[0], w[1], w[2], w[3]));
-    }
-
-    // post this block's column sums of K (rows summed in a fixed order)
-    double* const kpart = a.kpart + (int64_t)u * a.nblk * D;
-    if (tid < D) {
-        double t = 0.0;
-        for (int r = 0; r < ROWS; ++r) t += part[r][tid];
-        kpart[(int64_t)blk * D + tid] = t;
-        __threadfence();                             // the post reaches L2 before the arrival count
-    }
-    uint32_t* const arrive = sync + 2 + 3 * u;
-    uint32_t* const flag = arrive + 1;
-    uint32_t* const depart = arrive + 2;
-    const int g = a.table[p * a.ppc] / a.ppc;
-    float* const kmean = a.kmean + ((int64_t)g * a.heads + head) * D;
-    __syncthreads();
-    if (tid == 0) {
-        const uint32_t before = __hip_atomic_fetch_add(arrive, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-        s_last = before == (uint32_t)a.nblk - 1u;
-    }
-    __syncthreads();
-    if (s_last) {
-        // every post is in: the chunk mean from the posts in block order
-        if (tid < D) {
-            const double* src = kpart + tid;
-            double t = 0.0;
-            int b = 0;
-            for (; b + 8 <= a.nblk; b += 8) {
-                double v[8];
-#pragma unroll
-                for (int q = 0; q < 8; ++q) v[q] = src[(int64_t)(b + q) * D];
-#pragma unroll
-                for (int q = 0; q < 8; ++q) t += v[q];
-            }
-            for (; b < a.nblk; ++b) t += src[(int64_t)b * D];
-            const float m = (float)(t / (double)a.N);
-            mu[tid] = m;
-            kmean[tid] = m;
-            __threadfence();                         // the mean reaches L2 before the flag
-        }
-        __syncthreads();
-        if (tid == 0) {
-            __hip_atomic_store(arrive, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(flag, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-        }
-    } else {
-        if (tid == 0) {
-            uint32_t spins = 0;
-            while (__hip_atomic_load(flag, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
-                if (++spins == kFp8SpinLimit) {
-                    __hip_atomic_store(sync + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    break;
-                }
-                __builtin_amdgcn_s_sleep(2);
-            }
-        }
-        __syncthreads();
-        if (tid < D) mu[tid] = __hip_atomic_load(kmean + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    __syncthreads();
-    if (tid == 0) {
-        const uint32_t left = __hip_atomic_fetch_add(depart, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (left == (uint32_t)a.nblk - 1u) {         // every block has read the mean
-            __hip_atomic_store(flag, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(depart, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-    }
-
-    // K: subtract the mean, block absmax, codes, per-token scales
+    // K: rotate, subtract the mean, block absmax, codes, per-token scales
+    double kx[ITEMS][8];
     float km = 0.f;
 #pragma unroll
     for (int i = 0; i < ITEMS; ++i) {
         const int n = n0 + row + ROWS * i;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) kx[i][e] = 0.0;
         if (n >= a.N) continue;
+        rotate(kin[i], n, kx[i]);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             kx[i][e] -= (double)mu[ch * 8 + e];
@@ -580,6 +569,20 @@ __global__ __launch_bounds__(256) void publish_fp8_kernel(PublishArgs a) {
         const int pg = n / a.pt, tok = n - pg * a.pt;
         const int phys = a.table[p * a.ppc + pg];
         a.kscale[((int64_t)phys * a.heads + head) * a.pt + tok] = ks;
+    }
+    // V pages as in the bf16 publish
+    for (int j = tid; j < (kTokTile / 8) * D; j += 256) {
+        const int kc = j / D, d = j - kc * D;
+        const int n = n0 + kc * 8;
+        if (n >= a.N) continue;
+        uint32_t w[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            w[r] = (uint32_t)vst[(kc * 8 + 2 * r) * D + d] | ((uint32_t)vst[(kc * 8 + 2 * r + 1) * D + d] << 16);
+        const int pg = n / a.pt, tok = n - pg * a.pt;
+        const int phys = a.table[p * a.ppc + pg];
+        const int64_t base = ((int64_t)phys * a.heads + head) * a.pt * D;
+        st16(a.vpage + v_elem(base, D, tok, d), make_uint4(w[0], w[1], w[2], w[3]));
     }
 }
 
@@ -625,19 +628,11 @@ hipError_t launch_publish_t(const PublishArgs& a, bool fp8, hipStream_t st) {
         hipLaunchKernelGGL((publish_bf16_kernel<D, IN_FP32>), gb, dim3(256), tbytes, st, a);
         return hipGetLastError();
     }
-    const unsigned nb = (unsigned)(a.nslots * a.heads * ((a.N + kTokTile - 1) / kTokTile));
-    hipLaunchKernelGGL((publish_fp8_kernel<D, IN_FP32>), dim3(nb), dim3(256), tbytes, st, a);
+    const dim3 grid((a.N + kTokTile - 1) / kTokTile, a.heads, a.nslots);
+    hipLaunchKernelGGL((kmean_partial_kernel<D, IN_FP32>), grid, dim3(256), tbytes, st, a);
+    hipLaunchKernelGGL((kmean_reduce_kernel<D>), dim3(a.heads, a.nslots), dim3(D), 0, st, a);
+    hipLaunchKernelGGL((publish_fp8_kernel<D, IN_FP32>), grid, dim3(256), tbytes, st, a);
     return hipGetLastError();
-}
-
-template <int D, bool IN_FP32>
-int fp8_blocks_per_cu_t(int hw) {
-    int n = 0;
-    const size_t tbytes = (size_t)frames_per_tile(hw) * 32 * sizeof(double2);
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, publish_fp8_kernel<D, IN_FP32>, 256, tbytes) !=
-        hipSuccess)
-        return 0;
-    return n;
 }
 
 hipError_t launch_publish(const PublishArgs& a, bool fp8, hipStream_t st) {
@@ -646,10 +641,5 @@ hipError_t launch_publish(const PublishArgs& a, bool fp8, hipStream_t st) {
     return hipErrorInvalidValue;
 }
 
-int fp8_publish_blocks_per_cu(int D, bool in_fp32, int frame_hw) {
-    if (D == 128) return in_fp32 ? fp8_blocks_per_cu_t<128, true>(frame_hw) : fp8_blocks_per_cu_t<128, false>(frame_hw);
-    if (D == 64) return in_fp32 ? fp8_blocks_per_cu_t<64, true>(frame_hw) : fp8_blocks_per_cu_t<64, false>(frame_hw);
-    return 0;
-}
 
 }  // namespace wf
