@@ -161,6 +161,22 @@ int wf_kv_publish(wf_handle* h, int32_t layer, int32_t slot_first, int32_t nslot
                   const int32_t* chunk_t0_host, void* q_out, float* q_scales, void* stream);
 
 /*
+ * wf_kv_publish for callers that cannot allocate device memory or must not
+ * call hipMalloc (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid it). Same arguments, checks and results as wf_kv_publish,
+ * bit for bit; it allocates nothing. The scratch the fp8 publish needs (fp64
+ * sums of RoPE'd K per 64-token block: nslots * heads * ceil(N/64) *
+ * head_dim * 8 bytes) comes from one static device array of 16 MiB per GPU,
+ * held until the process ends, instead of the pool's scratch region; larger
+ * needs return WF_E_SHAPE and launch nothing (bf16 pools need none). Every
+ * call on one GPU shares that GPU's array, so calls that may overlap on one
+ * GPU (other streams, other threads, other pools) race: order them.
+ */
+int wf_kv_publish_noalloc(wf_handle* h, int32_t layer, int32_t slot_first, int32_t nslots,
+                          const void* q, const void* k, const void* v, int64_t row_stride_elems,
+                          const int32_t* chunk_t0_host, void* q_out, float* q_scales, void* stream);
+
+/*
  * QKV projection with RoPE + publish as its epilogue (hyper.ai summary,
  * "Method": WaveRT publishes K/V right after the QKV projection and RoPE;
  * thelatestinai.com listing, Table 11: the projection maps the hidden state,

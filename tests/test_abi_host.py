@@ -216,6 +216,40 @@ def test_publish_invalid_args(lib, args):
         wf.wf_pool_destroy(h)
 
 
+@pytest.mark.parametrize("noalloc", [False, True])
+def test_publish_noalloc_checks_like_publish_and_bounds_its_scratch(lib, noalloc):
+    """wf_kv_publish_noalloc takes wf_kv_publish's arguments and checks; on an
+    fp8 pool whose K-mean block sums (nslots * heads * ceil(N/64) * d * 8
+    bytes) exceed its static 16 MiB array it returns WF_E_SHAPE, launches
+    nothing and marks nothing published; bf16 pools need no scratch."""
+    import dataclasses
+    w = W.WORKLOADS["wan1.3b_s4_fp8"]
+    big = dataclasses.replace(w, heads=48)            # 5 slots x 48 heads x 74 blocks x 1 KiB > 16 MiB
+    h = wf.wf_pool_create_host_model(cfg_of(big))
+    try:
+        args = (h, 0, 0, big.S + 1, FAKE, FAKE, FAKE, 3 * big.hd, None, FAKE, FAKE, None)
+        if noalloc:
+            with pytest.raises(wf.WfError) as e:
+                wf.wf_kv_publish(*args, noalloc=True)
+            assert e.value.status == wf.WF_E_SHAPE and "scratch" in str(e.value)
+            assert wf.wf_ready_mask(h, 0) == 0
+            # a smaller range fits: 2 slots x 48 heads x 74 blocks x 1 KiB
+            wf.wf_kv_publish(h, 0, 0, 2, FAKE, FAKE, FAKE, 3 * big.hd, None, FAKE, FAKE, None, noalloc=True)
+            assert wf.wf_ready_mask(h, 0) == sum(1 << (big.T - 1 - s) for s in range(2))
+        else:
+            wf.wf_kv_publish(*args)
+        with pytest.raises(wf.WfError) as e:           # the shared argument checks
+            wf.wf_kv_publish(h, 1, 0, 1, FAKE, FAKE, FAKE, 3 * big.hd, None, FAKE, FAKE, None, noalloc=noalloc)
+        assert e.value.status == wf.WF_E_INVALID_ARG
+    finally:
+        wf.wf_pool_destroy(h)
+    hb = wf.wf_pool_create_host_model(cfg_of(dataclasses.replace(W.WORKLOADS["wan1.3b_s4"], heads=64)))
+    try:
+        wf.wf_kv_publish(hb, 0, 0, 5, FAKE, FAKE, FAKE, 64 * 128, None, FAKE, None, None, noalloc=noalloc)
+    finally:
+        wf.wf_pool_destroy(hb)
+
+
 @pytest.mark.parametrize("args", [
     dict(layer=2), dict(slot_first=5), dict(nslots=6), dict(q=None), dict(out=None),
     dict(out_dtype=wf.WF_DTYPE_FP8_E4M3), dict(out=FAKE + 8),

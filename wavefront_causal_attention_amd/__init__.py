@@ -87,9 +87,11 @@ class Pool:
         return torch.empty((c.S + 1, self.N, c.heads * c.head_dim), dtype=dt, device=self.pool.device)
 
     def publish(self, layer, slot_first, nslots, q, k, v, row_stride, q_out=None, q_scales=None,
-                chunk_t0=None, stream=None):
+                chunk_t0=None, stream=None, noalloc=False):
+        """noalloc: through wf_kv_publish_noalloc (scratch from the library's
+        static per-GPU array, not the pool)."""
         wf_kv_publish(self.handle, layer, slot_first, nslots, q, k, v, row_stride, chunk_t0,
-                      q_out, q_scales, stream)
+                      q_out, q_scales, stream, noalloc)
 
     def project_publish(self, layer, slot_first, nslots, x, x_row_stride, hidden, w, bias=None, q_out=None,
                         chunk_t0=None, stream=None):

@@ -80,6 +80,7 @@ def load() -> ctypes.CDLL:
         "wf_pool_create_host_model": (ctypes.c_int, [ctypes.POINTER(wf_config), ctypes.POINTER(P)]),
         "wf_pool_destroy": (None, [P]),
         "wf_kv_publish": (ctypes.c_int, [P, I32, I32, I32, P, P, P, I64, P, P, P, P]),
+        "wf_kv_publish_noalloc": (ctypes.c_int, [P, I32, I32, I32, P, P, P, I64, P, P, P, P]),
         "wf_qkv_project_publish": (ctypes.c_int, [P, I32, I32, I32, P, I64, I32, P, P, P, P, P]),
         "wf_qkv_project_publish_w8a8": (ctypes.c_int, [P, I32, I32, I32, P, I64, P, I32, P, P, P, P, P, P]),
         "wf_quantize_rows_fp8": (ctypes.c_int, [P, I64, I32, I64, P, I64, P, P]),
@@ -159,14 +160,16 @@ def wf_pool_destroy(h: int) -> None:
 
 
 def wf_kv_publish(h, layer, slot_first, nslots, q, k, v, row_stride_elems,
-                  chunk_t0=None, q_out=None, q_scales=None, stream=None) -> None:
+                  chunk_t0=None, q_out=None, q_scales=None, stream=None, noalloc=False) -> None:
+    """noalloc: call wf_kv_publish_noalloc (same arguments)."""
     t0 = None
     if chunk_t0 is not None:
         arr = (ctypes.c_int32 * len(chunk_t0))(*[int(x) for x in chunk_t0])
         t0 = ctypes.cast(arr, ctypes.c_void_p)
-    _check(load().wf_kv_publish(h, layer, slot_first, nslots, _ptr(q), _ptr(k), _ptr(v),
-                                int(row_stride_elems), t0, _ptr(q_out), _ptr(q_scales),
-                                _stream(stream)), "wf_kv_publish", h)
+    name = "wf_kv_publish_noalloc" if noalloc else "wf_kv_publish"
+    _check(getattr(load(), name)(h, layer, slot_first, nslots, _ptr(q), _ptr(k), _ptr(v),
+                                 int(row_stride_elems), t0, _ptr(q_out), _ptr(q_scales),
+                                 _stream(stream)), name, h)
 
 
 def wf_qkv_project_publish(h, layer, slot_first, nslots, x, x_row_stride_elems, hidden, w, bias=None,
@@ -259,7 +262,7 @@ def wf_geometry(h):
 
 EXPORTED = [
     "wf_pool_bytes", "wf_pool_create", "wf_pool_create_host_model", "wf_pool_destroy",
-    "wf_kv_publish", "wf_qkv_project_publish", "wf_qkv_project_publish_w8a8", "wf_quantize_rows_fp8",
+    "wf_kv_publish", "wf_kv_publish_noalloc", "wf_qkv_project_publish", "wf_qkv_project_publish_w8a8", "wf_quantize_rows_fp8",
     "wf_attention_round", "wf_round_advance", "wf_round_replayed", "wf_round_index",
     "wf_attention_work_list",
     "wf_schedule_chunk_ids", "wf_page_table_host", "wf_ready_mask", "wf_geometry",

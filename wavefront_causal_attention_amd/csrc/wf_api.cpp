@@ -412,7 +412,10 @@ int wf_pool_create(const wf_config* cfg, void* pool_dev, size_t pool_bytes,
     for (size_t i = 0; i < htab64.size(); ++i) htab[i] = (float)htab64[i];
     for (size_t i = 0; i < wtab64.size(); ++i) wtab[i] = (float)wtab64[i];
 
-    hipError_t e = hipMemcpy(h->pool + L.htab_off, htab.data(), htab.size() * 4, hipMemcpyHostToDevice);
+    // the static scratch of wf_kv_publish_noalloc, looked up once per device
+    void* sptr = nullptr;
+    hipError_t e = wf::static_scratch(&sptr);
+    if (e == hipSuccess) e = hipMemcpy(h->pool + L.htab_off, htab.data(), htab.size() * 4, hipMemcpyHostToDevice);
     if (e == hipSuccess)
         e = hipMemcpy(h->pool + L.wtab_off, wtab.data(), wtab.size() * 4, hipMemcpyHostToDevice);
     if (e == hipSuccess)
@@ -457,9 +460,11 @@ int wf_pool_create(const wf_config* cfg, void* pool_dev, size_t pool_bytes,
 
 void wf_pool_destroy(wf_handle* h) { delete h; }
 
-int wf_kv_publish(wf_handle* h, int32_t layer, int32_t slot_first, int32_t nslots,
-                  const void* q, const void* k, const void* v, int64_t row_stride_elems,
-                  const int32_t* chunk_t0_host, void* q_out, float* q_scales, void* stream) {
+// The publish; static_scratch: the fp8 K-mean block sums go to the library's
+// static per-GPU array instead of the pool's scratch region.
+static int publish(wf_handle* h, int32_t layer, int32_t slot_first, int32_t nslots, const void* q, const void* k,
+                   const void* v, int64_t row_stride_elems, const int32_t* chunk_t0_host, void* q_out,
+                   float* q_scales, void* stream, bool static_scratch) {
     if (!h) return WF_E_INVALID_ARG;
     const wf_config& c = h->cfg;
     const Layout& L = h->L;
@@ -483,6 +488,18 @@ int wf_kv_publish(wf_handle* h, int32_t layer, int32_t slot_first, int32_t nslot
                      (long long)h->round());
             return WF_E_INVALID_ARG;
         }
+    // fp8: K-mean block sums of the published slots, fp64
+    const size_t part_bytes = fp8 ? (size_t)nslots * c.heads * L.nblk * c.head_dim * 8 : 0;
+    if (static_scratch && part_bytes > wf::kStaticScratchBytes) {
+        snprintf(h->err, sizeof h->err, "wf_kv_publish_noalloc: %zu scratch bytes needed, the static array holds %zu",
+                 part_bytes, wf::kStaticScratchBytes);
+        return WF_E_SHAPE;
+    }
+    void* sptr = nullptr;
+    if (static_scratch && fp8 && !h->host_model) {
+        const hipError_t e = wf::static_scratch(&sptr);
+        if (e != hipSuccess) return h->fail_hip(e, "wf_kv_publish_noalloc scratch address");
+    }
     wf::PublishArgs a{};
     for (int i = 0; i < nslots; ++i) {
         const int64_t t0 = chunk_t0_host
@@ -507,7 +524,8 @@ int wf_kv_publish(wf_handle* h, int32_t layer, int32_t slot_first, int32_t nslot
         a.vpage = (uint16_t*)(h->pool + L.v_off + L.v_layer * layer);
         a.kscale = fp8 ? (float*)(h->pool + L.scale_off + L.scale_layer * layer) : nullptr;
         a.kmean = fp8 ? (float*)(h->pool + L.mean_off + L.mean_layer * layer) : nullptr;
-        a.kpart = fp8 ? (double*)(h->pool + L.part_off + L.part_layer * layer) : nullptr;
+        a.kpart = !fp8 ? nullptr
+                       : static_scratch ? (double*)sptr : (double*)(h->pool + L.part_off + L.part_layer * layer);
         a.table = h->table;
         a.htab = (const double2*)(h->pool + L.htab64_off);
         a.wtab = (const double2*)(h->pool + L.wtab64_off);
@@ -524,6 +542,20 @@ int wf_kv_publish(wf_handle* h, int32_t layer, int32_t slot_first, int32_t nslot
     }
     for (int i = 0; i < nslots; ++i) h->ready[layer] |= 1ull << h->position_of_slot(slot_first + i);
     return WF_OK;
+}
+
+int wf_kv_publish(wf_handle* h, int32_t layer, int32_t slot_first, int32_t nslots,
+                  const void* q, const void* k, const void* v, int64_t row_stride_elems,
+                  const int32_t* chunk_t0_host, void* q_out, float* q_scales, void* stream) {
+    return publish(h, layer, slot_first, nslots, q, k, v, row_stride_elems, chunk_t0_host, q_out, q_scales,
+                   stream, false);
+}
+
+int wf_kv_publish_noalloc(wf_handle* h, int32_t layer, int32_t slot_first, int32_t nslots,
+                          const void* q, const void* k, const void* v, int64_t row_stride_elems,
+                          const int32_t* chunk_t0_host, void* q_out, float* q_scales, void* stream) {
+    return publish(h, layer, slot_first, nslots, q, k, v, row_stride_elems, chunk_t0_host, q_out, q_scales,
+                   stream, true);
 }
 
 // The fused projection + publish, bf16 operands or (f8) e4m3 codes with

@@ -160,6 +160,9 @@ hipError_t launch_quant_rows(const uint16_t* x, int64_t rows, int cols, int64_t 
 hipError_t launch_page_table(int32_t* table, int T, int A, int ppc, int64_t ring, int64_t* ring_dev, int store_pos,
                              int store_anchor, hipStream_t st);
 hipError_t launch_publish(const PublishArgs& a, bool fp8, hipStream_t st);
+// wf_kv_publish_noalloc's scratch: one static device array per GPU
+constexpr size_t kStaticScratchBytes = (size_t)16 << 20;
+hipError_t static_scratch(void** ptr);
 
 hipError_t launch_attention(const AttnArgs& a, bool fp8, hipStream_t st);
 

@@ -10,7 +10,14 @@
 // K channel-chunk major, V token-chunk major).
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "wf_internal.h"
+
+// Scratch of wf_kv_publish_noalloc: the fp8 K-mean block sums, for callers
+// that cannot allocate. One array per GPU, held until the process ends; host
+// code reaches it only through the per-device address from static_scratch().
+static __device__ __align__(256) unsigned char scratch[wf::kStaticScratchBytes];
 
 namespace wf {
 namespace {
@@ -633,6 +640,31 @@ hipError_t launch_publish_t(const PublishArgs& a, bool fp8, hipStream_t st) {
     hipLaunchKernelGGL((kmean_reduce_kernel<D>), dim3(a.heads, a.nslots), dim3(D), 0, st, a);
     hipLaunchKernelGGL((publish_fp8_kernel<D, IN_FP32>), grid, dim3(256), tbytes, st, a);
     return hipGetLastError();
+}
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+// Device address of this GPU's copy of `scratch` (the array's name is a host
+// stand-in, not a device address), looked up once per device with that device
+// current.
+hipError_t static_scratch(void** ptr) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return hipSuccess;
 }
 
 hipError_t launch_publish(const PublishArgs& a, bool fp8, hipStream_t st) {
