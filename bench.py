@@ -223,6 +223,22 @@ def main():
     torch.cuda.synchronize()
     slot0_ms = [cev[i].elapsed_time(cev[i + 1]) for i in range(K)]
 
+    # the matrix-core rate this GPU sustains under MFMA load at its current
+    # clock (wf_mfma_calibrate: the attention step's MFMA mix, operands in
+    # registers, one 8-wave workgroup per CU), timed right after the attention
+    ncu = torch.cuda.get_device_properties(dev).multi_processor_count
+    csteps = 4096
+    cal_out = torch.empty(ncu * 512, dtype=torch.float32, device=dev)
+    wf.wf_mfma_calibrate(ncu, csteps, cal_out, stream=stream)
+    cal_ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+    cal_ev[0].record(stream)
+    for i in range(5):
+        wf.wf_mfma_calibrate(ncu, csteps, cal_out, stream=stream)
+        cal_ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    cal_ms = [cal_ev[i].elapsed_time(cal_ev[i + 1]) for i in range(5)]
+    cal_flops = float(ncu) * 8 * csteps * 32 * 32768
+
     graph = None
     if args.graph:
         # the same step captured once and replayed; each replay is one more round
@@ -386,6 +402,12 @@ def main():
                             "attention_ms_minmax": [round(min(slot0_ms), 4), round(max(slot0_ms), 4)],
                             "flops": f0, "tflops": round(f0 / (s0 * 1e-3) / 1e12, 2),
                             "launches": K}
+    cal_tflops = cal_flops / (float(np.median(cal_ms)) * 1e-3) / 1e12
+    res["mfma_ceiling"] = {"tflops": round(cal_tflops, 1), "frac_of_peak": round(cal_tflops / PEAK_BF16_TFLOPS, 4),
+                           "attention_frac_of_ceiling": round(attn_tflops / cal_tflops, 4),
+                           "ms": round(float(np.median(cal_ms)), 4), "cus": ncu,
+                           "what": "wf_mfma_calibrate: the attention step's 32 bf16 MFMAs per wave, operands in "
+                                   "registers, one 8-wave workgroup per CU, 4096 steps, median of 5 launches"}
     if graph is not None:
         res["graph"] = graph
     if proj is not None:

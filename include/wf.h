@@ -325,6 +325,18 @@ int wf_ready_mask(const wf_handle* h, int32_t layer, uint64_t* mask /* bit p = p
  * K-scale bytes per layer, fp8 K-mean region offset, K-mean bytes per layer,
  * 64-token blocks per chunk. Byte offsets are into the pool. */
 int wf_geometry(const wf_handle* h, int64_t* out);
+/*
+ * Matrix-core calibration for the attention roofline: `blocks` workgroups of
+ * 8 waves (one per CU, as the attention kernel runs), each wave issuing
+ * `steps` x 32 v_mfma_f32_32x32x16_bf16 on nonzero register operands, the
+ * attention step's MFMA mix (16 into two score blocks, 16 into four output
+ * blocks). FLOPs = blocks * 8 * steps * 32 * 32768. Timed by the caller on
+ * `stream`, it gives the dense bf16 rate this GPU sustains at the clock it
+ * holds under MFMA load, the attention kernel's attainable ceiling (no memory
+ * traffic, no softmax). out: device float [blocks * 512], a checksum per lane.
+ */
+int wf_mfma_calibrate(int32_t blocks, int32_t steps, float* out, void* stream);
+
 const char* wf_status_string(int status);
 const char* wf_last_error(const wf_handle* h);
 

@@ -10,7 +10,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libwf.so")
-SOURCES = ["wf_api.cpp", "wf_publish.hip", "wf_attention.hip", "wf_project.hip"]
+SOURCES = ["wf_api.cpp", "wf_publish.hip", "wf_attention.hip", "wf_project.hip", "wf_calib.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

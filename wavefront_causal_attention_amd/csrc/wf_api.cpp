@@ -899,6 +899,12 @@ int wf_geometry(const wf_handle* h, int64_t* out) {
     return WF_OK;
 }
 
+int wf_mfma_calibrate(int32_t blocks, int32_t steps, float* out, void* stream) {
+    if (blocks < 1 || steps < 1 || !out) return WF_E_INVALID_ARG;
+    const hipError_t e = wf::launch_mfma_calibrate(blocks, steps, out, (hipStream_t)stream);
+    return e == hipSuccess ? WF_OK : WF_E_HIP;
+}
+
 const char* wf_status_string(int status) {
     switch (status) {
         case WF_OK: return "ok";

@@ -165,5 +165,7 @@ constexpr size_t kStaticScratchBytes = (size_t)16 << 20;
 hipError_t static_scratch(void** ptr);
 
 hipError_t launch_attention(const AttnArgs& a, bool fp8, hipStream_t st);
+// blocks workgroups of 8 waves, each `steps` steps of 32 bf16 MFMAs per wave
+hipError_t launch_mfma_calibrate(int32_t blocks, int32_t steps, float* out, hipStream_t st);
 
 }  // namespace wf
