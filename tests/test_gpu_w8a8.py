@@ -6,16 +6,18 @@ The quantiser decides integers from floating point, so both sides decide in
 the same precision (the IEEE fp32 quotient x / scale) and codes and scales
 must be bit-identical. The projection then starts from the same codes on both
 sides: the oracle sums the dequantised products in fp64; the kernel sums code
-products on the e4m3 MFMA, which does not add its 64 products exactly. Probed
-on controlled inputs, one v_mfma_f32_32x32x64_f8f6f4 returns its dot product
-within 2^-12 of the instruction's largest product (small products are dropped
-below a fixed number of bits under the largest, as if aligned to it), while
-the fp32 accumulator add is exact. So each element of the projection may
-differ from the exact one by up to ACC_REL * sum_c |x^_c w^_c| (2x the probed
-worst case), and a published element is bounded by that (after RoPE: the sum
-over its channel pair) plus one bf16 ulp. End to end, attention over the W8A8
-publish meets the bf16 bar (max-abs 1e-2, rel-L2 5e-3, fp32 output mode)
-against the oracle's attention over the oracle's W8A8 projection.
+products on the e4m3 MFMA, which does not add its 64 products exactly: small
+products lose bits below a fixed distance from the instruction's largest one
+(test_e4m3_mfma_summation_on_controlled_codes: 448 - 448 + 62 x 2^-9 comes
+back as 0.109375 instead of 0.12109375, 448 x 2 - 448 x 2 + 60 x 2^-6 as
+0.875 instead of 0.9375), while the fp32 accumulator add is exact. So each
+element of the projection may differ from the exact one by up to ACC_REL *
+sum_c |x^_c w^_c|, and a published element is bounded by that (after RoPE:
+the sum over its channel pair) plus one bf16 ulp. Random full-range codes use
+up to 0.92 of that allowance, data drawn like the workloads' up to 0.8. End
+to end, attention over the W8A8 publish meets the bf16 bar (max-abs 1e-2,
+rel-L2 5e-3, fp32 output mode) against the oracle's attention over the
+oracle's W8A8 projection.
 """
 import sys
 
@@ -422,3 +424,57 @@ def test_projection_hidden_width_other_than_heads_times_dim(kind, hidden):
     torch.cuda.synchronize()
     diff, total, worst = _check_pages(r, live, range(w.S + 1))
     say("elements differing from the oracle: %d of %d; worst share of the allowance %.3f" % (diff, total, worst))
+
+
+def test_e4m3_mfma_summation_on_controlled_codes():
+    """The tolerance basis of the W8A8 pages, on codes chosen by hand: one
+    128-channel stage (two 64-code MFMA k-groups) with unit scales and unit
+    V weights, so a V element is the plain sum of its token's codes.
+      token 0: 448, -448 and 62 x 2^-9 -> exact 62 x 2^-9 = 0.12109375
+      token 1: 448, -448, 448, -448 and 60 x 2^-6 -> exact 0.9375
+      token 2: 448 and 63 x 2^-9 (the small ones far below the largest)
+      other tokens: random finite codes (Q/K/V weights random finite codes).
+    Every published element must lie within one bf16 ulp plus
+    ACC_REL * sum |x^ w^| of the exact sum (the bound the other W8A8 tests
+    use); the observed values of the cancelling tokens are printed."""
+    w = W.WORKLOADS["ragged128"]
+    hidden = 128
+    say("case ragged128, e4m3 MFMA summation on controlled codes")
+    rng = np.random.default_rng(77)
+    finite = np.array([c for c in range(256) if c & 0x7F != 0x7F], dtype=np.uint8)
+    xs_codes = []
+    for s in range(w.S + 1):
+        x = rng.choice(finite, size=(w.N, hidden))
+        if s == 0:
+            x[:3] = 0
+            x[0, 0], x[0, 1], x[0, 2:64] = 0x7E, 0xFE, 0x01
+            x[1, 0:4], x[1, 4:64] = [0x7E, 0xFE, 0x7E, 0xFE], 0x08
+            x[2, 0], x[2, 1:64] = 0x7E, 0x01
+        xs_codes.append(x)
+    wc = rng.choice(finite, size=(3 * w.hd, hidden))
+    wc[2 * w.hd:] = 0x38                                      # V weights: 1.0
+    ones = lambda n: np.ones(n, dtype=np.float32)
+    r = RoundRunner(w)
+    x8 = torch.from_numpy(np.concatenate(xs_codes, 0)).cuda()
+    sx = torch.from_numpy(ones((w.S + 1) * w.N)).cuda()
+    w8 = torch.from_numpy(wc).cuda()
+    sw = torch.from_numpy(ones(3 * w.hd)).cuda()
+    r.pool.project_publish_w8a8(0, 0, w.S + 1, x8, x8.stride(0), sx, hidden, w8, sw, None, q_out=r.q)
+    torch.cuda.synchronize()
+    live = [tuple(split_qkv(project_qkv_w8a8(xs_codes[s], ones(w.N), wc, ones(3 * w.hd), None), w.hd))
+            for s in range(w.S + 1)]
+    r.live = live
+    wabs = np.abs(fp8_e4m3_decode(wc))
+    r.absum = lambda s, rows=slice(None): np.abs(fp8_e4m3_decode(xs_codes[s][rows])) @ wabs.T
+    diff, total, worst = _check_pages(r, live, range(w.S + 1))
+    say("elements differing from the exact sums: %d of %d; worst share of the allowance %.3f" % (diff, total, worst))
+    # the cancelling tokens, through slot 0's V pages
+    _, vp = read_pages(r.pool, w)
+    v0 = position_rows(vp, r.pool.table.cpu().numpy(), w.T - 1, r.pool.ppc)      # [heads, N, d]
+    for tok, exact in [(0, 62 * 2.0 ** -9), (1, 60 * 2.0 ** -6), (2, 448 + 63 * 2.0 ** -9)]:
+        got = float(v0[0, tok, 0])
+        absum = float(np.sum(np.abs(fp8_e4m3_decode(xs_codes[0][tok]))))
+        say("token %d: exact %.8f, published %.8f, |error| / sum|x w| = %.3e (allowed %.3e)"
+            % (tok, exact, got, abs(got - exact) / absum, ACC_REL))
+        assert np.all(v0[:, tok, :] == got)                    # every V channel sums the same codes
+        assert abs(got - exact) <= float(_bf16_ulp(np.float64(exact))) + ACC_REL * absum
