@@ -27,7 +27,6 @@ METRIC = "wavefront-round attention TFLOP/s + rounds/sec, 1 MI355X, Wan2.1-1.3B 
 PEAK_BF16_TFLOPS = 2500.0          # MI355X dense bf16 MFMA
 PEAK_FP8_TFLOPS = 5000.0           # MI355X dense fp8 MFMA
 PEAK_HBM_GBPS = 8000.0             # MI355X HBM3E
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_bf16_wan1.3b_s4_traffic.txt")
 # the attention kernel and the host code that orders its work (the order
 # decides which K/V reads hit L2, so it changes the traffic)
 ATTN_SOURCES = [os.path.join(ROOT, "wavefront_causal_attention_amd", "csrc", f)
@@ -41,13 +40,20 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic():
-    """HBM bytes per attention launch from the committed counter summary, or
-    None if the kernel source changed since the counters were taken."""
-    if not os.path.exists(TRAFFIC_FILE):
+def traffic_file(workload: str, fp8: bool) -> str:
+    """The committed counter summary of this workload's attention kernel."""
+    return os.path.join(ROOT, "profiles", f"attn_{'fp8' if fp8 else 'bf16'}_{workload}_traffic.txt")
+
+
+def measured_traffic(workload: str, fp8: bool):
+    """HBM bytes per attention launch from the committed counter summary of
+    this workload, or None if there is none or the kernel source changed
+    since the counters were taken."""
+    path = traffic_file(workload, fp8)
+    if not os.path.exists(path):
         return None
     vals = {}
-    for line in open(TRAFFIC_FILE):
+    for line in open(path):
         if ":" in line:
             k, v = line.split(":", 1)
             vals[k.strip()] = v.strip()
@@ -282,7 +288,9 @@ def main():
     qk_bytes = 1 if w.qk_dtype == "fp8" else 2
     pub_bytes = in_bytes + 2 * n_el * qk_bytes + 2 * n_el            # read QKV; write Q, K, V
     attn_tflops = w.attention_flops() / (att_avg * 1e-3) / 1e12
-    traffic = measured_traffic()
+    # the counters were taken with the workload's own mask and bf16 output
+    same_launch = args.live_mask == W.WORKLOADS[args.workload].live_mask and args.out_dtype == "bf16"
+    traffic = measured_traffic(args.workload, w.qk_dtype == "fp8") if same_launch else None
 
     proj = None
     if args.project:
@@ -344,6 +352,25 @@ def main():
                     "unfused_publish_ms": round(avg["publish"], 4),
                     "unfused_ms": round(avg["addmm"] + avg["publish"], 4)}
 
+    # A plain device copy moving as many bytes as the publish (half read, half
+    # written), timed in the same session: the rate an HBM-bound kernel with
+    # this read/write mix reaches here, beside the publish's own rate.
+    ncopy = pub_bytes // 2
+    csrc = torch.empty(ncopy, dtype=torch.uint8, device=dev).fill_(1)
+    cdst = torch.empty_like(csrc)
+    torch.cuda.synchronize()
+    kev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    with torch.cuda.stream(stream):
+        for _ in range(3):
+            cdst.copy_(csrc)
+        kev[0].record(stream)
+        for _ in range(20):
+            cdst.copy_(csrc)
+        kev[1].record(stream)
+    torch.cuda.synchronize()
+    copy_gbps = 2 * ncopy / (kev[0].elapsed_time(kev[1]) / 20 * 1e-3) / 1e9
+    del csrc, cdst
+
     if args.calibrate_copy_mib > 0:
         nb = args.calibrate_copy_mib * (1 << 20)
         src = torch.empty(nb, dtype=torch.uint8, device=dev).fill_(1)
@@ -352,6 +379,10 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
 
+    # bf16: the dense bf16 MFMA peak. fp8: half the flops (QK^T) run on fp8
+    # MFMAs and half (PV) on bf16, so the bound is F / (F/2 / 5000 + F/2 / 2500)
+    attn_peak = (PEAK_BF16_TFLOPS if w.qk_dtype == "bf16"
+                 else 1.0 / (0.5 / PEAK_FP8_TFLOPS + 0.5 / PEAK_BF16_TFLOPS))
     res = {
         "metric": METRIC,
         "value": round(F * K / wall / 1e12, 3),
@@ -382,13 +413,15 @@ def main():
         "advance_ms": round(float(np.mean(adv_ms)), 4),
         "attention_tflops": round(attn_tflops, 2),
         "publish_gbps": round(pub_bytes / (pub_avg * 1e-3) / 1e9, 1),
-        "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+        "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": round(attn_peak, 1),
+                     "unit": "TFLOP/s", "frac": round(attn_tflops / attn_peak, 4),
                      "traffic": traffic},
         "publish_roofline": {"bound": "hbm", "achieved": round(pub_bytes / (pub_avg * 1e-3) / 1e9, 1),
                              "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                              "frac": round(pub_bytes / (pub_avg * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
-                             "algorithmic_bytes": pub_bytes},
+                             "algorithmic_bytes": pub_bytes,
+                             "device_copy_gbps": round(copy_gbps, 1),
+                             "frac_of_device_copy": round(pub_bytes / (pub_avg * 1e-3) / 1e9 / copy_gbps, 4)},
     }
     def _spread(key):
         v = [b[key] for b in blocks]
@@ -404,7 +437,9 @@ def main():
                             "launches": K}
     cal_tflops = cal_flops / (float(np.median(cal_ms)) * 1e-3) / 1e12
     res["mfma_ceiling"] = {"tflops": round(cal_tflops, 1), "frac_of_peak": round(cal_tflops / PEAK_BF16_TFLOPS, 4),
-                           "attention_frac_of_ceiling": round(attn_tflops / cal_tflops, 4),
+                           # the ceiling is that of bf16 MFMAs: compared with bf16 attention only
+                           "attention_frac_of_ceiling": (round(attn_tflops / cal_tflops, 4)
+                                                         if w.qk_dtype == "bf16" else None),
                            "ms": round(float(np.median(cal_ms)), 4), "cus": ncu,
                            "what": "wf_mfma_calibrate: the attention step's 32 bf16 MFMAs per wave, operands in "
                                    "registers, one 8-wave workgroup per CU, 4096 steps, median of 5 launches"}
