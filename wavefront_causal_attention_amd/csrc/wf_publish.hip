@@ -37,6 +37,30 @@ __host__ __device__ inline int frames_per_tile(int hw) {
     return f < kMaxFramesPerTile ? f : kMaxFramesPerTile;
 }
 
+// floor(n / d) for 0 <= n < 2^22 (every token index: the host keeps T * N
+// below 2^22) as one fp32 fma, floor((n + 1/2) r) with r = 1/d rounded to
+// fp32: (n + 1/2) / d lies at least 1/(2d) from an integer, and the fma's
+// result is within about 2^-23 of it relative, which stays below that margin
+// for n < 2^22. Runtime integer division costs tens of instructions a token.
+struct SmallDiv {
+    float r;
+    __device__ explicit SmallDiv(int d) : r(1.0f / (float)d) {}
+    __device__ int operator()(int n) const { return (int)__builtin_fmaf((float)n, r, 0.5f * r); }
+};
+__device__ __forceinline__ int mul24(int a, int b) { return (int)__umul24((uint32_t)a, (uint32_t)b); }
+// Frame, row and column of token n of a chunk (frames of h x w patches, row-major).
+struct TokenGrid {
+    SmallDiv dhw, dw;
+    int hw, w;
+    __device__ TokenGrid(int h, int w_) : dhw(h * w_), dw(w_), hw(h * w_), w(w_) {}
+    __device__ void pos(int n, int& f, int& y, int& x) const {
+        f = dhw(n);
+        const int r = n - mul24(f, hw);
+        y = dw(r);
+        x = r - mul24(y, w);
+    }
+};
+
 __device__ __forceinline__ float bf_to_f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
 // Projection rows are read exactly once, so their loads take the
@@ -202,12 +226,13 @@ __global__ __launch_bounds__(256) void publish_bf16_kernel(PublishArgs a) {
 
     const int64_t row0 = (int64_t)sr * a.N;
     const int64_t col = (int64_t)head * D;
+    const TokenGrid grid(a.frame_h, a.frame_w);
+    const SmallDiv dpt(a.pt);
     auto rotate_and_stage = [&](int tk, int ch, float (&x)[8], float (&y)[8], float (&z)[8]) {
         // x = K, y = Q, z = V of token n0 + tk, channels ch*8 .. ch*8+7
         const int n = n0 + tk;
-        const int f = n / HW;
-        const int yy = (n / a.frame_w) % a.frame_h;
-        const int xw = n % a.frame_w;
+        int f, yy, xw;
+        grid.pos(n, f, yy, xw);
         const double2* tf = ttab[f - f_lo];
         const double2* hrow = a.htab + yy * (a.dh >> 1);
         const double2* wrow = a.wtab + xw * (a.dw >> 1);
@@ -269,7 +294,7 @@ __global__ __launch_bounds__(256) void publish_bf16_kernel(PublishArgs a) {
         const int ch = j / kTokB, tk = j - ch * kTokB;
         const int n = n0 + tk;
         if (n >= a.N) continue;
-        const int pg = n / a.pt, tok = n - pg * a.pt;
+        const int pg = dpt(n), tok = n - mul24(pg, a.pt);
         const int phys = a.table[p * a.ppc + pg];
         const int64_t base = ((int64_t)phys * a.heads + head) * a.pt * D;
         st16(static_cast<uint16_t*>(a.kpage) + k_elem(base, a.pt, tok, ch * 8),
@@ -286,7 +311,7 @@ __global__ __launch_bounds__(256) void publish_bf16_kernel(PublishArgs a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r)
             w[r] = (uint32_t)vst[(kc * 8 + 2 * r) * D + d] | ((uint32_t)vst[(kc * 8 + 2 * r + 1) * D + d] << 16);
-        const int pg = n / a.pt, tok = n - pg * a.pt;
+        const int pg = dpt(n), tok = n - mul24(pg, a.pt);
         const int phys = a.table[p * a.ppc + pg];
         const int64_t base = ((int64_t)phys * a.heads + head) * a.pt * D;
         st16(a.vpage + v_elem(base, D, tok, d), make_uint4(w[0], w[1], w[2], w[3]));
@@ -407,16 +432,18 @@ __global__ __launch_bounds__(256) void kmean_partial_kernel(PublishArgs a) {
     }
     fill_ttab(ttab, a, sr, f_lo, nf);
     __syncthreads();
+    const TokenGrid grid(a.frame_h, a.frame_w);
     double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
     for (int i = 0; i < IT; ++i) {
         const int n = n0 + row + ROWS * i;
         if (n >= a.N) break;
-        const int y = (n / a.frame_w) % a.frame_h, xw = n % a.frame_w;
+        int f, y, xw;
+        grid.pos(n, f, y, xw);
         float x[8];
         double r[8];
         kin[i].unpack(x);
-        rope8(x, r, ch * 8, ttab[n / HW - f_lo], a.htab + y * (a.dh >> 1), a.wtab + xw * (a.dw >> 1), a.dt, a.dh);
+        rope8(x, r, ch * 8, ttab[f - f_lo], a.htab + y * (a.dh >> 1), a.wtab + xw * (a.dw >> 1), a.dt, a.dh);
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[e] += r[e];
     }
@@ -490,11 +517,14 @@ __global__ __launch_bounds__(256) void publish_fp8_kernel(PublishArgs a) {
     const int g = a.table[p * a.ppc] / a.ppc;
     if (tid < D) mu[tid] = a.kmean[((int64_t)g * a.heads + head) * D + tid];
     __syncthreads();
+    const TokenGrid grid(a.frame_h, a.frame_w);
+    const SmallDiv dpt(a.pt);
     auto rotate = [&](const Raw8<IN_FP32>& in, int n, double* out) {
-        const int y = (n / a.frame_w) % a.frame_h, xw = n % a.frame_w;
+        int f, y, xw;
+        grid.pos(n, f, y, xw);
         float x[8];
         in.unpack(x);
-        rope8(x, out, ch * 8, ttab[n / HW - f_lo], a.htab + y * (a.dh >> 1), a.wtab + xw * (a.dw >> 1), a.dt, a.dh);
+        rope8(x, out, ch * 8, ttab[f - f_lo], a.htab + y * (a.dh >> 1), a.wtab + xw * (a.dw >> 1), a.dt, a.dh);
     };
 
     // V staged for the page stores
@@ -565,7 +595,7 @@ __global__ __launch_bounds__(256) void publish_fp8_kernel(PublishArgs a) {
         const int v16 = j / kTokTile, tk = j - v16 * kTokTile;
         const int n = n0 + tk;
         if (n >= a.N) continue;
-        const int pg = n / a.pt, tok = n - pg * a.pt;
+        const int pg = dpt(n), tok = n - mul24(pg, a.pt);
         const int phys = a.table[p * a.ppc + pg];
         const int64_t base = ((int64_t)phys * a.heads + head) * a.pt * D;
         st16(static_cast<uint8_t*>(a.kpage) + k8_byte(base, a.pt, tok, v16 * 16),
@@ -573,7 +603,7 @@ __global__ __launch_bounds__(256) void publish_fp8_kernel(PublishArgs a) {
     }
     if (tid < kTokTile && n0 + tid < a.N) {
         const int n = n0 + tid;
-        const int pg = n / a.pt, tok = n - pg * a.pt;
+        const int pg = dpt(n), tok = n - mul24(pg, a.pt);
         const int phys = a.table[p * a.ppc + pg];
         a.kscale[((int64_t)phys * a.heads + head) * a.pt + tok] = ks;
     }
@@ -586,7 +616,7 @@ __global__ __launch_bounds__(256) void publish_fp8_kernel(PublishArgs a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r)
             w[r] = (uint32_t)vst[(kc * 8 + 2 * r) * D + d] | ((uint32_t)vst[(kc * 8 + 2 * r + 1) * D + d] << 16);
-        const int pg = n / a.pt, tok = n - pg * a.pt;
+        const int pg = dpt(n), tok = n - mul24(pg, a.pt);
         const int phys = a.table[p * a.ppc + pg];
         const int64_t base = ((int64_t)phys * a.heads + head) * a.pt * D;
         st16(a.vpage + v_elem(base, D, tok, d), make_uint4(w[0], w[1], w[2], w[3]));
