@@ -152,8 +152,11 @@ void wf_pool_destroy(wf_handle* h);
  *          NULL to publish K/V only.
  * The K pages of the slot's context position receive RoPE'd K (bf16, or fp8
  * with per-64-token-block scales after subtracting the chunk's per-channel
- * mean); the V pages receive V in bf16. Marks the slots published for this
- * layer and round. WF_E_INVALID_ARG if a slot in the range holds no chunk in
+ * mean); the V pages receive V in bf16. RoPE is computed in fp64 and every
+ * published Q/K value is rounded once from it: bf16 to nearest even, fp8 as
+ * the nearest-even e4m3 code of the fp64 quotient value / scale, scale =
+ * fp32(block absmax) / 448, the mean the fp32 rounding of the fp64 mean.
+ * Marks the slots published for this layer and round. WF_E_INVALID_ARG if a slot in the range holds no chunk in
  * this round (fill and drain rounds).
  */
 int wf_kv_publish(wf_handle* h, int32_t layer, int32_t slot_first, int32_t nslots,
