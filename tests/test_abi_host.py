@@ -553,3 +553,13 @@ def test_round_replayed_only_in_steady_rounds(lib):
     finally:
         wf.wf_pool_destroy(fill)
         wf.wf_pool_destroy(last)
+
+
+@pytest.mark.parametrize("blocks,steps,out", [(0, 1, FAKE), (1, 0, FAKE), (-3, 8, FAKE), (1, 1, None)])
+def test_mfma_calibrate_rejects_bad_arguments_before_any_launch(lib, blocks, steps, out):
+    """The calibration entry checks its arguments on the host: no workgroups,
+    no steps or no output buffer return WF_E_INVALID_ARG and launch nothing
+    (the fake address is never touched)."""
+    with pytest.raises(wf.WfError) as e:
+        _lib.wf_mfma_calibrate(blocks, steps, out, stream=0)
+    assert e.value.status == _lib.WF_E_INVALID_ARG
