@@ -23,9 +23,6 @@ namespace wf {
 namespace {
 
 constexpr int kTokTile = 64;                 // tokens per fp8 publish block (one quantisation block)
-// tokens per bf16 publish block: 32 gives twice the blocks of 64 and a finer
-// last wave of blocks, measured 2-4% faster at the Wan shapes (16 and 128 slower)
-constexpr int kTokB = 32;
 constexpr int kMaxFramesPerTile = kTokTile + 2;
 
 // Time-axis (cos, sin) table of the frames one publish block (at most 64
@@ -137,25 +134,36 @@ __device__ __forceinline__ uint4 pack8(const float* x) {
                       pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7]));
 }
 
-// Rotate the 4 channel pairs of one 8-channel vector starting at channel c0,
-// in fp64 from fp64 (cos, sin) tables: the published page holds the rotated
-// value rounded once to the page format, so the rotation itself must be
-// accurate far below a bf16 (or e4m3) rounding step. In fp32 about one element
-// in 10^5 landed on the other side of a bf16 rounding midpoint, which on a
-// x20 outlier channel moves a score by several units.
-__device__ __forceinline__ void rope8(const float* x, double* y, int c0, const double2* ttab_f,
-                                      const double2* hrow, const double2* wrow, int dt, int dh) {
+// Rotate the 4 channel pairs of one 8-channel vector starting at channel c0
+// (rope_cs looks up their (cos, sin), rot8 rotates), in fp64 from fp64
+// (cos, sin) tables: the published page holds the rotated value rounded once
+// to the page format, so the rotation itself must be accurate far below a
+// bf16 (or e4m3) rounding step. In fp32 about one element in 10^5 landed on
+// the other side of a bf16 rounding midpoint, which on a x20 outlier channel
+// moves a score by several units.
+__device__ __forceinline__ void rope_cs(double2* cs, int c0, const double2* ttab_f, const double2* hrow,
+                                        const double2* wrow, int dt, int dh) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int c = c0 + 2 * i;
-        double2 cs;
-        if (c < dt) cs = ttab_f[c >> 1];
-        else if (c < dt + dh) cs = hrow[(c - dt) >> 1];
-        else cs = wrow[(c - dt - dh) >> 1];
-        const double a = x[2 * i], b = x[2 * i + 1];
-        y[2 * i] = fma(a, cs.x, -(b * cs.y));
-        y[2 * i + 1] = fma(a, cs.y, b * cs.x);
+        if (c < dt) cs[i] = ttab_f[c >> 1];
+        else if (c < dt + dh) cs[i] = hrow[(c - dt) >> 1];
+        else cs[i] = wrow[(c - dt - dh) >> 1];
     }
+}
+__device__ __forceinline__ void rot8(const float* x, double* y, const double2* cs) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const double a = x[2 * i], b = x[2 * i + 1];
+        y[2 * i] = fma(a, cs[i].x, -(b * cs[i].y));
+        y[2 * i + 1] = fma(a, cs[i].y, b * cs[i].x);
+    }
+}
+__device__ __forceinline__ void rope8(const float* x, double* y, int c0, const double2* ttab_f,
+                                      const double2* hrow, const double2* wrow, int dt, int dh) {
+    double2 cs[4];
+    rope_cs(cs, c0, ttab_f, hrow, wrow, dt, dh);
+    rot8(x, y, cs);
 }
 
 // Rounding an fp64 value once into bf16 (or e4m3) through fp32: the fp32
@@ -202,118 +210,103 @@ __device__ __forceinline__ void fill_ttab(double2 (*ttab)[32], const Args& a, in
     }
 }
 
-// grid: (ceil(N/32), heads, nslots); block 256. One block rotates and
-// publishes 32 tokens of one head of one slot. Reads run along channels
-// (coalesced rows of the projection output); page writes run along tokens, so
-// K and V are transposed through LDS.
-template <int D, bool IN_FP32>
+// grid: (ceil(N / TOK), heads / HPB, nslots); block 256. One block rotates
+// and publishes TOK = 256 / (D/8) tokens (16 at D = 128) of HPB heads of one
+// slot. A thread owns one token and one 8-channel group in each of the HPB
+// heads: the rotation's (cos, sin) depend on the token and channel only, so
+// one lookup serves HPB heads of Q and of K, and a token's input reads are
+// HPB * 2*D contiguous bytes of its row. Reads run along channels (coalesced
+// rows of the projection output); page writes run along tokens, so K and V
+// are transposed through LDS.
+template <int D, bool IN_FP32, int HPB>
 __global__ __launch_bounds__(256) void publish_bf16_kernel(PublishArgs a) {
     constexpr int CPR = D / 8;                       // 8-channel vectors per token row
+    constexpr int TOK = 256 / CPR;                   // tokens per block
     double2 (*ttab)[32] = reinterpret_cast<double2 (*)[32]>(g_ttab_dyn);   // time-axis (cos, sin), this tile's frames
-    __shared__ __align__(16) uint4 kst[CPR * kTokB];       // K vectors, [ch][tok ^ (ch & 7)]
-    __shared__ __align__(16) uint16_t vst[kTokB * D];      // V rows, [tok][d]
+    __shared__ __align__(16) uint4 kst[HPB * CPR * TOK];     // K vectors, [head][ch][tok ^ (ch & 7)]
+    __shared__ __align__(16) uint16_t vst[HPB * TOK * D];    // V rows, [head][tok][d]
 
     const int tid = threadIdx.x;
     const int sr = blockIdx.z;
     const int s = a.slot_first + sr;
-    const int head = blockIdx.y;
-    const int n0 = blockIdx.x * kTokB;
+    const int h0 = blockIdx.y * HPB;
+    const int n0 = blockIdx.x * TOK;
     const int p = a.T - 1 - s;                       // context position of slot s
     const int HW = a.frame_h * a.frame_w;
     const int f_lo = n0 / HW;
-    const int n_hi = min(n0 + kTokB, a.N) - 1;
+    const int n_hi = min(n0 + TOK, a.N) - 1;
     const int nf = n_hi / HW - f_lo + 1;
+    const int tk = tid / CPR, ch = tid - tk * CPR;
+    const int n = n0 + tk;
+    const bool live = n < a.N;
 
-    const int64_t row0 = (int64_t)sr * a.N;
-    const int64_t col = (int64_t)head * D;
-    const TokenGrid grid(a.frame_h, a.frame_w);
-    const SmallDiv dpt(a.pt);
-    auto rotate_and_stage = [&](int tk, int ch, float (&x)[8], float (&y)[8], float (&z)[8]) {
-        // x = K, y = Q, z = V of token n0 + tk, channels ch*8 .. ch*8+7
-        const int n = n0 + tk;
+    // every row load of this thread is issued before the time-axis table is
+    // built, so the HBM latency overlaps the fp64 sincos work (rows past the
+    // chunk are clamped to its last row and not used)
+    const int64_t e0 = ((int64_t)sr * a.N + min(n, a.N - 1)) * a.row_stride + (int64_t)h0 * D + ch * 8;
+    Raw8<IN_FP32> kin[HPB], qin[HPB], vin[HPB];
+#pragma unroll
+    for (int hh = 0; hh < HPB; ++hh) {
+        kin[hh].load(a.k, e0 + hh * D);
+        vin[hh].load(a.v, e0 + hh * D);
+        if (a.q) qin[hh].load(a.q, e0 + hh * D);
+    }
+    fill_ttab(ttab, a, sr, f_lo, nf);
+    __syncthreads();
+
+    if (live) {
+        const TokenGrid grid(a.frame_h, a.frame_w);
         int f, yy, xw;
         grid.pos(n, f, yy, xw);
-        const double2* tf = ttab[f - f_lo];
-        const double2* hrow = a.htab + yy * (a.dh >> 1);
-        const double2* wrow = a.wtab + xw * (a.dw >> 1);
-        double r[8];
-        rope8(x, r, ch * 8, tf, hrow, wrow, a.dt, a.dh);
-        kst[ch * kTokB + (tk ^ (ch & 7))] = pack8_f64(r);
-        if (a.q) {
-            rope8(y, r, ch * 8, tf, hrow, wrow, a.dt, a.dh);
-            uint16_t* qp = static_cast<uint16_t*>(a.q_out) + (((int64_t)s * a.heads + head) * a.N + n) * D + ch * 8;
-            st16(qp, pack8_f64(r));
-        }
-        *reinterpret_cast<uint4*>(&vst[tk * D + ch * 8]) = pack8(z);
-    };
-
-    if constexpr (!IN_FP32) {
-        // Every load of this thread's rows is issued before the time-axis
-        // table is built, so the HBM latency overlaps the fp64 sincos work.
-        constexpr int IT = (kTokB * CPR + 255) / 256;   // the last may reach past the block
-        uint4 kr[IT], qr[IT], vr[IT];
+        double2 cs[4];                               // one lookup for every head and for Q and K
+        rope_cs(cs, ch * 8, ttab[f - f_lo], a.htab + yy * (a.dh >> 1), a.wtab + xw * (a.dw >> 1), a.dt, a.dh);
 #pragma unroll
-        for (int i = 0; i < IT; ++i) {
-            const int c = tid + 256 * i, tk = c / CPR, ch = c - tk * CPR;
-            const int n = min(n0 + tk, a.N - 1);          // rows past the chunk are read but not used
-            const int64_t e = (row0 + n) * a.row_stride + col + ch * 8;
-            kr[i] = ld_stream16(static_cast<const uint16_t*>(a.k) + e);
-            vr[i] = ld_stream16(static_cast<const uint16_t*>(a.v) + e);
-            qr[i] = a.q ? ld_stream16(static_cast<const uint16_t*>(a.q) + e) : make_uint4(0, 0, 0, 0);
-        }
-        fill_ttab(ttab, a, sr, f_lo, nf);
-        __syncthreads();
-#pragma unroll
-        for (int i = 0; i < IT; ++i) {
-            const int c = tid + 256 * i, tk = c / CPR, ch = c - tk * CPR;
-            if (tk >= kTokB || n0 + tk >= a.N) continue;
-            float x[8], y[8], z[8];
-            unpack8(kr[i], x);
-            unpack8(qr[i], y);
-            unpack8(vr[i], z);
-            rotate_and_stage(tk, ch, x, y, z);
-        }
-    } else {
-        fill_ttab(ttab, a, sr, f_lo, nf);
-        __syncthreads();
-        for (int c = tid; c < kTokB * CPR; c += 256) {
-            const int tk = c / CPR, ch = c - tk * CPR;
-            if (n0 + tk >= a.N) continue;
-            const int64_t e = (row0 + n0 + tk) * a.row_stride + col + ch * 8;
-            float x[8], y[8], z[8];
-            load8<true>(a.k, e, x);
-            if (a.q) load8<true>(a.q, e, y);
-            load8<true>(a.v, e, z);
-            rotate_and_stage(tk, ch, x, y, z);
+        for (int hh = 0; hh < HPB; ++hh) {
+            float x[8];
+            double r[8];
+            kin[hh].unpack(x);
+            rot8(x, r, cs);
+            kst[(hh * CPR + ch) * TOK + (tk ^ (ch & 7))] = pack8_f64(r);
+            if (a.q) {
+                qin[hh].unpack(x);
+                rot8(x, r, cs);
+                uint16_t* qp = static_cast<uint16_t*>(a.q_out) +
+                               (((int64_t)s * a.heads + h0 + hh) * a.N + n) * D + ch * 8;
+                st16(qp, pack8_f64(r));
+            }
+            vin[hh].unpack(x);
+            *reinterpret_cast<uint4*>(&vst[(hh * TOK + tk) * D + ch * 8]) = pack8(x);
         }
     }
     __syncthreads();
 
+    const SmallDiv dpt(a.pt);
     // K pages: one 16-byte vector (8 channels of one token) per thread, tokens fastest
-    for (int j = tid; j < CPR * kTokB; j += 256) {
-        const int ch = j / kTokB, tk = j - ch * kTokB;
-        const int n = n0 + tk;
-        if (n >= a.N) continue;
-        const int pg = dpt(n), tok = n - mul24(pg, a.pt);
+    for (int j = tid; j < HPB * CPR * TOK; j += 256) {
+        const int hc = j / TOK, t = j - hc * TOK;    // hc = head * CPR + channel vector
+        const int hh = hc / CPR, c = hc - hh * CPR;
+        const int nn = n0 + t;
+        if (nn >= a.N) continue;
+        const int pg = dpt(nn), tok = nn - mul24(pg, a.pt);
         const int phys = a.table[p * a.ppc + pg];
-        const int64_t base = ((int64_t)phys * a.heads + head) * a.pt * D;
-        st16(static_cast<uint16_t*>(a.kpage) + k_elem(base, a.pt, tok, ch * 8),
-                    kst[ch * kTokB + (tk ^ (ch & 7))]);
+        const int64_t base = ((int64_t)phys * a.heads + h0 + hh) * a.pt * D;
+        st16(static_cast<uint16_t*>(a.kpage) + k_elem(base, a.pt, tok, c * 8), kst[hc * TOK + (t ^ (c & 7))]);
     }
     // V pages: one vector of 8 consecutive tokens of one channel per thread,
     // channels fastest. N and pages are multiples of 8, so a group never
     // straddles a page.
-    for (int j = tid; j < (kTokB / 8) * D; j += 256) {
-        const int kc = j / D, d = j - kc * D;
-        const int n = n0 + kc * 8;
-        if (n >= a.N) continue;
+    for (int j = tid; j < HPB * (TOK / 8) * D; j += 256) {
+        const int hk = j / D, d = j - hk * D;        // hk = head * (TOK / 8) + token group
+        const int hh = hk / (TOK / 8), kc = hk - hh * (TOK / 8);
+        const int nn = n0 + kc * 8;
+        if (nn >= a.N) continue;
+        const uint16_t* vrow = vst + (hh * TOK + kc * 8) * D + d;
         uint32_t w[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-            w[r] = (uint32_t)vst[(kc * 8 + 2 * r) * D + d] | ((uint32_t)vst[(kc * 8 + 2 * r + 1) * D + d] << 16);
-        const int pg = dpt(n), tok = n - mul24(pg, a.pt);
+        for (int r = 0; r < 4; ++r) w[r] = (uint32_t)vrow[(2 * r) * D] | ((uint32_t)vrow[(2 * r + 1) * D] << 16);
+        const int pg = dpt(nn), tok = nn - mul24(pg, a.pt);
         const int phys = a.table[p * a.ppc + pg];
-        const int64_t base = ((int64_t)phys * a.heads + head) * a.pt * D;
+        const int64_t base = ((int64_t)phys * a.heads + h0 + hh) * a.pt * D;
         st16(a.vpage + v_elem(base, D, tok, d), make_uint4(w[0], w[1], w[2], w[3]));
     }
 }
@@ -661,8 +654,18 @@ template <int D, bool IN_FP32>
 hipError_t launch_publish_t(const PublishArgs& a, bool fp8, hipStream_t st) {
     const size_t tbytes = (size_t)frames_per_tile(a.frame_h * a.frame_w) * 32 * sizeof(double2);
     if (!fp8) {
-        const dim3 gb((a.N + kTokB - 1) / kTokB, a.heads, a.nslots);
-        hipLaunchKernelGGL((publish_bf16_kernel<D, IN_FP32>), gb, dim3(256), tbytes, st, a);
+        // heads per block: 4 where they divide the head count (one (cos, sin)
+        // lookup per token and channel serves 4 heads; measured 2% faster
+        // than one head in 32-token blocks at the Wan shapes, 2 heads equal,
+        // 1 head in 16-token blocks 10% slower), else 2 or 1; fp32 inputs (a
+        // full-precision check mode) take one, as their rows take twice the
+        // registers
+        constexpr int TOK = 256 / (D / 8);
+        const int hpb = IN_FP32 ? 1 : a.heads % 4 == 0 ? 4 : a.heads % 2 == 0 ? 2 : 1;
+        const dim3 gb((a.N + TOK - 1) / TOK, a.heads / hpb, a.nslots);
+        if (hpb == 4) hipLaunchKernelGGL((publish_bf16_kernel<D, IN_FP32, (IN_FP32 ? 1 : 4)>), gb, dim3(256), tbytes, st, a);
+        else if (hpb == 2) hipLaunchKernelGGL((publish_bf16_kernel<D, IN_FP32, (IN_FP32 ? 1 : 2)>), gb, dim3(256), tbytes, st, a);
+        else hipLaunchKernelGGL((publish_bf16_kernel<D, IN_FP32, 1>), gb, dim3(256), tbytes, st, a);
         return hipGetLastError();
     }
     const dim3 grid((a.N + kTokTile - 1) / kTokTile, a.heads, a.nslots);
