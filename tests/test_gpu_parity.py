@@ -6,6 +6,7 @@ fp32 output mode, against the oracle with bf16 storage of the published Q/K
 placement, schedule) is compared bit for bit, and so are the published pages:
 each is the round-to-nearest-even of the fp64 rotation (V: of the input).
 """
+import dataclasses
 import sys
 
 import numpy as np
@@ -71,12 +72,33 @@ def test_round_parity_full(name):
     assert np.array_equal(gb, bf16_round(g))
 
 
-@pytest.mark.parametrize("name", ["tiny", "ragged128", "ragged64", "edge_s1_h0", "wan1.3b_s4", "wan14b_s4"])
+# The publish groups up to 4 heads per block (4 where they divide the head
+# count, else 2, else 1) and takes 256 / (head_dim / 8) tokens a block: these
+# variants of the mid-size shapes reach each grouping at both head sizes, with
+# a partial last token block (312 and 216 tokens), and a fused [tokens, 3*h*d]
+# input row.
+PLACEMENT_VARIANTS = {
+    "ragged128_h2": ("ragged128", {"heads": 2}),
+    "ragged128_h4_fused": ("ragged128", {"heads": 4, "fused_qkv": True}),
+    "ragged64_h4": ("ragged64", {"heads": 4}),
+    "ragged64_h3": ("ragged64", {"heads": 3}),
+}
+
+
+def _placement_workload(name):
+    if name in PLACEMENT_VARIANTS:
+        base, kw = PLACEMENT_VARIANTS[name]
+        return dataclasses.replace(W.WORKLOADS[base], name=name, **kw)
+    return W.WORKLOADS[name]
+
+
+@pytest.mark.parametrize("name", ["tiny", "ragged128", "ragged64", "edge_s1_h0", "wan1.3b_s4", "wan14b_s4"]
+                         + list(PLACEMENT_VARIANTS))
 def test_page_table_and_publish_placement(name):
     """Page table against the closed form; every published Q, K and V element
     equal, bit for bit, to the bf16 rounding of the oracle's fp64 RoPE (V: of
     the input), at its closed-form place in the pages."""
-    w = W.WORKLOADS[name]
+    w = _placement_workload(name)
     say("case", name, "placement")
     r = RoundRunner(w)
     r.seed_clean()
