@@ -370,6 +370,18 @@ def main():
         kev[1].record(stream)
     torch.cuda.synchronize()
     copy_gbps = 2 * ncopy / (kev[0].elapsed_time(kev[1]) / 20 * 1e-3) / 1e9
+    # the library's streaming copy of the same bytes (wf_stream_copy_calibrate:
+    # non-temporal 16-byte loads, nothing else): the HBM rate attainable for
+    # this read/write mix, the publish kernels' same-session ceiling
+    nstream = ncopy // 16 * 16
+    for _ in range(3):
+        wf.wf_stream_copy_calibrate(csrc, cdst, nstream, stream=stream)
+    kev[0].record(stream)
+    for _ in range(20):
+        wf.wf_stream_copy_calibrate(csrc, cdst, nstream, stream=stream)
+    kev[1].record(stream)
+    torch.cuda.synchronize()
+    stream_gbps = 2 * nstream / (kev[0].elapsed_time(kev[1]) / 20 * 1e-3) / 1e9
     del csrc, cdst
 
     if args.calibrate_copy_mib > 0:
@@ -422,7 +434,9 @@ def main():
                              "frac": round(pub_bytes / (pub_avg * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
                              "algorithmic_bytes": pub_bytes,
                              "d2d_memcpy_gbps": round(copy_gbps, 1),
-                             "frac_of_d2d_memcpy": round(pub_bytes / (pub_avg * 1e-3) / 1e9 / copy_gbps, 4)},
+                             "frac_of_d2d_memcpy": round(pub_bytes / (pub_avg * 1e-3) / 1e9 / copy_gbps, 4),
+                             "stream_copy_gbps": round(stream_gbps, 1),
+                             "frac_of_stream_copy": round(pub_bytes / (pub_avg * 1e-3) / 1e9 / stream_gbps, 4)},
     }
     def _spread(key):
         v = [b[key] for b in blocks]

@@ -340,6 +340,18 @@ int wf_geometry(const wf_handle* h, int64_t* out);
  */
 int wf_mfma_calibrate(int32_t blocks, int32_t steps, float* out, void* stream);
 
+/*
+ * HBM calibration for the publish roofline: copies `bytes` (a positive
+ * multiple of 16) from device buffer src to device buffer dst (both 16-byte
+ * aligned, not overlapping) with a streaming kernel that does nothing else:
+ * two 16-byte non-temporal loads and plain stores per thread. Timed by the
+ * caller on `stream`, (2 * bytes) / time is the read+write rate this GPU
+ * reaches for that byte count, the attainable ceiling of an HBM-bound kernel
+ * with the same mix. WF_E_INVALID_ARG (nothing launched) for a null pointer,
+ * a size that is not a positive multiple of 16 or a misaligned pointer.
+ */
+int wf_stream_copy_calibrate(const void* src, void* dst, int64_t bytes, void* stream);
+
 const char* wf_status_string(int status);
 const char* wf_last_error(const wf_handle* h);
 

@@ -563,3 +563,15 @@ def test_mfma_calibrate_rejects_bad_arguments_before_any_launch(lib, blocks, ste
     with pytest.raises(wf.WfError) as e:
         _lib.wf_mfma_calibrate(blocks, steps, out, stream=0)
     assert e.value.status == _lib.WF_E_INVALID_ARG
+
+
+@pytest.mark.parametrize("src,dst,nbytes", [(None, FAKE, 64), (FAKE, None, 64), (FAKE, FAKE + 16, 0),
+                                            (FAKE, FAKE + 64, -16), (FAKE, FAKE + 64, 24), (FAKE + 8, FAKE + 64, 32),
+                                            (FAKE, FAKE + 68, 32)])
+def test_stream_copy_calibrate_rejects_bad_arguments_before_any_launch(lib, src, dst, nbytes):
+    """Null pointers, sizes that are not a positive multiple of 16 and pointers
+    that are not 16-byte aligned return WF_E_INVALID_ARG and launch nothing
+    (the fake addresses are never touched)."""
+    with pytest.raises(wf.WfError) as e:
+        _lib.wf_stream_copy_calibrate(src, dst, nbytes, stream=0)
+    assert e.value.status == _lib.WF_E_INVALID_ARG

@@ -107,3 +107,20 @@ def test_mfma_calibrate_checksum_equals_host_sum_of_products(blocks, steps):
         # third and a dropped step by 1/steps of it, 1e-4 of sum |products|
         assert err <= 2.0 ** -20, (wv, s, tot, mag)
     say("waves", len(exp), "worst |checksum - exact| / sum|products| = %.2e" % worst)
+
+
+@pytest.mark.parametrize("nbytes", [16, 4096 + 16, (1 << 20) + 48, 215654400])
+def test_stream_copy_calibrate_copies_exactly_the_bytes_asked(nbytes):
+    """The streaming copy (the publish roofline's same-session HBM rate) moves
+    exactly nbytes: the destination equals the source and the guard bytes
+    after it are untouched."""
+    from wavefront_causal_attention_amd import _lib
+    say("case stream copy", nbytes, "bytes")
+    guard = 4096
+    g = torch.Generator(device="cpu").manual_seed(nbytes % 9973)
+    src = torch.randint(0, 256, (nbytes,), dtype=torch.uint8, generator=g).cuda()
+    dst = torch.full((nbytes + guard,), 0xA5, dtype=torch.uint8, device="cuda")
+    _lib.wf_stream_copy_calibrate(src, dst, nbytes)
+    torch.cuda.synchronize()
+    assert torch.equal(dst[:nbytes], src)
+    assert bool((dst[nbytes:] == 0xA5).all())

@@ -13,7 +13,8 @@ from ._lib import (WF_DTYPE_BF16, WF_DTYPE_FP32, WF_DTYPE_FP8_E4M3, WF_E_HIP, WF
                    wf_geometry, wf_kv_publish, wf_page_table_host, wf_pool_bytes, wf_pool_create,
                    wf_qkv_project_publish, wf_qkv_project_publish_w8a8, wf_quantize_rows_fp8,
                    wf_pool_create_host_model, wf_pool_destroy, wf_ready_mask, wf_round_advance,
-                   wf_round_index, wf_round_replayed, wf_schedule_chunk_ids, wf_mfma_calibrate)
+                   wf_round_index, wf_round_replayed, wf_schedule_chunk_ids, wf_mfma_calibrate,
+                   wf_stream_copy_calibrate)
 
 _DT = {"bf16": WF_DTYPE_BF16, "fp32": WF_DTYPE_FP32, "fp8": WF_DTYPE_FP8_E4M3}
 

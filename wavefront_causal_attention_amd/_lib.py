@@ -95,6 +95,7 @@ def load() -> ctypes.CDLL:
         "wf_ready_mask": (ctypes.c_int, [P, I32, ctypes.POINTER(ctypes.c_uint64)]),
         "wf_geometry": (ctypes.c_int, [P, P]),
         "wf_mfma_calibrate": (ctypes.c_int, [I32, I32, P, P]),
+        "wf_stream_copy_calibrate": (ctypes.c_int, [P, P, I64, P]),
         "wf_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "wf_last_error": (ctypes.c_char_p, [P]),
     }
@@ -158,6 +159,11 @@ def wf_pool_create_host_model(cfg: wf_config) -> int:
 
 def wf_mfma_calibrate(blocks, steps, out, stream=None) -> None:
     _check(load().wf_mfma_calibrate(int(blocks), int(steps), _ptr(out), _stream(stream)), "wf_mfma_calibrate")
+
+
+def wf_stream_copy_calibrate(src, dst, nbytes, stream=None) -> None:
+    _check(load().wf_stream_copy_calibrate(_ptr(src), _ptr(dst), int(nbytes), _stream(stream)),
+           "wf_stream_copy_calibrate")
 
 
 def wf_pool_destroy(h: int) -> None:
@@ -267,7 +273,7 @@ def wf_geometry(h):
 
 EXPORTED = [
     "wf_pool_bytes", "wf_pool_create", "wf_pool_create_host_model", "wf_pool_destroy",
-    "wf_mfma_calibrate", "wf_kv_publish", "wf_kv_publish_noalloc", "wf_qkv_project_publish", "wf_qkv_project_publish_w8a8", "wf_quantize_rows_fp8",
+    "wf_mfma_calibrate", "wf_stream_copy_calibrate", "wf_kv_publish", "wf_kv_publish_noalloc", "wf_qkv_project_publish", "wf_qkv_project_publish_w8a8", "wf_quantize_rows_fp8",
     "wf_attention_round", "wf_round_advance", "wf_round_replayed", "wf_round_index",
     "wf_attention_work_list",
     "wf_schedule_chunk_ids", "wf_page_table_host", "wf_ready_mask", "wf_geometry",

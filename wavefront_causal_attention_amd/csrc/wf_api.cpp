@@ -905,6 +905,13 @@ int wf_mfma_calibrate(int32_t blocks, int32_t steps, float* out, void* stream) {
     return e == hipSuccess ? WF_OK : WF_E_HIP;
 }
 
+int wf_stream_copy_calibrate(const void* src, void* dst, int64_t bytes, void* stream) {
+    if (!src || !dst || bytes <= 0 || bytes % 16 != 0 || ((uintptr_t)src | (uintptr_t)dst) % 16 != 0)
+        return WF_E_INVALID_ARG;
+    const hipError_t e = wf::launch_stream_copy(src, dst, bytes, (hipStream_t)stream);
+    return e == hipSuccess ? WF_OK : WF_E_HIP;
+}
+
 const char* wf_status_string(int status) {
     switch (status) {
         case WF_OK: return "ok";

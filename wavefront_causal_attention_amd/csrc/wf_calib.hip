@@ -1,3 +1,5 @@
+// Calibration kernels for the rooflines.
+//
 // Matrix-core calibration: the rate at which this GPU sustains the attention
 // kernel's MFMA instruction (v_mfma_f32_32x32x16_bf16) at the clock it holds
 // under that load. The roofline's peak is the vendor's dense bf16 figure at
@@ -60,7 +62,33 @@ __global__ __launch_bounds__(512, 1) void mfma_calibrate_kernel(int32_t steps, f
     out[id] = acc;                                   // keeps every MFMA live
 }
 
+// HBM streaming copy: the rate this GPU moves a byte count between two
+// device buffers (half read, half written) when the kernel does nothing else,
+// for the publish kernels' rooflines (their traffic is such a read/write mix).
+// Each thread copies two 16-byte vectors, loaded non-temporally (each byte is
+// read once) and stored plainly: on gfx950 this form measured fastest (four
+// or eight vectors per thread, cached loads or non-temporal stores slower).
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+__global__ __launch_bounds__(256) void stream_copy_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
+                                                         int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * 512 + threadIdx.x;
+    u32x4 v0, v1;
+    if (i < n) v0 = __builtin_nontemporal_load(src + i);
+    if (i + 256 < n) v1 = __builtin_nontemporal_load(src + i + 256);
+    if (i < n) dst[i] = v0;
+    if (i + 256 < n) dst[i + 256] = v1;
+}
+
 }  // namespace
+
+hipError_t launch_stream_copy(const void* src, void* dst, int64_t bytes, hipStream_t st) {
+    const int64_t n = bytes / 16;
+    const int64_t blocks = (n + 511) / 512;
+    if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(stream_copy_kernel, dim3((unsigned)blocks), dim3(256), 0, st,
+                       static_cast<const u32x4*>(src), static_cast<u32x4*>(dst), n);
+    return hipGetLastError();
+}
 
 hipError_t launch_mfma_calibrate(int32_t blocks, int32_t steps, float* out, hipStream_t st) {
     hipLaunchKernelGGL(mfma_calibrate_kernel, dim3(blocks), dim3(512), 0, st, steps, out);

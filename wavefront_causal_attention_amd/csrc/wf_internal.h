@@ -167,5 +167,6 @@ hipError_t static_scratch(void** ptr);
 hipError_t launch_attention(const AttnArgs& a, bool fp8, hipStream_t st);
 // blocks workgroups of 8 waves, each `steps` steps of 32 bf16 MFMAs per wave
 hipError_t launch_mfma_calibrate(int32_t blocks, int32_t steps, float* out, hipStream_t st);
+hipError_t launch_stream_copy(const void* src, void* dst, int64_t bytes, hipStream_t st);
 
 }  // namespace wf
