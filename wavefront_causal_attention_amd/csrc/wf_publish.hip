@@ -240,9 +240,11 @@ __global__ __launch_bounds__(256) void publish_bf16_kernel(PublishArgs a) {
     const int n = n0 + tk;
     const bool live = n < a.N;
 
-    // every row load of this thread is issued before the time-axis table is
-    // built, so the HBM latency overlaps the fp64 sincos work (rows past the
-    // chunk are clamped to its last row and not used)
+    // the time-axis table is built first (by the block's first threads only),
+    // then every row load of this thread is issued: the fp64 sincos and the
+    // held rows do not need registers at the same time (rows past the chunk
+    // are clamped to its last row and not used)
+    fill_ttab(ttab, a, sr, f_lo, nf);
     const int64_t e0 = ((int64_t)sr * a.N + min(n, a.N - 1)) * a.row_stride + (int64_t)h0 * D + ch * 8;
     Raw8<IN_FP32> kin[HPB], qin[HPB], vin[HPB];
 #pragma unroll
@@ -251,10 +253,16 @@ __global__ __launch_bounds__(256) void publish_bf16_kernel(PublishArgs a) {
         vin[hh].load(a.v, e0 + hh * D);
         if (a.q) qin[hh].load(a.q, e0 + hh * D);
     }
-    fill_ttab(ttab, a, sr, f_lo, nf);
     __syncthreads();
 
     if (live) {
+        // V first: its rows leave the registers before the rotation needs them
+#pragma unroll
+        for (int hh = 0; hh < HPB; ++hh) {
+            float x[8];
+            vin[hh].unpack(x);
+            *reinterpret_cast<uint4*>(&vst[(hh * TOK + tk) * D + ch * 8]) = pack8(x);
+        }
         const TokenGrid grid(a.frame_h, a.frame_w);
         int f, yy, xw;
         grid.pos(n, f, yy, xw);
@@ -274,8 +282,6 @@ __global__ __launch_bounds__(256) void publish_bf16_kernel(PublishArgs a) {
                                (((int64_t)s * a.heads + h0 + hh) * a.N + n) * D + ch * 8;
                 st16(qp, pack8_f64(r));
             }
-            vin[hh].unpack(x);
-            *reinterpret_cast<uint4*>(&vst[(hh * TOK + tk) * D + ch * 8]) = pack8(x);
         }
     }
     __syncthreads();
