@@ -108,8 +108,16 @@ def run_whole_video(w, C, check_round):
     fill round to the last drain round, publishing and attending only the
     slots that hold a chunk; check_round(k, out, live, clean, lo, hi) checks
     each round. Anchor and history are never seeded: they are what the store
-    slot published in earlier rounds."""
+    slot published in earlier rounds. Every K/V page, key scale and key mean of
+    the pool starts as NaN (all bytes 0xFF: NaN in bf16, e4m3 and fp32), so a
+    read of a page no chunk was published to shows up in the outputs."""
     pool = wf.Pool(config_of(w, first_round=0, total_chunks=C))
+    g = pool.geometry
+    for off, nbytes in ((g["k_off"], g["k_layer_bytes"]), (g["v_off"], g["v_layer_bytes"]),
+                        (g["kscale_off"], g["kscale_layer_bytes"]), (g["kmean_off"], g["kmean_layer_bytes"])):
+        if nbytes > 0:
+            pool.pool[off:off + nbytes].fill_(0xFF)
+    torch.cuda.synchronize()
     q, qs = pool.q_buffer(), pool.q_scale_buffer()
     clean = {}
     for k in range(C + w.S):
